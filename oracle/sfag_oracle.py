@@ -193,26 +193,29 @@ def forward(q, k, v, qr, kr, idx, geom, block, mode, scale_value, tokens=None):
     return O, M, L
 
 
-def backward(q, k, v, qr, kr, idx, dO, O, smax, ssum, geom, block, mode, scale_value):
+def backward(q, k, v, qr, kr, idx, dO, O, smax, ssum, geom, block, mode, scale_value, tokens=None):
     """Full backward pass.  Shapes: q/dO/O (T1, G, D), qr (T1, G, Dr) or None,
     k/v (T2, D), kr (T2, Dr) or None, idx (T1, Kent), smax/ssum (T1, G).
 
     Returns float64 dq (T1,G,D), dk (T2,D), dv (T2,D), dqr, dkr (None without
     rope).  dK and dV rows are accumulated over every (token, position) that
     selects them (np.add.at, so duplicates add up); rows never selected stay 0.
+    ``tokens`` restricts the pass to those query tokens (their dQ rows and
+    their contributions to dK/dV); by default every token.
     """
     sc = scale32(scale_value)
     T1, T2 = geom["T1"], geom["T2"]
     G, D = q.shape[1], k.shape[1]
     rope = qr is not None
-    rows = decode(idx, block, mode, geom)
+    tokens = np.arange(T1) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    rows = decode(idx, block, mode, geom, tokens)
     dq = np.zeros((T1, G, D))
     dk = np.zeros((T2, D))
     dv = np.zeros((T2, v.shape[1]))
     dqr = np.zeros((T1, G, qr.shape[2])) if rope else None
     dkr = np.zeros((T2, kr.shape[1])) if rope else None
-    for t in range(T1):
-        sel = rows[t][rows[t] >= 0]
+    for i, t in enumerate(tokens):
+        sel = rows[i][rows[i] >= 0]
         if sel.size == 0:
             continue
         Ks, Vs = _f64(k, sel), _f64(v, sel)

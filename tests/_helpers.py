@@ -61,3 +61,18 @@ def rel_l2(x, ref):
     if den == 0:
         return 0.0 if num == 0 else float("inf")
     return float(num / den)
+
+
+def call_backward(case, inp, **kw):
+    """Run the library on generator inputs (all tensors on the GPU)."""
+    import top_sparse_attention_sfag_amd as sfag
+    return sfag.backward(
+        inp["query"], inp["key"], inp["value"], inp["sparse_indices"], inp["dout"], inp["out"],
+        inp["softmax_max"], inp["softmax_sum"], seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"),
+        query_rope=inp.get("query_rope"), key_rope=inp.get("key_rope"), scale=case.scale_value,
+        block_size=case.block, layout=case.layout, sparse_mode=case.mode,
+        deterministic=kw.pop("deterministic", case.deterministic), **kw)
+
+
+def to_device(inp, device="cuda"):
+    return {k: v.to(device) for k, v in inp.items()}

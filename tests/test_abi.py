@@ -1,0 +1,145 @@
+"""C ABI on the CPU: the library loads and exports what include/sfag.h declares,
+and phase-1 validation returns the status codes of the operator page's 返回值
+table (161001 null pointer, 161002 invalid dtype/format, 561002 attribute or
+shape outside the supported range).  Phase 1 reads no tensor data, so these
+tests run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import top_sparse_attention_sfag_amd as sfag
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sfag.h")
+
+
+def test_exports_every_declared_function():
+    src = open(HDR).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s+(sfag_\w+)\s*\(", src, re.M))
+    assert {"sfag_workspace_size", "sfag_backward", "sfag_plan_destroy", "sfag_last_error",
+            "sfag_index_workspace_size", "sfag_build_index"} <= names
+    L = ctypes.CDLL(sfag.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(L, n), n
+
+
+def _tensors(layout="BSND", B=1, S1=2, S2=8, G=4, D=512, Dr=64, K=4, dtype=torch.bfloat16):
+    if layout == "BSND":
+        q = torch.zeros(B, S1, G, D, dtype=dtype)
+        k = torch.zeros(B, S2, 1, D, dtype=dtype)
+        idx = torch.zeros(B, S1, 1, K, dtype=torch.int32)
+        st = torch.zeros(B, 1, S1, G)
+        qr = torch.zeros(B, S1, G, Dr, dtype=dtype) if Dr else None
+        kr = torch.zeros(B, S2, 1, Dr, dtype=dtype) if Dr else None
+        lq = lk = None
+    else:
+        T1, T2 = B * S1, B * S2
+        q = torch.zeros(T1, G, D, dtype=dtype)
+        k = torch.zeros(T2, 1, D, dtype=dtype)
+        idx = torch.zeros(T1, 1, K, dtype=torch.int32)
+        st = torch.zeros(1, T1, G)
+        qr = torch.zeros(T1, G, Dr, dtype=dtype) if Dr else None
+        kr = torch.zeros(T2, 1, Dr, dtype=dtype) if Dr else None
+        lq = torch.full((B,), S1, dtype=torch.int32)
+        lk = torch.full((B,), S2, dtype=torch.int32)
+    return dict(query=q, key=k, value=k.clone(), sparse_indices=idx, dout=q.clone(), out=q.clone(),
+                softmax_max=st, softmax_sum=st.clone(), dq=q.clone(), dk=k.clone(), dv=k.clone(),
+                query_rope=qr, key_rope=kr, dq_rope=None if qr is None else qr.clone(),
+                dk_rope=None if kr is None else kr.clone(), seqlens_q=lq, seqlens_kv=lk, layout=layout)
+
+
+def _plan(t, **over):
+    t = dict(t)
+    t.update(over)
+    args = [t.pop(n) for n in ("query", "key", "value", "sparse_indices", "dout", "out", "softmax_max",
+                               "softmax_sum", "dq", "dk", "dv")]
+    return sfag.plan(*args, **t)
+
+
+def _code(t, **over):
+    try:
+        ws, p = _plan(t, **over)
+    except sfag.SfagError as e:
+        return e.code
+    sfag.destroy(p)
+    return 0
+
+
+def test_valid_plans():
+    for layout in ("BSND", "TND"):
+        for Dr in (0, 64):
+            t = _tensors(layout, Dr=Dr)
+            ws, p = _plan(t)
+            assert ws > 0
+            sfag.destroy(p)
+    t = _tensors("BSND", dtype=torch.float16)
+    assert _code(t, block_size=16, sparse_mode=3, deterministic=True) == 0
+
+
+def test_empty_query_needs_no_workspace():
+    t = _tensors(S1=0)
+    ws, p = _plan(t)
+    assert ws == 0
+    sfag.destroy(p)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(layout="BNSD"), 561002),
+    (dict(sparse_mode=1), 561002),
+    (dict(sparse_mode=4), 561002),
+    (dict(block_size=2), 561002),
+    (dict(pre_tokens=100), 561002),
+    (dict(next_tokens=0), 561002),
+    (dict(scale=float("nan")), 161002),
+    (dict(key_rope=None), 161002),
+    (dict(dq_rope=None), 161001),
+    (dict(query=None), 161001),
+    (dict(dk=None), 161001),
+])
+def test_attribute_and_presence_errors(over, code):
+    assert _code(_tensors(), **over) == code
+
+
+def test_dtype_and_format_errors():
+    t = _tensors()
+    assert _code(t, key=t["key"].half()) == 161002
+    assert _code(t, sparse_indices=t["sparse_indices"].long()) == 161002
+    assert _code(t, softmax_max=t["softmax_max"].half()) == 161002
+    assert _code(t, query=t["query"].float(), dout=t["dout"].float(), out=t["out"].float(),
+                 dq=t["dq"].float()) == 161002
+    nc = t["query"].transpose(1, 2).contiguous().transpose(1, 2)
+    assert not nc.is_contiguous()
+    assert _code(t, query=nc) == 161002
+    tt = _tensors("TND")
+    assert _code(tt, seqlens_q=tt["seqlens_q"].long()) == 161002
+
+
+def test_shape_errors():
+    assert _code(_tensors(D=256)) == 561002
+    assert _code(_tensors(Dr=32)) == 561002
+    assert _code(_tensors(G=129, S1=1, K=1, Dr=0)) == 561002
+    assert _code(_tensors(B=257, S1=1, S2=1, K=1, Dr=0, G=1)) == 561002
+    t = _tensors()
+    k2 = torch.zeros(1, 8, 2, 512, dtype=torch.bfloat16)
+    assert _code(t, key=k2, value=k2.clone(), dk=k2.clone(), dv=k2.clone()) == 561002   # N2 != 1
+    assert _code(t, sparse_indices=torch.zeros(1, 3, 1, 4, dtype=torch.int32)) == 561002
+    assert _code(t, softmax_sum=torch.zeros(1, 1, 2, 5)) == 561002
+    assert _code(t, dv=torch.zeros(1, 9, 1, 512, dtype=torch.bfloat16)) == 561002
+    tt = _tensors("TND")
+    assert _code(tt, seqlens_q=None) == 561002
+    assert _code(tt, seqlens_kv=torch.zeros(2, dtype=torch.int32)) == 561002
+    assert _code(_tensors(S1=131073, G=1, K=1, Dr=0)) == 561002
+
+
+def test_backward_rejects_small_workspace_before_launch():
+    t = _tensors()
+    ws, p = _plan(t)
+    rc = sfag.lib().sfag_backward(None, ctypes.c_uint64(ws - 1), p, None)   # consumes the plan
+    assert rc == 161002
+    assert b"workspace" in sfag.lib().sfag_last_error()
+
+
+def test_null_plan():
+    assert sfag.lib().sfag_backward(None, ctypes.c_uint64(0), None, None) == 161001

@@ -1,0 +1,226 @@
+"""ctypes binding of libsfag (argument marshalling only: every step of the
+backward pass runs in the library's HIP kernels).
+
+PyTorch provides the device memory (outputs and workspace) and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libsfag.so")
+
+OK = 0
+ERR_NULLPTR = 161001
+ERR_PARAM_INVALID = 161002
+ERR_RUNTIME = 361001
+ERR_TILING = 561002
+
+_DTYPE = {torch.bfloat16: 1, torch.float16: 2, torch.float32: 3, torch.int32: 4}
+WINDOW = 2147483647
+
+
+class SfagTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class SfagError(Exception):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libsfag error {code}: {msg}")
+        self.code = code
+
+
+class SfagValueError(SfagError, ValueError):
+    pass
+
+
+class SfagRuntimeError(SfagError, RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python top_sparse_attention_sfag_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        T = ctypes.POINTER(SfagTensor)
+        L.sfag_workspace_size.restype = ctypes.c_int
+        L.sfag_workspace_size.argtypes = [T] * 12 + [ctypes.c_double, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_bool] + [T] * 5 + [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p)]
+        L.sfag_backward.restype = ctypes.c_int
+        L.sfag_backward.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        L.sfag_plan_destroy.restype = None
+        L.sfag_plan_destroy.argtypes = [ctypes.c_void_p]
+        L.sfag_last_error.restype = ctypes.c_char_p
+        L.sfag_last_error.argtypes = []
+        L.sfag_index_workspace_size.restype = ctypes.c_uint64
+        L.sfag_index_workspace_size.argtypes = [ctypes.c_int64] * 4
+        L.sfag_build_index.restype = ctypes.c_int
+        L.sfag_build_index.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 7 + [ctypes.c_int32, ctypes.c_int64]
+                                       + [ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_void_p] * 5)
+        L.sfag_profile_enable.restype = None
+        L.sfag_profile_enable.argtypes = [ctypes.c_int]
+        L.sfag_profile_reset.restype = None
+        L.sfag_profile_reset.argtypes = []
+        L.sfag_profile_read.restype = ctypes.c_int
+        L.sfag_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
+        _lib = L
+    return _lib
+
+
+KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "col", "csr", "key_reduce", "cast")
+
+
+def profile_enable(on: bool = True):
+    lib().sfag_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    lib().sfag_profile_reset()
+
+
+def profile_read():
+    """{kernel group: (total ms, launches)} since the last reset."""
+    out = {}
+    for n in KERNEL_GROUPS:
+        ms, cnt = ctypes.c_double(0), ctypes.c_int64(0)
+        lib().sfag_profile_read(n.encode(), ctypes.byref(ms), ctypes.byref(cnt))
+        if cnt.value:
+            out[n] = (ms.value, cnt.value)
+    return out
+
+
+def _desc(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.dim() > 4:
+        raise SfagValueError(ERR_PARAM_INVALID, "tensors have at most 4 dims")
+    d = SfagTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPE.get(t.dtype, 0)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return ctypes.pointer(d)
+
+
+def _raise(code: int):
+    msg = lib().sfag_last_error().decode()
+    if code == ERR_RUNTIME:
+        raise SfagRuntimeError(code, msg)
+    raise SfagValueError(code, msg)
+
+
+def plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, dq, dk, dv, *, dq_rope=None,
+         dk_rope=None, seqlens_q=None, seqlens_kv=None, query_rope=None, key_rope=None, scale=None, block_size=1,
+         layout: Optional[str] = "BSND", sparse_mode=0, pre_tokens=WINDOW, next_tokens=WINDOW, deterministic=False):
+    """Phase 1: returns (workspace bytes, plan handle).  Reads no tensor data."""
+    if scale is None and query is not None:
+        scale = 1.0 / (query.shape[-1] + (query_rope.shape[-1] if query_rope is not None else 0)) ** 0.5
+    if scale is None:
+        scale = 1.0
+    ws = ctypes.c_uint64(0)
+    p = ctypes.c_void_p(None)
+    rc = lib().sfag_workspace_size(
+        _desc(query), _desc(key), _desc(value), _desc(sparse_indices), _desc(dout), _desc(out), _desc(softmax_max),
+        _desc(softmax_sum), _desc(seqlens_q), _desc(seqlens_kv), _desc(query_rope), _desc(key_rope), float(scale),
+        int(block_size), None if layout is None else layout.encode(), int(sparse_mode), int(pre_tokens),
+        int(next_tokens), bool(deterministic), _desc(dq), _desc(dk), _desc(dv), _desc(dq_rope), _desc(dk_rope),
+        ctypes.byref(ws), ctypes.byref(p))
+    if rc != OK:
+        _raise(rc)
+    return int(ws.value), p
+
+
+def destroy(p):
+    lib().sfag_plan_destroy(p)
+
+
+def _stream_ptr(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def backward(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, *, seqlens_q=None,
+             seqlens_kv=None, query_rope=None, key_rope=None, scale=None, block_size=1, layout="BSND", sparse_mode=0,
+             pre_tokens=WINDOW, next_tokens=WINDOW, deterministic=False, outputs=None, workspace=None, stream=None):
+    """Backward pass of top-k sparse flash attention on the GPU.
+
+    Returns (dq, dk, dv, dq_rope, dk_rope); the rope gradients are None without
+    rope inputs.  ``outputs`` may supply preallocated gradients and
+    ``workspace`` a uint8 device buffer of at least the planned size.
+    """
+    if not query.is_cuda:
+        raise SfagValueError(ERR_PARAM_INVALID, "tensors must be on the GPU")
+    if outputs is None:
+        dq, dk, dv = torch.empty_like(query), torch.empty_like(key), torch.empty_like(value)
+        dqr = torch.empty_like(query_rope) if query_rope is not None else None
+        dkr = torch.empty_like(key_rope) if key_rope is not None else None
+    else:
+        dq, dk, dv, dqr, dkr = outputs
+    ws, p = plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, dq, dk, dv, dq_rope=dqr,
+                 dk_rope=dkr, seqlens_q=seqlens_q, seqlens_kv=seqlens_kv, query_rope=query_rope, key_rope=key_rope,
+                 scale=scale, block_size=block_size, layout=layout, sparse_mode=sparse_mode, pre_tokens=pre_tokens,
+                 next_tokens=next_tokens, deterministic=deterministic)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
+    rc = lib().sfag_backward(ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()), p,
+                             _stream_ptr(query.device, stream))
+    if rc != OK:
+        _raise(rc)
+    return dq, dk, dv, dqr, dkr
+
+
+def workspace_size(*args, **kw) -> int:
+    ws, p = plan(*args, **kw)
+    destroy(p)
+    return ws
+
+
+def build_index(sparse_indices, *, T2, block_size=1, layout="BSND", sparse_mode=0, B=None, S1=None, S2=None,
+                seqlens_q=None, seqlens_kv=None, stream=None):
+    """Index decode and key -> (token, position) CSR on the GPU.
+
+    Returns (n_valid (T1,), rows (T1, K*block), csr_offsets (T2+1,),
+    csr_pairs (T1*K*block,)) as int32 device tensors; see sfag_build_index.
+    """
+    dev = sparse_indices.device
+    K = sparse_indices.shape[-1]
+    T1 = sparse_indices.numel() // max(K, 1) if K else sparse_indices.shape[0]
+    lay = 0 if layout == "BSND" else 1
+    if lay == 0:
+        B = B if B is not None else sparse_indices.shape[0]
+        S1 = S1 if S1 is not None else sparse_indices.shape[1]
+        S2 = S2 if S2 is not None else T2 // max(B, 1)
+    else:
+        B = seqlens_q.numel()
+        S1 = S2 = 0
+    E = K * block_size
+    n_valid = torch.empty(T1, dtype=torch.int32, device=dev)
+    rows = torch.empty((T1, E), dtype=torch.int32, device=dev)
+    off = torch.empty(T2 + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(max(T1 * E, 1), dtype=torch.int32, device=dev)
+    wsz = lib().sfag_index_workspace_size(T1, T2, K, block_size)
+    ws = torch.empty(max(int(wsz), 1), dtype=torch.uint8, device=dev)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+    rc = lib().sfag_build_index(ptr(sparse_indices), ptr(seqlens_q), ptr(seqlens_kv), B, S1, S2, T1, T2, K,
+                                block_size, lay, sparse_mode, ptr(ws), ctypes.c_uint64(ws.numel()), ptr(n_valid),
+                                ptr(rows), ptr(off), ptr(pairs), _stream_ptr(dev, stream))
+    if rc != OK:
+        _raise(rc)
+    return n_valid, rows, off, pairs[: T1 * E]

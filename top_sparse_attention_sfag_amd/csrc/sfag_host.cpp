@@ -1,0 +1,311 @@
+// Phase 1 of the two-phase call: argument validation, planning and workspace
+// layout.  Plain C++ (no HIP headers): it reads no device memory.
+//
+// The checks follow the operator page "aclnnSparseFlashAttentionGrad":
+// GetWorkspaceSize parameter table (dtypes, shapes, N2 = 1, D = 512, Dr = 64,
+// sparseBlockSize, layout, sparseMode, preTokens/nextTokens, contiguity), the
+// 返回值 table (which status code each failure class returns) and 规格约束
+// (B in 1..256, S1/S2 up to 128K).
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <sstream>
+#include <string>
+
+#include "sfag_plan.h"
+
+namespace sfag {
+
+static thread_local std::string g_error;
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+static void carve(uint64_t& cursor, uint64_t& field, uint64_t bytes) {
+  field = cursor;
+  cursor = align256(cursor + bytes);
+}
+
+WorkspaceLayout layout_for(const Dims& d, bool partials) {
+  WorkspaceLayout w;
+  uint64_t c = 0;
+  const uint64_t ch = (uint64_t)d.chunk, E = (uint64_t)d.E;
+  carve(c, w.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
+  carve(c, w.delta, (uint64_t)d.T1 * d.G * 4);
+  carve(c, w.acc, (uint64_t)d.T2 * d.AW * 4);
+  carve(c, w.nvalid, ch * 4);
+  carve(c, w.rows, ch * E * 4);
+  carve(c, w.ds, ch * E * d.Gp * 2);
+  carve(c, w.p, ch * E * d.Gp * 2);
+  if (partials) {
+    const uint64_t n = ch * E;
+    const uint64_t nblk = (n + kSortBlock - 1) / kSortBlock;
+    carve(c, w.partials, n * d.AW * 4);
+    carve(c, w.sort_keys[0], n * 4);
+    carve(c, w.sort_keys[1], n * 4);
+    carve(c, w.sort_vals[0], n * 4);
+    carve(c, w.sort_vals[1], n * 4);
+    carve(c, w.sort_hist, 256 * nblk * 4);
+    carve(c, w.csr_off, (uint64_t)(d.T2 + 1) * 4);
+  }
+  w.total = c;
+  return w;
+}
+
+}  // namespace sfag
+
+using namespace sfag;
+
+namespace {
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+int64_t numel(const sfag_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+bool contiguous(const sfag_tensor* t) {
+  int64_t s = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != s) return false;
+    s *= t->shape[i];
+  }
+  return true;
+}
+
+std::string shape_str(const sfag_tensor* t) {
+  std::ostringstream o;
+  o << "(";
+  for (int i = 0; i < t->ndim; ++i) o << (i ? "," : "") << t->shape[i];
+  o << ")";
+  return o.str();
+}
+
+bool shape_is(const sfag_tensor* t, std::initializer_list<int64_t> s) {
+  if (t->ndim != (int)s.size()) return false;
+  int i = 0;
+  for (int64_t v : s) {
+    if (t->shape[i++] != v) return false;
+  }
+  return true;
+}
+
+bool same_shape(const sfag_tensor* a, const sfag_tensor* b) {
+  if (a->ndim != b->ndim) return false;
+  for (int i = 0; i < a->ndim; ++i)
+    if (a->shape[i] != b->shape[i]) return false;
+  return true;
+}
+
+int64_t env_i64(const char* name, int64_t dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::strtoll(s, nullptr, 10);
+}
+
+constexpr int64_t kMaxTokensPerSeq = 131072;  // 规格约束: S1, S2 up to 128K
+constexpr int64_t kMaxBatch = 256;            // 规格约束: B 1..256
+constexpr int64_t kWindow = 2147483647;       // preTokens / nextTokens: only this value
+
+}  // namespace
+
+extern "C" const char* sfag_last_error(void) { return g_error.c_str(); }
+
+extern "C" void sfag_plan_destroy(sfag_plan* plan) { delete plan; }
+
+extern "C" int sfag_workspace_size(
+    const sfag_tensor* query, const sfag_tensor* key, const sfag_tensor* value, const sfag_tensor* sparseIndices,
+    const sfag_tensor* dOut, const sfag_tensor* out, const sfag_tensor* softmaxMax, const sfag_tensor* softmaxSum,
+    const sfag_tensor* lensQ, const sfag_tensor* lensKv, const sfag_tensor* queryRope, const sfag_tensor* keyRope,
+    double scaleValue, int64_t sparseBlockSize, const char* layoutOptional, int64_t sparseMode, int64_t preTokens,
+    int64_t nextTokens, bool deterministic, const sfag_tensor* dQueryOut, const sfag_tensor* dKeyOut,
+    const sfag_tensor* dValueOut, const sfag_tensor* dQueryRopeOut, const sfag_tensor* dKeyRopeOut,
+    uint64_t* workspaceSize, sfag_plan** plan) {
+  set_error("");
+  if (plan) *plan = nullptr;
+  // ---- 161001: required arguments present --------------------------------
+  struct Named {
+    const sfag_tensor* t;
+    const char* name;
+  };
+  const Named required[] = {{query, "query"},        {key, "key"},           {value, "value"},
+                            {sparseIndices, "sparseIndices"}, {dOut, "dOut"}, {out, "out"},
+                            {softmaxMax, "softmaxMax"}, {softmaxSum, "softmaxSum"}, {dQueryOut, "dQueryOut"},
+                            {dKeyOut, "dKeyOut"},    {dValueOut, "dValueOut"}};
+  for (const Named& n : required)
+    if (!n.t) return fail(SFAG_ERR_NULLPTR, std::string(n.name) + " is NULL");
+  if (!workspaceSize || !plan) return fail(SFAG_ERR_NULLPTR, "workspaceSize or plan output pointer is NULL");
+  const bool rope = queryRope || keyRope;
+  if (rope && !(queryRope && keyRope))
+    return fail(SFAG_ERR_PARAM_INVALID, "queryRope and keyRope must be given together");
+  if (rope && (!dQueryRopeOut || !dKeyRopeOut))
+    return fail(SFAG_ERR_NULLPTR, "dQueryRopeOut and dKeyRopeOut are required when rope inputs are given");
+
+  const Named all[] = {{query, "query"},           {key, "key"},
+                       {value, "value"},           {sparseIndices, "sparseIndices"},
+                       {dOut, "dOut"},             {out, "out"},
+                       {softmaxMax, "softmaxMax"}, {softmaxSum, "softmaxSum"},
+                       {lensQ, "actualSeqLengthsQuery"}, {lensKv, "actualSeqLengthsKv"},
+                       {queryRope, "queryRope"},   {keyRope, "keyRope"},
+                       {dQueryOut, "dQueryOut"},   {dKeyOut, "dKeyOut"},
+                       {dValueOut, "dValueOut"},   {rope ? dQueryRopeOut : nullptr, "dQueryRopeOut"},
+                       {rope ? dKeyRopeOut : nullptr, "dKeyRopeOut"}};
+  for (const Named& n : all) {
+    if (!n.t) continue;
+    if (n.t->ndim < 1 || n.t->ndim > 4) return fail(SFAG_ERR_PARAM_INVALID, std::string(n.name) + ": ndim must be 1..4");
+    for (int i = 0; i < n.t->ndim; ++i)
+      if (n.t->shape[i] < 0) return fail(SFAG_ERR_PARAM_INVALID, std::string(n.name) + ": negative extent");
+    if (numel(n.t) > 0 && !n.t->data) return fail(SFAG_ERR_NULLPTR, std::string(n.name) + ": data is NULL");
+  }
+  // ---- 161002: dtypes and contiguity --------------------------------------
+  const int32_t ft = query->dtype;
+  if (ft != SFAG_BF16 && ft != SFAG_FP16) return fail(SFAG_ERR_PARAM_INVALID, "query dtype must be bf16 or fp16");
+  const Named floats[] = {{key, "key"}, {value, "value"}, {dOut, "dOut"}, {out, "out"}, {queryRope, "queryRope"},
+                          {keyRope, "keyRope"}, {dQueryOut, "dQueryOut"}, {dKeyOut, "dKeyOut"},
+                          {dValueOut, "dValueOut"}, {rope ? dQueryRopeOut : nullptr, "dQueryRopeOut"},
+                          {rope ? dKeyRopeOut : nullptr, "dKeyRopeOut"}};
+  for (const Named& n : floats)
+    if (n.t && n.t->dtype != ft) return fail(SFAG_ERR_PARAM_INVALID, std::string(n.name) + " dtype differs from query");
+  if (sparseIndices->dtype != SFAG_INT32) return fail(SFAG_ERR_PARAM_INVALID, "sparseIndices must be int32");
+  if (softmaxMax->dtype != SFAG_FP32 || softmaxSum->dtype != SFAG_FP32)
+    return fail(SFAG_ERR_PARAM_INVALID, "softmaxMax and softmaxSum must be float32");
+  if ((lensQ && lensQ->dtype != SFAG_INT32) || (lensKv && lensKv->dtype != SFAG_INT32))
+    return fail(SFAG_ERR_PARAM_INVALID, "actual sequence lengths must be int32");
+  for (const Named& n : all)
+    if (n.t && !contiguous(n.t)) return fail(SFAG_ERR_PARAM_INVALID, std::string(n.name) + " is not contiguous");
+  if (!std::isfinite(scaleValue)) return fail(SFAG_ERR_PARAM_INVALID, "scaleValue must be finite");
+
+  // ---- 561002: attributes -------------------------------------------------
+  std::string layout = layoutOptional ? layoutOptional : "BSND";
+  Dims d;
+  if (layout == "BSND") d.layout = 0;
+  else if (layout == "TND") d.layout = 1;
+  else return fail(SFAG_ERR_TILING, "layout must be BSND or TND, got '" + layout + "'");
+  if (sparseMode != 0 && sparseMode != 3) return fail(SFAG_ERR_TILING, "sparseMode must be 0 or 3");
+  if (sparseBlockSize != 1 && sparseBlockSize != 8 && sparseBlockSize != 16 && sparseBlockSize != 32 &&
+      sparseBlockSize != 64)
+    return fail(SFAG_ERR_TILING, "sparseBlockSize must be one of 1, 8, 16, 32, 64");
+  if (preTokens != kWindow || nextTokens != kWindow)
+    return fail(SFAG_ERR_TILING, "preTokens and nextTokens must be 2147483647");
+  d.mode = (int32_t)sparseMode;
+  d.block = sparseBlockSize;
+
+  // ---- 561002: shapes -----------------------------------------------------
+  const int qd = d.layout == 0 ? 4 : 3;
+  if (query->ndim != qd || key->ndim != qd || value->ndim != qd || dOut->ndim != qd || out->ndim != qd ||
+      sparseIndices->ndim != qd)
+    return fail(SFAG_ERR_TILING, "query/key/value/dOut/out/sparseIndices must have " + std::to_string(qd) +
+                                     " dims for layout " + layout);
+  if (d.layout == 0) {
+    d.B = query->shape[0];
+    d.S1 = query->shape[1];
+    d.G = query->shape[2];
+    d.D = query->shape[3];
+    d.S2 = key->shape[1];
+    d.T1 = d.B * d.S1;
+    d.T2 = d.B * d.S2;
+    if (key->shape[0] != d.B) return fail(SFAG_ERR_TILING, "key batch differs from query batch");
+    if (d.B > kMaxBatch) return fail(SFAG_ERR_TILING, "B must be at most 256");
+    if (d.S1 > kMaxTokensPerSeq || d.S2 > kMaxTokensPerSeq) return fail(SFAG_ERR_TILING, "S1 and S2 must be at most 128K");
+  } else {
+    d.T1 = query->shape[0];
+    d.G = query->shape[1];
+    d.D = query->shape[2];
+    d.T2 = key->shape[0];
+    if (!lensQ || !lensKv) return fail(SFAG_ERR_TILING, "TND layout needs actualSeqLengthsQuery and actualSeqLengthsKv");
+    if (lensQ->ndim != 1 || lensKv->ndim != 1 || lensQ->shape[0] != lensKv->shape[0])
+      return fail(SFAG_ERR_TILING, "actual sequence lengths must both have shape (B,)");
+    d.B = lensQ->shape[0];
+    if (d.B < 1 || d.B > kMaxBatch) return fail(SFAG_ERR_TILING, "B must be in 1..256");
+    if (d.T1 > kMaxBatch * kMaxTokensPerSeq || d.T2 > kMaxBatch * kMaxTokensPerSeq)
+      return fail(SFAG_ERR_TILING, "T1/T2 exceed 256 sequences of 128K tokens");
+  }
+  const int64_t N2 = key->shape[qd - 2];
+  if (N2 != 1) return fail(SFAG_ERR_TILING, "N2 must be 1 (one shared key/value head)");
+  if (d.D != 512) return fail(SFAG_ERR_TILING, "D must be 512");
+  if (d.G < 1 || d.G > 128) return fail(SFAG_ERR_TILING, "N1 must be in 1..128");
+  if (key->shape[qd - 1] != d.D) return fail(SFAG_ERR_TILING, "key last dim must equal query's (512)");
+  if (!same_shape(value, key)) return fail(SFAG_ERR_TILING, "value shape must equal key shape");
+  if (!same_shape(dOut, query) || !same_shape(out, query)) return fail(SFAG_ERR_TILING, "dOut and out must have query's shape");
+  d.K = sparseIndices->shape[qd - 1];
+  const bool idx_ok = d.layout == 0 ? shape_is(sparseIndices, {d.B, d.S1, 1, d.K}) : shape_is(sparseIndices, {d.T1, 1, d.K});
+  if (!idx_ok) return fail(SFAG_ERR_TILING, "sparseIndices shape " + shape_str(sparseIndices) + " does not match query");
+  const bool st_ok = d.layout == 0 ? shape_is(softmaxMax, {d.B, 1, d.S1, d.G}) && shape_is(softmaxSum, {d.B, 1, d.S1, d.G})
+                                   : shape_is(softmaxMax, {1, d.T1, d.G}) && shape_is(softmaxSum, {1, d.T1, d.G});
+  if (!st_ok) return fail(SFAG_ERR_TILING, "softmaxMax/softmaxSum must be (B,1,S1,N1) or (1,T1,N1)");
+  if (rope) {
+    d.Dr = queryRope->shape[queryRope->ndim - 1];
+    if (d.Dr != 64) return fail(SFAG_ERR_TILING, "Drope must be 64");
+    const bool qr_ok = d.layout == 0 ? shape_is(queryRope, {d.B, d.S1, d.G, 64}) : shape_is(queryRope, {d.T1, d.G, 64});
+    const bool kr_ok = d.layout == 0 ? shape_is(keyRope, {d.B, d.S2, 1, 64}) : shape_is(keyRope, {d.T2, 1, 64});
+    if (!qr_ok || !kr_ok) return fail(SFAG_ERR_TILING, "queryRope/keyRope shapes do not match query/key");
+    if (!same_shape(dQueryRopeOut, queryRope) || !same_shape(dKeyRopeOut, keyRope))
+      return fail(SFAG_ERR_TILING, "rope gradient outputs must match the rope inputs");
+  }
+  if (!same_shape(dQueryOut, query) || !same_shape(dKeyOut, key) || !same_shape(dValueOut, value))
+    return fail(SFAG_ERR_TILING, "gradient outputs must match their inputs' shapes");
+
+  d.E = d.K * d.block;
+  d.Gp = d.G <= 16 ? 16 : (d.G + 31) / 32 * 32;
+  d.AW = 2 * d.D + d.Dr;
+  int bits = 1;
+  while (((int64_t)1 << bits) <= d.T2) ++bits;
+  d.sort_bits = bits;
+
+  auto* p = new (std::nothrow) sfag_plan();
+  if (!p) return fail(SFAG_ERR_RUNTIME, "out of host memory");
+  p->q = query->data; p->k = key->data; p->v = value->data; p->idx = sparseIndices->data;
+  p->dout = dOut->data; p->out = out->data; p->smax = softmaxMax->data; p->ssum = softmaxSum->data;
+  p->lq = d.layout == 1 ? lensQ->data : nullptr;
+  p->lk = d.layout == 1 ? lensKv->data : nullptr;
+  p->qr = rope ? queryRope->data : nullptr; p->kr = rope ? keyRope->data : nullptr;
+  p->dq = dQueryOut->data; p->dk = dKeyOut->data; p->dv = dValueOut->data;
+  p->dqr = rope ? dQueryRopeOut->data : nullptr; p->dkr = rope ? dKeyRopeOut->data : nullptr;
+  p->dtype = ft;
+  p->deterministic = deterministic;
+  p->scale = (float)scaleValue;
+
+  // Scatter of the dK/dV partial rows: the deterministic mode always reduces
+  // key-centrically over the CSR; otherwise fp32 atomics unless overridden.
+  const char* sc_env = std::getenv("SFAG_SCATTER");
+  const bool want_partials = sc_env && std::strcmp(sc_env, "partials") == 0;
+  p->scatter = (deterministic || want_partials) ? kScatterPartials : kScatterAtomic;
+  const bool partials = p->scatter == kScatterPartials;
+
+  if (d.T1 == 0) {  // empty query: the outputs are zero-filled, no workspace
+    d.chunk = 0;
+    p->d = d;
+    p->ws = WorkspaceLayout();
+    *workspaceSize = 0;
+    *plan = p;
+    return SFAG_OK;
+  }
+  // Tokens per chunk: the chunk's buffers (index rows, dS/P, and for the
+  // partials scatter the partial rows and the sort buffers) within a budget.
+  uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
+  if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
+  const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 16384);
+  int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
+  const int64_t forced = env_i64("SFAG_CHUNK_TOKENS", 0);
+  if (forced > 0) chunk = forced;
+  if (chunk < 1) chunk = 1;
+  if (chunk > d.T1) chunk = d.T1;
+  if (d.E > 0 && chunk > (int64_t)(0x7fffffffLL / d.E)) chunk = 0x7fffffffLL / d.E;
+  if (chunk < 1) {
+    delete p;
+    return fail(SFAG_ERR_TILING, "K * sparseBlockSize too large for 32-bit pair indices");
+  }
+  d.chunk = chunk;
+  p->d = d;
+  p->ws = layout_for(d, partials);
+  *workspaceSize = p->ws.total;
+  *plan = p;
+  return SFAG_OK;
+}

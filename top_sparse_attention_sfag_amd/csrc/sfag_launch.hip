@@ -1,0 +1,324 @@
+// Phase 2 of the two-phase call (the operator page's aclnnSparseFlashAttentionGrad
+// execute step): carve the caller's workspace and enqueue the kernels on the
+// caller's stream.  Also the stand-alone index inversion entry point.
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sfag_device.h"
+#include "sfag_kernels.h"
+#include "sfag_plan.h"
+
+using namespace sfag;
+
+namespace {
+
+int fail(int code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SFAG_ERR_RUNTIME, std::string(what) + ": " + hipGetErrorString(e));
+  return SFAG_OK;
+}
+
+template <typename T>
+T* at(void* base, uint64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+// Optional per-kernel timing: HIP events recorded on the caller's stream
+// around each kernel group, read back (and accumulated per name) on demand.
+struct PendingTiming {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<PendingTiming> g_prof_pending;
+std::map<std::string, std::pair<double, int64_t>> g_prof_acc;
+
+struct TimedScope {
+  bool on;
+  PendingTiming t;
+  hipStream_t s;
+  TimedScope(const char* name, hipStream_t stream) : on(false), s(stream) {
+    {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      on = g_prof_on;
+    }
+    if (!on) return;
+    t.name = name;
+    if (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess) {
+      on = false;
+      return;
+    }
+    (void)hipEventRecord(t.start, s);
+  }
+  ~TimedScope() {
+    if (!on) return;
+    (void)hipEventRecord(t.stop, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending.push_back(t);
+  }
+};
+
+void prof_drain() {
+  for (PendingTiming& t : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.stop) == hipSuccess && hipEventElapsedTime(&ms, t.start, t.stop) == hipSuccess) {
+      auto& a = g_prof_acc[t.name];
+      a.first += ms;
+      a.second += 1;
+    }
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_prof_pending.clear();
+}
+
+}  // namespace
+
+extern "C" void sfag_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+}
+
+extern "C" void sfag_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_drain();
+  g_prof_acc.clear();
+}
+
+extern "C" int sfag_profile_read(const char* name, double* total_ms, int64_t* launches) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_drain();
+  auto it = g_prof_acc.find(name ? name : "");
+  if (total_ms) *total_ms = it == g_prof_acc.end() ? 0.0 : it->second.first;
+  if (launches) *launches = it == g_prof_acc.end() ? 0 : it->second.second;
+  return SFAG_OK;
+}
+
+extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream) {
+  set_error("");
+  std::unique_ptr<sfag_plan> own(plan);
+  if (!plan) return fail(SFAG_ERR_NULLPTR, "plan is NULL");
+  const Dims& d = plan->d;
+  const WorkspaceLayout& w = plan->ws;
+  if (workspaceSize < w.total) return fail(SFAG_ERR_PARAM_INVALID, "workspace smaller than the phase-1 size");
+  if (w.total > 0 && !workspace) return fail(SFAG_ERR_NULLPTR, "workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const bool rope = d.Dr > 0;
+
+  if (d.T1 == 0) {  // empty query (约束说明: return directly); dK/dV are still defined as 0
+    launch_fill_u32(plan->dk, (uint64_t)d.T2 * d.D / 2, 0u, s);
+    launch_fill_u32(plan->dv, (uint64_t)d.T2 * d.D / 2, 0u, s);
+    if (rope) launch_fill_u32(plan->dkr, (uint64_t)d.T2 * d.Dr / 2, 0u, s);
+    return check_launch("zero fill");
+  }
+
+  int32_t* q_off = nullptr;
+  int32_t* kv_off = nullptr;
+  if (d.layout == 1) {
+    q_off = at<int32_t>(workspace, w.seq_off);
+    kv_off = q_off + (d.B + 1);
+    TimedScope ts("seq_offsets", s);
+    launch_seq_offsets((const int32_t*)plan->lq, (const int32_t*)plan->lk, (int32_t)d.B, q_off, kv_off, s);
+  }
+  float* delta = at<float>(workspace, w.delta);
+  float* acc = at<float>(workspace, w.acc);
+  int32_t* nvalid = at<int32_t>(workspace, w.nvalid);
+  int32_t* rows = at<int32_t>(workspace, w.rows);
+  uint16_t* ds = at<uint16_t>(workspace, w.ds);
+  uint16_t* pb = at<uint16_t>(workspace, w.p);
+  {
+    TimedScope ts("delta", s);
+    launch_delta(plan->dtype, plan->dout, plan->out, delta, d.T1 * d.G, s);
+  }
+  {
+    TimedScope ts("fill", s);
+    launch_fill_u32(acc, (uint64_t)d.T2 * d.AW, 0u, s);
+  }
+
+  // fp16 keeps dS above its subnormal range by a power-of-two factor that the
+  // dQ and dK epilogues divide out again.
+  const float ds_scale = plan->dtype == SFAG_FP16 ? 256.f : 1.f;
+  const bool partial = plan->scatter == kScatterPartials;
+
+  RowArgs ra;
+  ra.q = (const uint16_t*)plan->q;
+  ra.qr = (const uint16_t*)plan->qr;
+  ra.dO = (const uint16_t*)plan->dout;
+  ra.k = (const uint16_t*)plan->k;
+  ra.kr = (const uint16_t*)plan->kr;
+  ra.v = (const uint16_t*)plan->v;
+  ra.smax = (const float*)plan->smax;
+  ra.ssum = (const float*)plan->ssum;
+  ra.delta = delta;
+  ra.rows = rows;
+  ra.nvalid = nvalid;
+  ra.ds_out = ds;
+  ra.p_out = pb;
+  ra.dq = (uint16_t*)plan->dq;
+  ra.dqr = (uint16_t*)plan->dqr;
+  ra.G = d.G;
+  ra.Gp = d.Gp;
+  ra.E = d.E;
+  ra.n_hb = (int32_t)((d.Gp + 63) / 64);
+  ra.scale_log2 = plan->scale * kLog2e;
+  ra.ds_scale = ds_scale;
+  ra.dq_mul = plan->scale / ds_scale;
+
+  ColArgs ca;
+  ca.q = ra.q;
+  ca.qr = ra.qr;
+  ca.dO = ra.dO;
+  ca.ds = ds;
+  ca.p = pb;
+  ca.rows = rows;
+  ca.nvalid = nvalid;
+  ca.acc = acc;
+  ca.partials = partial ? at<float>(workspace, w.partials) : nullptr;
+  ca.G = d.G;
+  ca.Gp = d.Gp;
+  ca.E = d.E;
+  ca.AW = d.AW;
+
+  int32_t* keys[2] = {nullptr, nullptr};
+  int32_t* vals[2] = {nullptr, nullptr};
+  if (partial) {
+    keys[0] = at<int32_t>(workspace, w.sort_keys[0]);
+    keys[1] = at<int32_t>(workspace, w.sort_keys[1]);
+    vals[0] = at<int32_t>(workspace, w.sort_vals[0]);
+    vals[1] = at<int32_t>(workspace, w.sort_vals[1]);
+  }
+
+  for (int64_t t0 = 0; t0 < d.T1; t0 += d.chunk) {
+    const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
+    {
+      TimedScope ts("decode", s);
+      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s);
+    }
+    ra.t0 = ca.t0 = t0;
+    ra.ntok = ca.ntok = ntok;
+    {
+      TimedScope ts("row", s);
+      launch_row(plan->dtype, rope, ra, s);
+    }
+    {
+      TimedScope ts("col", s);
+      launch_col(plan->dtype, rope, partial, ca, s);
+    }
+    if (partial && d.E > 0) {
+      int32_t* sorted = nullptr;
+      int32_t* off = at<int32_t>(workspace, w.csr_off);
+      {
+        TimedScope ts("csr", s);
+        launch_csr(ntok * d.E, rows, nvalid, d.E, d.T2, d.sort_bits, keys, vals,
+                   at<int32_t>(workspace, w.sort_hist), off, &sorted, s);
+      }
+      TimedScope ts("key_reduce", s);
+      launch_key_reduce(off, sorted, ca.partials, d.AW, d.T2, acc, s);
+    }
+    const int rc = check_launch("chunk kernels");
+    if (rc != SFAG_OK) return rc;
+  }
+  {
+    TimedScope ts("cast", s);
+    launch_cast(plan->dtype, acc, d.T2, (int32_t)d.D, (int32_t)d.Dr, plan->scale / ds_scale, plan->dk, plan->dkr,
+                plan->dv, s);
+  }
+  return check_launch("cast");
+}
+
+namespace {
+
+struct IndexLayout {
+  uint64_t seq_off, keys0, keys1, vals0, vals1, hist, total;
+};
+
+IndexLayout index_layout(int64_t T1, int64_t E) {
+  IndexLayout L;
+  const uint64_t n = (uint64_t)T1 * E;
+  const uint64_t nblk = (n + kSortBlock - 1) / kSortBlock;
+  uint64_t c = 0;
+  auto carve = [&](uint64_t& f, uint64_t bytes) {
+    f = c;
+    c = align256(c + bytes);
+  };
+  carve(L.seq_off, 2 * 257 * 4);
+  carve(L.keys0, n * 4);
+  carve(L.keys1, n * 4);
+  carve(L.vals0, n * 4);
+  carve(L.vals1, n * 4);
+  carve(L.hist, 256 * nblk * 4 + 4);
+  L.total = c;
+  return L;
+}
+
+}  // namespace
+
+extern "C" uint64_t sfag_index_workspace_size(int64_t T1, int64_t T2, int64_t K, int64_t block) {
+  (void)T2;
+  if (T1 < 0 || K < 0 || block < 1) return 0;
+  return index_layout(T1, K * block).total;
+}
+
+extern "C" int sfag_build_index(const void* sparseIndices, const void* seqLensQ, const void* seqLensKv, int64_t B,
+                                int64_t S1, int64_t S2, int64_t T1, int64_t T2, int64_t K, int64_t block,
+                                int32_t layout, int64_t sparseMode, void* workspace, uint64_t workspaceSize,
+                                void* nValid, void* rows, void* csrOffsets, void* csrPairs, void* stream) {
+  set_error("");
+  if (layout != 0 && layout != 1) return fail(SFAG_ERR_TILING, "layout must be 0 (BSND) or 1 (TND)");
+  if (sparseMode != 0 && sparseMode != 3) return fail(SFAG_ERR_TILING, "sparseMode must be 0 or 3");
+  if (block < 1 || K < 0 || T1 < 0 || T2 < 0 || B < 0 || B > 256) return fail(SFAG_ERR_TILING, "bad sizes");
+  if (layout == 0 && (B * S1 != T1 || B * S2 != T2)) return fail(SFAG_ERR_TILING, "BSND needs T1 = B*S1, T2 = B*S2");
+  const int64_t E = K * block;
+  if ((double)T1 * (double)E >= 2147483648.0) return fail(SFAG_ERR_TILING, "T1*K*block must be below 2^31");
+  const IndexLayout L = index_layout(T1, E);
+  if (workspaceSize < L.total) return fail(SFAG_ERR_PARAM_INVALID, "workspace too small");
+  if (!workspace || !csrOffsets || (T1 > 0 && (!sparseIndices || !nValid || !rows || !csrPairs)) ||
+      (layout == 1 && (!seqLensQ || !seqLensKv)))
+    return fail(SFAG_ERR_NULLPTR, "NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  Dims d;
+  d.layout = layout;
+  d.B = B;
+  d.S1 = S1;
+  d.S2 = S2;
+  d.T1 = T1;
+  d.T2 = T2;
+  d.K = K;
+  d.block = block;
+  d.E = E;
+  d.mode = (int32_t)sparseMode;
+  int bits = 1;
+  while (((int64_t)1 << bits) <= T2) ++bits;
+  int32_t* q_off = nullptr;
+  int32_t* kv_off = nullptr;
+  if (layout == 1) {
+    q_off = at<int32_t>(workspace, L.seq_off);
+    kv_off = q_off + (B + 1);
+    launch_seq_offsets((const int32_t*)seqLensQ, (const int32_t*)seqLensKv, (int32_t)B, q_off, kv_off, s);
+  }
+  launch_decode((const int32_t*)sparseIndices, 0, T1, d, q_off, kv_off, (int32_t*)rows, (int32_t*)nValid, s);
+  const int64_t n = T1 * E;
+  if (n == 0) {
+    launch_fill_u32(csrOffsets, (uint64_t)T2 + 1, 0u, s);
+    return check_launch("index");
+  }
+  int32_t* keys[2] = {at<int32_t>(workspace, L.keys0), at<int32_t>(workspace, L.keys1)};
+  int32_t* vals[2] = {at<int32_t>(workspace, L.vals0), at<int32_t>(workspace, L.vals1)};
+  int32_t* sorted = nullptr;
+  launch_csr(n, (const int32_t*)rows, (const int32_t*)nValid, E, T2, bits, keys, vals, at<int32_t>(workspace, L.hist),
+             (int32_t*)csrOffsets, &sorted, s);
+  if (hipMemcpyAsync(csrPairs, sorted, (size_t)n * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return fail(SFAG_ERR_RUNTIME, "copy of the CSR pairs failed");
+  return check_launch("index");
+}

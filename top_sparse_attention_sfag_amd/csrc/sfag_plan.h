@@ -1,0 +1,68 @@
+// Host-side plan shared by the validation unit (plain C++) and the launch unit
+// (HIP).  Holds copies of the caller's pointers and attributes, the derived
+// sizes and the workspace layout; never the data.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "sfag.h"
+
+namespace sfag {
+
+enum Scatter : int32_t { kScatterAtomic = 0, kScatterPartials = 1 };
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct WorkspaceLayout {
+  uint64_t seq_off = 0;    // TND: int32 q_off[B+1], kv_off[B+1]
+  uint64_t delta = 0;      // fp32 (T1, G): rowsum(dO ∘ O)
+  uint64_t acc = 0;        // fp32 (T2, AW): dK | dKrope | dV accumulators
+  uint64_t nvalid = 0;     // int32 (chunk): valid positions per token of the chunk
+  uint64_t rows = 0;       // int32 (chunk, E): global key row of each valid position
+  uint64_t ds = 0;         // 16-bit (chunk, E, Gp): dS of each (token, position, head)
+  uint64_t p = 0;          // 16-bit (chunk, E, Gp): P
+  uint64_t partials = 0;   // fp32 (chunk, E, AW): per-pair dK|dKr|dV rows (partials scatter)
+  uint64_t sort_keys[2] = {0, 0};  // int32 (chunk*E): radix sort ping-pong
+  uint64_t sort_vals[2] = {0, 0};
+  uint64_t sort_hist = 0;  // int32 (256, nblocks)
+  uint64_t csr_off = 0;    // int32 (T2 + 1)
+  uint64_t total = 0;
+};
+
+struct Dims {
+  int32_t layout = 0;      // 0 BSND, 1 TND
+  int64_t B = 0, S1 = 0, S2 = 0, T1 = 0, T2 = 0;
+  int64_t G = 0, D = 512, Dr = 0;
+  int64_t K = 0, block = 1, E = 0;
+  int32_t mode = 0;
+  int64_t Gp = 0;          // heads padded for the dS/P buffers (16 or a multiple of 32)
+  int64_t AW = 0;          // accumulator row width 2*D + Dr
+  int64_t chunk = 0;       // tokens per chunk
+  int32_t sort_bits = 0;   // bits of the CSR sort key (rows < T2, sentinel T2)
+};
+
+uint64_t align256(uint64_t x);
+
+// Workspace layout for `d` (chunk and flags already set).
+WorkspaceLayout layout_for(const Dims& d, bool partials);
+
+// Radix-sort block geometry shared by host and kernels.
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 16;
+constexpr int kSortBlock = kSortThreads * kSortItems;  // items per sort block
+
+void set_error(const std::string& msg);
+
+}  // namespace sfag
+
+struct sfag_plan {
+  const void *q = nullptr, *k = nullptr, *v = nullptr, *idx = nullptr, *dout = nullptr, *out = nullptr;
+  const void *smax = nullptr, *ssum = nullptr, *lq = nullptr, *lk = nullptr, *qr = nullptr, *kr = nullptr;
+  void *dq = nullptr, *dk = nullptr, *dv = nullptr, *dqr = nullptr, *dkr = nullptr;
+  int32_t dtype = 0;
+  bool deterministic = false;
+  float scale = 0.f;
+  int32_t scatter = 0;
+  sfag::Dims d;
+  sfag::WorkspaceLayout ws;
+};

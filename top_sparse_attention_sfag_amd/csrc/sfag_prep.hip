@@ -1,0 +1,352 @@
+// Bandwidth-bound kernels around the MFMA core: sequence offsets, Delta,
+// accumulator fill, index decode, the stable radix sort that inverts the
+// indices into a key -> (token, position) CSR, the key-centric reduction of
+// per-pair rows, and the final cast.
+#include "sfag_device.h"
+#include "sfag_kernels.h"
+#include "sfag_plan.h"
+
+namespace sfag {
+
+// ---------------------------------------------------------------------------
+// TND: exclusive prefix sums of the per-sequence lengths (parameter table:
+// actualSeqLengthsQuery / actualSeqLengthsKv hold the valid tokens of each
+// sequence).  Negative lengths count as 0.  One block, B <= 256.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B,
+                                                     int32_t* q_off, int32_t* kv_off) {
+  __shared__ int32_t sq[257], sk[257];
+  const int t = threadIdx.x;
+  if (t < B) {
+    sq[t + 1] = max(lq[t], 0);
+    sk[t + 1] = max(lk[t], 0);
+  }
+  if (t == 0) sq[0] = sk[0] = 0;
+  __syncthreads();
+  if (t == 0) {
+    for (int b = 1; b <= B; ++b) {
+      sq[b] += sq[b - 1];
+      sk[b] += sk[b - 1];
+    }
+  }
+  __syncthreads();
+  if (t <= B) {
+    q_off[t] = sq[t];
+    kv_off[t] = sk[t];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Delta[t][h] = Σ_d dO[t][h][d] · O[t][h][d] in fp32 (the page's
+// FlashSoftmaxGrad(dO, O), stage 2).  One wave per (token, head) row of 512.
+// ---------------------------------------------------------------------------
+template <typename TT>
+__global__ void __launch_bounds__(256) k_delta(const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
+                                               float* __restrict__ delta, int64_t nrows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= nrows) return;
+  const uint4 a = *(const uint4*)(dO + row * 512 + lane * 8);
+  const uint4 b = *(const uint4*)(O + row * 512 + lane * 8);
+  const uint16_t* pa = (const uint16_t*)&a;
+  const uint16_t* pb = (const uint16_t*)&b;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = fmaf(TT::to_f(pa[i]), TT::to_f(pb[i]), s);
+  s = wave_sum(s);
+  if (lane == 0) delta[row] = s;
+}
+
+__global__ void __launch_bounds__(256) k_fill_u32(uint32_t* __restrict__ p, uint64_t n, uint32_t v) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 4;
+  for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      *(uint4*)(p + i) = make_uint4(v, v, v, v);
+    } else {
+      for (uint64_t j = i; j < n; ++j) p[j] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Index decode (功能说明: gather of sparseBlockSize rows per index; Mask table:
+// sparseMode 0 / 3).  Position e = j*block + r of token t is p = idx[t][j] + r,
+// valid iff idx[t][j] >= 0, p < Lk and (mode 3) p <= t_loc + Lk - Lq.  The
+// valid positions are compacted in position order: rows[tl][c] = kv_base + p.
+// One block per token of the chunk.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx, int64_t t0, int64_t K, int32_t block,
+                                                int32_t mode, int32_t layout, int64_t S1, int64_t S2,
+                                                const int32_t* q_off, const int32_t* kv_off, int32_t B, int64_t T2,
+                                                int32_t* __restrict__ rows, int32_t* __restrict__ nvalid) {
+  const int64_t tl = blockIdx.x;
+  const int64_t t = t0 + tl;
+  const int64_t E = K * block;
+  __shared__ int32_t warp_tot[4];
+  __shared__ int32_t base_s;
+  const TokenGeo g = token_geo(t, layout, S1, S2, q_off, kv_off, B);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) base_s = 0;
+  __syncthreads();
+  int32_t* out = rows + tl * E;
+  for (int64_t e0 = 0; e0 < E; e0 += 256) {
+    const int64_t e = e0 + tid;
+    bool valid = false;
+    int64_t row = 0;
+    if (e < E && g.ok) {
+      const int64_t j = e / block, r = e - j * block;
+      const int32_t ent = idx[t * K + j];
+      const int64_t p = (int64_t)ent + r;
+      valid = ent >= 0 && p < g.Lk && (mode != 3 || p <= g.bound);
+      row = g.kv_base + p;
+      valid = valid && row < T2;
+    }
+    const uint64_t bal = __ballot(valid);
+    const int rank = __popcll(bal & ((1ull << lane) - 1));
+    if (lane == 0) warp_tot[w] = __popcll(bal);
+    __syncthreads();
+    int off = base_s;
+    for (int i = 0; i < w; ++i) off += warp_tot[i];
+    if (valid) out[off + rank] = (int32_t)row;
+    __syncthreads();
+    if (tid == 0) base_s += warp_tot[0] + warp_tot[1] + warp_tot[2] + warp_tot[3];
+    __syncthreads();
+  }
+  if (tid == 0) nvalid[tl] = base_s;
+}
+
+// ---------------------------------------------------------------------------
+// Stable LSD radix sort of (key, value) pairs, 8 bits per pass, used to group
+// the valid pairs by key row while keeping ascending pair order inside a key.
+// Item i of the chunk is pair (tl = i / E, c = i % E); its key is the key row
+// when c < nvalid[tl] and the sentinel T2 otherwise.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load_item(int64_t i, int pass, const int32_t* keys_in, const int32_t* vals_in,
+                                          const int32_t* rows, const int32_t* nvalid, int64_t E, int32_t sentinel,
+                                          int32_t& key, int32_t& val) {
+  if (pass == 0) {
+    const int64_t tl = i / E, c = i - tl * E;
+    key = c < nvalid[tl] ? rows[i] : sentinel;
+    val = (int32_t)i;
+  } else {
+    key = keys_in[i];
+    val = vals_in[i];
+  }
+}
+
+__global__ void __launch_bounds__(kSortThreads) k_sort_hist(int64_t n, int pass, const int32_t* keys_in,
+                                                            const int32_t* vals_in, const int32_t* rows,
+                                                            const int32_t* nvalid, int64_t E, int32_t sentinel,
+                                                            int32_t* __restrict__ hist, int64_t nblk) {
+  __shared__ int32_t h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t b0 = (int64_t)blockIdx.x * kSortBlock;
+  for (int k = 0; k < kSortItems; ++k) {
+    const int64_t i = b0 + (int64_t)k * kSortThreads + threadIdx.x;
+    if (i < n) {
+      int32_t key, val;
+      load_item(i, pass, keys_in, vals_in, rows, nvalid, E, sentinel, key, val);
+      atomicAdd(&h[(key >> (8 * pass)) & 255], 1);
+    }
+  }
+  __syncthreads();
+  hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+}
+
+// Exclusive scan of n int32 counts in place (one block of 1024 threads).
+__global__ void __launch_bounds__(1024) k_scan(int32_t* __restrict__ a, int64_t n) {
+  __shared__ int32_t part[1024];
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t s = threadIdx.x * per, e = min(n, s + per);
+  int32_t sum = 0;
+  for (int64_t i = s; i < e; ++i) sum += a[i];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - sum;
+  for (int64_t i = s; i < e; ++i) {
+    const int32_t v = a[i];
+    a[i] = run;
+    run += v;
+  }
+}
+
+__global__ void __launch_bounds__(kSortThreads) k_sort_scatter(int64_t n, int pass, const int32_t* keys_in,
+                                                               const int32_t* vals_in, const int32_t* rows,
+                                                               const int32_t* nvalid, int64_t E, int32_t sentinel,
+                                                               const int32_t* __restrict__ hist, int64_t nblk,
+                                                               int32_t* __restrict__ keys_out,
+                                                               int32_t* __restrict__ vals_out) {
+  __shared__ int32_t run[256];
+  __shared__ int32_t cnt[kSortThreads / 64][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  run[tid] = hist[(int64_t)tid * nblk + blockIdx.x];
+  for (int i = 0; i < kSortThreads / 64; ++i) cnt[i][tid] = 0;
+  __syncthreads();
+  const int64_t b0 = (int64_t)blockIdx.x * kSortBlock;
+  for (int k = 0; k < kSortItems; ++k) {
+    const int64_t i = b0 + (int64_t)k * kSortThreads + tid;
+    const bool in = i < n;
+    int32_t key = 0, val = 0;
+    if (in) load_item(i, pass, keys_in, vals_in, rows, nvalid, E, sentinel, key, val);
+    const int d = in ? (key >> (8 * pass)) & 255 : 256;
+    // lanes of this wave holding the same digit
+    uint64_t peers = __ballot(in);
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t bal = __ballot(((d >> b) & 1) != 0);
+      peers &= ((d >> b) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1));
+    const bool leader = in && rank == 0;
+    if (leader) cnt[w][d] = __popcll(peers);
+    __syncthreads();
+    if (in) {
+      int pos = run[d] + rank;
+      for (int ww = 0; ww < w; ++ww) pos += cnt[ww][d];
+      keys_out[pos] = key;
+      vals_out[pos] = val;
+    }
+    __syncthreads();
+    int add = 0;
+    for (int ww = 0; ww < kSortThreads / 64; ++ww) {
+      add += cnt[ww][tid];
+      cnt[ww][tid] = 0;
+    }
+    run[tid] += add;
+    __syncthreads();
+  }
+}
+
+// csr_off[p] = number of sorted keys < p, p in [0, T2].
+__global__ void __launch_bounds__(256) k_csr_offsets(const int32_t* __restrict__ keys, int64_t n, int64_t T2,
+                                                     int32_t* __restrict__ off) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p > T2) return;
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (keys[mid] < p) lo = mid + 1;
+    else hi = mid;
+  }
+  off[p] = (int32_t)lo;
+}
+
+// Key-centric reduction (deterministic path): for each key row p, the partial
+// rows of its pairs are summed in CSR (ascending pair) order and added to the
+// accumulator.  One block per key row; fixed order, so bitwise reproducible.
+__global__ void __launch_bounds__(256) k_key_reduce(const int32_t* __restrict__ off, const int32_t* __restrict__ pairs,
+                                                    const float* __restrict__ part, int64_t AW,
+                                                    float* __restrict__ acc) {
+  const int64_t p = blockIdx.x;
+  const int32_t s = off[p], e = off[p + 1];
+  if (s == e) return;
+  for (int64_t col = threadIdx.x; col < AW; col += 256) {
+    float sum = 0.f;
+    for (int32_t i = s; i < e; ++i) sum += part[(int64_t)pairs[i] * AW + col];
+    acc[p * AW + col] += sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cast: dK = scale·acc[:, :D] / ds_scale, dKrope likewise, dV = acc[:, D+Dr:],
+// rounded to the output type (round to nearest even).
+// ---------------------------------------------------------------------------
+template <typename TT>
+__global__ void __launch_bounds__(256) k_cast(const float* __restrict__ acc, int64_t T2, int32_t D, int32_t Dr,
+                                              float kscale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dkr,
+                                              uint16_t* __restrict__ dv) {
+  const int64_t AW = 2 * D + Dr;
+  const int64_t n = T2 * AW;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / AW, c = i - r * AW;
+    const float x = acc[i];
+    if (c < D) dk[r * D + c] = TT::from_f(x * kscale);
+    else if (c < D + Dr) dkr[r * Dr + (c - D)] = TT::from_f(x * kscale);
+    else dv[r * D + (c - D - Dr)] = TT::from_f(x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static inline unsigned grid_for(uint64_t n, unsigned per_block, unsigned cap = 65536) {
+  uint64_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int32_t* q_off, int32_t* kv_off,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_seq_offsets, dim3(1), dim3(256), 0, s, lq, lk, B, q_off, kv_off);
+}
+
+void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, int64_t nrows, hipStream_t s) {
+  if (nrows == 0) return;
+  const dim3 grid((unsigned)((nrows + 3) / 4));
+  if (dtype == SFAG_BF16)
+    hipLaunchKernelGGL(k_delta<BF16>, grid, dim3(256), 0, s, (const uint16_t*)dO, (const uint16_t*)O, delta, nrows);
+  else
+    hipLaunchKernelGGL(k_delta<FP16>, grid, dim3(256), 0, s, (const uint16_t*)dO, (const uint16_t*)O, delta, nrows);
+}
+
+void launch_fill_u32(void* p, uint64_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return;
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n, 1024, 8192)), dim3(256), 0, s, (uint32_t*)p, n, v);
+}
+
+void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, const int32_t* q_off,
+                   const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s) {
+  if (ntok == 0) return;
+  hipLaunchKernelGGL(k_decode, dim3((unsigned)ntok), dim3(256), 0, s, idx, t0, d.K, (int32_t)d.block, d.mode,
+                     d.layout, d.S1, d.S2, q_off, kv_off, (int32_t)d.B, d.T2, rows, nvalid);
+}
+
+void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E, int64_t T2, int32_t sort_bits,
+                int32_t* keys[2], int32_t* vals[2], int32_t* hist, int32_t* csr_off, int32_t** sorted_vals,
+                hipStream_t s) {
+  const int64_t nblk = (n + kSortBlock - 1) / kSortBlock;
+  const int npass = (sort_bits + 7) / 8;
+  int cur = 0;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int32_t* kin = pass ? keys[cur] : nullptr;
+    const int32_t* vin = pass ? vals[cur] : nullptr;
+    const int nxt = pass ? cur ^ 1 : 0;
+    hipLaunchKernelGGL(k_sort_hist, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows, nvalid,
+                       E, (int32_t)T2, hist, nblk);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, 256 * nblk);
+    hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows,
+                       nvalid, E, (int32_t)T2, hist, nblk, keys[nxt], vals[nxt]);
+    cur = nxt;
+  }
+  hipLaunchKernelGGL(k_csr_offsets, dim3(grid_for(T2 + 1, 256, 1u << 30)), dim3(256), 0, s, keys[cur], n, T2,
+                     csr_off);
+  *sorted_vals = vals[cur];
+}
+
+void launch_key_reduce(const int32_t* off, const int32_t* pairs, const float* part, int64_t AW, int64_t T2, float* acc,
+                       hipStream_t s) {
+  if (T2 == 0) return;
+  hipLaunchKernelGGL(k_key_reduce, dim3((unsigned)T2), dim3(256), 0, s, off, pairs, part, AW, acc);
+}
+
+void launch_cast(int32_t dtype, const float* acc, int64_t T2, int32_t D, int32_t Dr, float kscale, void* dk, void* dkr,
+                 void* dv, hipStream_t s) {
+  const uint64_t n = (uint64_t)T2 * (2 * D + Dr);
+  if (n == 0) return;
+  const dim3 grid(grid_for(n, 256 * 8, 16384));
+  if (dtype == SFAG_BF16)
+    hipLaunchKernelGGL(k_cast<BF16>, grid, dim3(256), 0, s, acc, T2, D, Dr, kscale, (uint16_t*)dk, (uint16_t*)dkr,
+                       (uint16_t*)dv);
+  else
+    hipLaunchKernelGGL(k_cast<FP16>, grid, dim3(256), 0, s, acc, T2, D, Dr, kscale, (uint16_t*)dk, (uint16_t*)dkr,
+                       (uint16_t*)dv);
+}
+
+}  // namespace sfag

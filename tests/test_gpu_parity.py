@@ -170,18 +170,33 @@ def test_deterministic_independent_of_chunking(monkeypatch):
         assert torch.equal(a, b)
 
 
-def test_atomic_and_partials_paths_agree(monkeypatch):
-    case = si.Case("paths", S1=50, S2=90, G=64, K=60, mode=3, index_rule="causal_mix")
+@pytest.mark.parametrize("path", ["keyblock", "atomic", "partials"])
+@pytest.mark.parametrize("chunk", [0, 9])
+def test_scatter_paths_agree(monkeypatch, path, chunk):
+    """Every dK/dV path (key-block contraction, fp32 atomics, per-pair rows with
+    the CSR reduction), with and without token chunking, against the oracle."""
+    case = si.Case("paths", S1=50, S2=300, G=64, K=60, mode=3, index_rule="causal_mix")
     inp = add_oracle_stats(case, si.make_inputs(case, 8))
     ref = oracle_backward(case, inp)
     dev = to_device(inp)
-    a = _outs_np(case, call_backward(case, dev, deterministic=False))
-    monkeypatch.setenv("SFAG_SCATTER", "partials")
-    b = _outs_np(case, call_backward(case, dev, deterministic=False))
-    monkeypatch.setenv("SFAG_CHUNK_TOKENS", "9")
-    c = _outs_np(case, call_backward(case, dev, deterministic=False))
-    for got in (a, b, c):
-        _check(case, got, ref, label="paths")
+    monkeypatch.setenv("SFAG_SCATTER", path)
+    if chunk:
+        monkeypatch.setenv("SFAG_CHUNK_TOKENS", str(chunk))
+    got = _outs_np(case, call_backward(case, dev, deterministic=False))
+    _check(case, got, ref, label=f"paths {path} chunk {chunk}")
+
+
+@pytest.mark.parametrize("path", ["keyblock", "partials"])
+def test_deterministic_paths_bitwise(monkeypatch, path):
+    case = si.Case("detpaths", S1=40, S2=260, G=32, K=50, mode=3, index_rule="zipf", deterministic=True)
+    inp = to_device(add_oracle_stats(case, si.make_inputs(case, 4)))
+    monkeypatch.setenv("SFAG_SCATTER", path)
+    first = [o.clone() for o in call_backward(case, inp) if o is not None]
+    for _ in range(2):
+        again = [o for o in call_backward(case, inp) if o is not None]
+        torch.cuda.synchronize()
+        for x, y in zip(first, again):
+            assert torch.equal(x, y)
 
 
 def test_build_index_bit_exact():

@@ -346,3 +346,27 @@ def test_csr_properties():
         seg = pairs[off[key]:off[key + 1]]
         assert np.all(keys[seg] == key)
         assert np.all(np.diff(seg) > 0)
+
+
+def test_sampled_rows_equal_full_backward():
+    """The one-row-at-a-time evaluation used at full sizes equals the full
+    backward pass on the sampled rows (including a duplicated index, rows
+    past the causal bound and a token with no valid position)."""
+    p = _problem(51, S1=6, S2=12, G=3, D=8, Dr=4, Kent=7, mode=3, neg_frac=0.25, dup=True)
+    scale = 0.33
+    O, M, L = orc.forward(p["q"], p["k"], p["v"], p["qr"], p["kr"], p["idx"], p["geom"], 1, 3, scale)
+    g = orc.backward(p["q"], p["k"], p["v"], p["qr"], p["kr"], p["idx"], p["dO"], O, M, L, p["geom"], 1, 3, scale)
+    tokens, keys = [0, 2, 5], [0, 3, 7, 11]
+    r = orc.backward_rows(p["q"], p["k"], p["v"], p["qr"], p["kr"], p["idx"], p["dO"], O, M, L, p["geom"], 1, 3,
+                          scale, tokens=tokens, keys=keys, batch=2)
+    np.testing.assert_allclose(r["dq"], g["dq"][tokens], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dqr"], g["dqr"][tokens], rtol=1e-12, atol=1e-13)
+    for n in ("dk", "dv", "dkr"):
+        np.testing.assert_allclose(r[n], g[n][keys], rtol=1e-12, atol=1e-13, err_msg=n)
+    # token-subset backward: the same rows and the same per-key sums
+    sub = orc.backward(p["q"], p["k"], p["v"], p["qr"], p["kr"], p["idx"], p["dO"], O, M, L, p["geom"], 1, 3, scale,
+                       tokens=[1, 4])
+    rest = orc.backward(p["q"], p["k"], p["v"], p["qr"], p["kr"], p["idx"], p["dO"], O, M, L, p["geom"], 1, 3, scale,
+                        tokens=[0, 2, 3, 5])
+    for n in ("dk", "dv", "dkr"):
+        np.testing.assert_allclose(sub[n] + rest[n], g[n], rtol=1e-12, atol=1e-13)

@@ -81,7 +81,8 @@ def lib():
     return _lib
 
 
-KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "col", "csr", "key_reduce", "cast")
+KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "col", "csr", "key_reduce", "transpose", "kb_sort",
+                 "keyblock", "kb_reduce", "cast")
 
 
 def profile_enable(on: bool = True):

@@ -23,7 +23,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
-HIP_SOURCES = ["sfag_prep.hip", "sfag_mfma.hip", "sfag_launch.hip"]
+HIP_SOURCES = ["sfag_prep.hip", "sfag_row.hip", "sfag_mfma.hip", "sfag_keyblock.hip", "sfag_launch.hip"]
 HOST_SOURCES = ["sfag_host.cpp"]
 
 

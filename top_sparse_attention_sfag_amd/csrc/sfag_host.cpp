@@ -28,7 +28,9 @@ static void carve(uint64_t& cursor, uint64_t& field, uint64_t bytes) {
   cursor = align256(cursor + bytes);
 }
 
-WorkspaceLayout layout_for(const Dims& d, bool partials) {
+WorkspaceLayout layout_for(const Dims& d, int32_t scatter) {
+  const bool partials = scatter == kScatterPartials;
+  const bool keyblock = scatter == kScatterKeyBlock;
   WorkspaceLayout w;
   uint64_t c = 0;
   const uint64_t ch = (uint64_t)d.chunk, E = (uint64_t)d.E;
@@ -49,6 +51,19 @@ WorkspaceLayout layout_for(const Dims& d, bool partials) {
     carve(c, w.sort_vals[1], n * 4);
     carve(c, w.sort_hist, 256 * nblk * 4);
     carve(c, w.csr_off, (uint64_t)(d.T2 + 1) * 4);
+  }
+  if (keyblock) {
+    const uint64_t n = ch * E;
+    const uint64_t nblk = (n + kSortBlock - 1) / kSortBlock;
+    carve(c, w.sort_keys[0], n * 4);
+    carve(c, w.sort_keys[1], n * 4);
+    carve(c, w.sort_vals[0], n * 4);
+    carve(c, w.sort_vals[1], n * 4);
+    carve(c, w.sort_hist, 256 * nblk * 4);
+    carve(c, w.qT, ch * (uint64_t)(d.D + d.Dr) * d.Gp * 2);
+    carve(c, w.oT, ch * (uint64_t)d.D * d.Gp * 2);
+    carve(c, w.kb_part, (uint64_t)d.nTR * d.T2 * d.AW * 4);
+    carve(c, w.kb_nonempty, (uint64_t)d.nTR * d.nKB * 4);
   }
   w.total = c;
   return w;
@@ -272,12 +287,31 @@ extern "C" int sfag_workspace_size(
   p->deterministic = deterministic;
   p->scale = (float)scaleValue;
 
-  // Scatter of the dK/dV partial rows: the deterministic mode always reduces
-  // key-centrically over the CSR; otherwise fp32 atomics unless overridden.
-  const char* sc_env = std::getenv("SFAG_SCATTER");
-  const bool want_partials = sc_env && std::strcmp(sc_env, "partials") == 0;
-  p->scatter = (deterministic || want_partials) ? kScatterPartials : kScatterAtomic;
+  // dK/dV path.  When a token selects a sizeable fraction of the keys it can
+  // reach (estimated from the shapes alone), the key-block contraction wins:
+  // it moves no per-pair rows and is deterministic.  Otherwise the per-pair
+  // rows go through the CSR reduction (deterministic) or fp32 atomics.
+  // SFAG_SCATTER=atomic|partials|keyblock overrides the choice (the atomic
+  // path is never used when deterministic is requested).
+  {
+    double reach;  // average number of key positions a token may select
+    if (d.layout == 0) {
+      reach = d.mode == 3 ? (double)d.S2 - (double)d.S1 + 0.5 * (double)(d.S1 + 1) : (double)d.S2;
+    } else {
+      const double lk = d.B > 0 ? (double)d.T2 / (double)d.B : 0.0;
+      reach = d.mode == 3 ? 0.5 * lk : lk;
+    }
+    if (reach < 1.0) reach = 1.0;
+    const double density = (double)d.E / reach;
+    int32_t sc = density >= 0.125 ? kScatterKeyBlock : (deterministic ? kScatterPartials : kScatterAtomic);
+    const char* env = std::getenv("SFAG_SCATTER");
+    if (env && std::strcmp(env, "keyblock") == 0) sc = kScatterKeyBlock;
+    if (env && std::strcmp(env, "partials") == 0) sc = kScatterPartials;
+    if (env && std::strcmp(env, "atomic") == 0) sc = deterministic ? kScatterPartials : kScatterAtomic;
+    p->scatter = sc;
+  }
   const bool partials = p->scatter == kScatterPartials;
+  const bool keyblock = p->scatter == kScatterKeyBlock;
 
   if (d.T1 == 0) {  // empty query: the outputs are zero-filled, no workspace
     d.chunk = 0;
@@ -291,6 +325,7 @@ extern "C" int sfag_workspace_size(
   // partials scatter the partial rows and the sort buffers) within a budget.
   uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
   if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
+  if (keyblock) per_tok += 4 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
   const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 16384);
   int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
   const int64_t forced = env_i64("SFAG_CHUNK_TOKENS", 0);
@@ -303,8 +338,22 @@ extern "C" int sfag_workspace_size(
     return fail(SFAG_ERR_TILING, "K * sparseBlockSize too large for 32-bit pair indices");
   }
   d.chunk = chunk;
+  d.nKB = (d.T2 + kKeyBlockRows - 1) / kKeyBlockRows;
+  if (keyblock) {
+    // up to 16 token ranges per chunk; the key-block sort key must fit in 31 bits
+    d.TR = (chunk + 15) / 16;
+    d.nTR = (chunk + d.TR - 1) / d.TR;
+    const int64_t sentinel = d.nKB * chunk;
+    if (sentinel >= 0x7fffffffLL) {
+      delete p;
+      return fail(SFAG_ERR_TILING, "key-block sort key exceeds 31 bits; lower SFAG_WORKSPACE_BUDGET_MB");
+    }
+    int kbits = 1;
+    while (((int64_t)1 << kbits) <= sentinel) ++kbits;
+    d.kb_sort_bits = kbits;
+  }
   p->d = d;
-  p->ws = layout_for(d, partials);
+  p->ws = layout_for(d, p->scatter);
   *workspaceSize = p->ws.total;
   *plan = p;
   return SFAG_OK;

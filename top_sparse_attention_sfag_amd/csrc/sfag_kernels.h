@@ -20,6 +20,28 @@ struct RowArgs {
   float dq_mul;      // scale / ds_scale
 };
 
+constexpr int kKeyBlock = kKeyBlockRows;
+constexpr int kMaxColBlocks = 6;
+
+// A block of output columns of the key-centric kernel: `src` 0 contracts dS
+// with [Q|Qr] (dK, dKrope), 1 contracts P with dO (dV); `tcol0` is the first
+// column in the transposed source, `ocol0` the first accumulator column.
+struct ColBlock {
+  int32_t src, tcol0, ocol0, width;
+};
+
+struct KbArgs {
+  const uint16_t *qT, *oT;     // (ntok, 512+Dr, Gp) and (ntok, 512, Gp) transposed Q|Qr and dO
+  const uint16_t *ds, *p;      // (ntok, E, Gp)
+  const int32_t *rows;         // (ntok, E) key row of each valid position
+  const int32_t *skeys, *svals;  // pairs sorted by key block * ntok + token, pair ids
+  int32_t* nonempty;           // (nTR, nKB) flags
+  float* part;                 // (nTR, T2, AW) partial sums per token range
+  int64_t n, ntok, Gp, T2, AW, TR, Dq;
+  int32_t nKB, nTR, nCB;
+  ColBlock cbs[kMaxColBlocks];
+};
+
 struct ColArgs {
   const uint16_t *q, *qr, *dO, *ds, *p;
   const int32_t *rows, *nvalid;
@@ -33,14 +55,22 @@ void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, in
 void launch_fill_u32(void* p, uint64_t n, uint32_t v, hipStream_t s);
 void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, const int32_t* q_off,
                    const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s);
+// Stable radix sort of the chunk's valid pairs.  key_mode 0: by key row (then
+// csr_off gets the per-key offsets); key_mode 1: by (key row / kKeyBlock) *
+// ntok + token (csr_off may be NULL).  Invalid positions sort last.
 void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E, int64_t T2, int32_t sort_bits,
                 int32_t* keys[2], int32_t* vals[2], int32_t* hist, int32_t* csr_off, int32_t** sorted_vals,
-                hipStream_t s);
+                hipStream_t s, int key_mode = 0, int64_t ntok = 0, int32_t** sorted_keys = nullptr);
 void launch_key_reduce(const int32_t* off, const int32_t* pairs, const float* part, int64_t AW, int64_t T2, float* acc,
                        hipStream_t s);
 void launch_cast(int32_t dtype, const float* acc, int64_t T2, int32_t D, int32_t Dr, float kscale, void* dk, void* dkr,
                  void* dv, hipStream_t s);
 void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
+void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO, int64_t t0, int64_t ntok, int64_t G,
+                      int64_t Gp, int32_t Dr, uint16_t* qT, uint16_t* oT, hipStream_t s);
+void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s);
+void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
+                      float* acc, hipStream_t s);
 void launch_col(int32_t dtype, bool rope, bool partial, const ColArgs& a, hipStream_t s);
 
 }  // namespace sfag

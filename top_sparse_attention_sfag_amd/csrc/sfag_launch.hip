@@ -149,6 +149,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   // dQ and dK epilogues divide out again.
   const float ds_scale = plan->dtype == SFAG_FP16 ? 256.f : 1.f;
   const bool partial = plan->scatter == kScatterPartials;
+  const bool keyblock = plan->scatter == kScatterKeyBlock;
 
   RowArgs ra;
   ra.q = (const uint16_t*)plan->q;
@@ -191,7 +192,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
 
   int32_t* keys[2] = {nullptr, nullptr};
   int32_t* vals[2] = {nullptr, nullptr};
-  if (partial) {
+  if (partial || keyblock) {
     keys[0] = at<int32_t>(workspace, w.sort_keys[0]);
     keys[1] = at<int32_t>(workspace, w.sort_keys[1]);
     vals[0] = at<int32_t>(workspace, w.sort_vals[0]);
@@ -210,7 +211,58 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
       TimedScope ts("row", s);
       launch_row(plan->dtype, rope, ra, s);
     }
-    {
+    if (keyblock) {
+      if (d.E > 0) {
+        uint16_t* qT = at<uint16_t>(workspace, w.qT);
+        uint16_t* oT = at<uint16_t>(workspace, w.oT);
+        {
+          TimedScope ts("transpose", s);
+          launch_transpose(ra.q, ra.qr, ra.dO, t0, ntok, d.G, d.Gp, (int32_t)d.Dr, qT, oT, s);
+        }
+        int32_t* skeys = nullptr;
+        int32_t* svals = nullptr;
+        {
+          TimedScope ts("kb_sort", s);
+          launch_csr(ntok * d.E, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals,
+                     at<int32_t>(workspace, w.sort_hist), nullptr, &svals, s, 1, ntok, &skeys);
+        }
+        KbArgs ka;
+        ka.qT = qT;
+        ka.oT = oT;
+        ka.ds = ds;
+        ka.p = pb;
+        ka.rows = rows;
+        ka.skeys = skeys;
+        ka.svals = svals;
+        ka.nonempty = at<int32_t>(workspace, w.kb_nonempty);
+        ka.part = at<float>(workspace, w.kb_part);
+        ka.n = ntok * d.E;
+        ka.ntok = ntok;
+        ka.Gp = d.Gp;
+        ka.T2 = d.T2;
+        ka.AW = d.AW;
+        ka.TR = d.TR;
+        ka.Dq = d.D + d.Dr;
+        ka.nKB = (int32_t)d.nKB;
+        ka.nTR = (int32_t)((ntok + d.TR - 1) / d.TR);
+        // column blocks: dK (two of 256), dKrope (64), dV (two of 256)
+        int m = 0;
+        ka.cbs[m++] = ColBlock{0, 0, 0, 256};
+        ka.cbs[m++] = ColBlock{0, 256, 256, 256};
+        if (rope) ka.cbs[m++] = ColBlock{0, 512, 512, 64};
+        ka.cbs[m++] = ColBlock{1, 0, (int32_t)(d.D + d.Dr), 256};
+        ka.cbs[m++] = ColBlock{1, 256, (int32_t)(d.D + d.Dr) + 256, 256};
+        ka.nCB = m;
+        {
+          TimedScope ts("keyblock", s);
+          launch_keyblock(plan->dtype, ka, s);
+        }
+        {
+          TimedScope ts("kb_reduce", s);
+          launch_kb_reduce(ka.part, ka.nonempty, d.T2, d.AW, ka.nTR, ka.nKB, acc, s);
+        }
+      }
+    } else {
       TimedScope ts("col", s);
       launch_col(plan->dtype, rope, partial, ca, s);
     }

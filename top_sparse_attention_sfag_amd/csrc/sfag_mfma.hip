@@ -24,152 +24,7 @@
 
 namespace sfag {
 
-constexpr int kRowTile = 32;  // gathered positions per k_row tile
 constexpr int kColTile = 16;  // positions per k_col tile
-
-template <typename TT, int DR>
-__global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
-  constexpr int DQK = 512 + DR;
-  constexpr int KS_QK = DQK / 32;  // k-steps of the logits contraction
-  constexpr int KS_V = 512 / 32;
-  constexpr int NB_Q = DQK / 16;   // 16-column blocks of dQ
-  constexpr int KSTR = DQK + 8;    // LDS row strides (elements), keep 16-byte alignment
-  constexpr int VSTR = 512 + 8;
-  constexpr int CK = DQK / 8;      // 16-byte chunks of a K(+Kr) row
-  constexpr int CPR = CK + 64;
-  typedef typename TT::vec8 V8;
-
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kRowTile * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kRowTile * VSTR];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
-  const int64_t tl = blockIdx.x / a.n_hb;
-  const int hb = blockIdx.x - (int)tl * a.n_hb;
-  const int64_t t = a.t0 + tl;
-  const int h0 = hb * 64 + wave * 16;
-  const bool wave_on = h0 < a.Gp;
-  const int h = h0 + n;
-  const bool hv = h < a.G;
-
-  V8 Qf[KS_QK], dOf[KS_V];
-#pragma unroll
-  for (int ks = 0; ks < KS_QK; ++ks) {
-    const int d0 = 32 * ks + 8 * g;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (wave_on && hv) {
-      if (d0 < 512) u = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
-      else u = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
-    }
-    Qf[ks] = as_vec8<V8>(u);
-  }
-#pragma unroll
-  for (int ks = 0; ks < KS_V; ++ks) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (wave_on && hv) u = *(const uint4*)(a.dO + (t * a.G + h) * 512 + 32 * ks + 8 * g);
-    dOf[ks] = as_vec8<V8>(u);
-  }
-  float mlog = 0.f, inv_l = 0.f, dl = 0.f;
-  bool live = false;
-  if (wave_on && hv) {
-    const float m = a.smax[t * a.G + h], l = a.ssum[t * a.G + h];
-    live = l > 0.f;
-    inv_l = live ? 1.f / l : 0.f;
-    mlog = m * kLog2e;
-    dl = a.delta[t * a.G + h];
-  }
-  f32x4 acc[NB_Q];
-#pragma unroll
-  for (int i = 0; i < NB_Q; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nv = a.nvalid[tl];
-  const int32_t* rt = a.rows + tl * a.E;
-  for (int c0 = 0; c0 < nv; c0 += kRowTile) {
-    __syncthreads();
-    for (int i = tid; i < kRowTile * CPR; i += 256) {
-      const int r = i / CPR, j = i - r * CPR;
-      const int c = c0 + r;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (c < nv) {
-        const int64_t key = rt[c];
-        if (j < 64) val = *(const uint4*)(a.k + key * 512 + j * 8);
-        else if (j < CK) val = *(const uint4*)(a.kr + key * DR + (j - 64) * 8);
-        else val = *(const uint4*)(a.v + key * 512 + (j - CK) * 8);
-      }
-      if (j < CK) *(uint4*)(Ks + r * KSTR + j * 8) = val;
-      else *(uint4*)(Vs + r * VSTR + (j - CK) * 8) = val;
-    }
-    __syncthreads();
-    if (!wave_on) continue;
-
-    // Sᵀ and dPᵀ for two blocks of 16 positions: rows = positions, columns = heads.
-    f32x4 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = Ks + (mb * 16 + n) * KSTR + 8 * g;
-      const uint16_t* vr = Vs + (mb * 16 + n) * VSTR + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < KS_QK; ++ks) s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)(kr + 32 * ks)), Qf[ks], s[mb]);
-#pragma unroll
-      for (int ks = 0; ks < KS_V; ++ks) dp[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)(vr + 32 * ks)), dOf[ks], dp[mb]);
-    }
-    // P = exp(scale·S − max)/sum, dS = P ∘ (dP − Delta); lane holds head h and
-    // positions 4g+i (block 0) and 16+4g+i (block 1).
-    uint16_t pv[8], dsv[8];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = mb * 16 + 4 * g + i;
-        const bool ok = live && (c0 + j < nv);
-        const float p = ok ? exp2f(s[mb][i] * a.scale_log2 - mlog) * inv_l : 0.f;
-        const float ds = p * (dp[mb][i] - dl);
-        pv[mb * 4 + i] = TT::from_f(p);
-        dsv[mb * 4 + i] = TT::from_f(ds * a.ds_scale);
-      }
-    }
-    const uint4 dsu = make_uint4(dsv[0] | ((uint32_t)dsv[1] << 16), dsv[2] | ((uint32_t)dsv[3] << 16),
-                                 dsv[4] | ((uint32_t)dsv[5] << 16), dsv[6] | ((uint32_t)dsv[7] << 16));
-    const V8 A8 = as_vec8<V8>(dsu);
-    // dQ += dS·K over the 32 positions; K fragments come transposed from LDS.
-    const uint16_t* b1 = Ks + (4 * g + (n >> 2)) * KSTR + 4 * (n & 3);
-    const uint16_t* b2 = b1 + 16 * KSTR;
-#pragma unroll
-    for (int nb = 0; nb < NB_Q; ++nb) {
-      const V8 B8 = join_tr<V8>(lds_read_tr(b1 + 16 * nb), lds_read_tr(b2 + 16 * nb));
-      acc[nb] = TT::mfma(A8, B8, acc[nb]);
-    }
-    if (h < a.Gp) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = c0 + mb * 16 + 4 * g + i;
-          if (c < nv) {
-            const int64_t o = (tl * a.E + c) * a.Gp + h;
-            a.ds_out[o] = dsv[mb * 4 + i];
-            a.p_out[o] = pv[mb * 4 + i];
-          }
-        }
-      }
-    }
-  }
-  if (!wave_on) return;
-#pragma unroll
-  for (int nb = 0; nb < NB_Q; ++nb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = h0 + 4 * g + i;
-      if (hh < a.G) {
-        const int col = 16 * nb + n;
-        const uint16_t u = TT::from_f(acc[nb][i] * a.dq_mul);
-        if (col < 512) a.dq[(t * a.G + hh) * 512 + col] = u;
-        else a.dqr[(t * a.G + hh) * DR + (col - 512)] = u;
-      }
-    }
-  }
-}
 
 // PART 0: dK|dKr partial rows = dSᵀ·[Q|Qr]; PART 1: dV partial rows = Pᵀ·dO.
 template <typename TT, int DR, int PART, bool PARTIAL>
@@ -257,18 +112,6 @@ __global__ void __launch_bounds__(256, 1) k_col(ColArgs a) {
         for (int nb = 0; nb < NB; ++nb) unsafeAtomicAdd(dst + 16 * nb, o[nb][i]);
       }
     }
-  }
-}
-
-void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.ntok * a.n_hb)), block(256);
-  if (a.ntok == 0) return;
-  if (dtype == SFAG_BF16) {
-    if (rope) hipLaunchKernelGGL((k_row<BF16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_row<BF16, 0>), grid, block, 0, s, a);
-  } else {
-    if (rope) hipLaunchKernelGGL((k_row<FP16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_row<FP16, 0>), grid, block, 0, s, a);
   }
 }
 

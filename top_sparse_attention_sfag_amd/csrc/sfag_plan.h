@@ -10,7 +10,12 @@
 
 namespace sfag {
 
-enum Scatter : int32_t { kScatterAtomic = 0, kScatterPartials = 1 };
+// How the per-(token, position) dK/dV contributions reach the key rows:
+//   kScatterAtomic   fp32 atomic adds of each pair's row into the accumulators;
+//   kScatterPartials each pair's row stored, then summed per key in CSR order;
+//   kScatterKeyBlock contraction per block of 128 key rows over the tokens
+//                    selecting them (pairs sorted by key block and token).
+enum Scatter : int32_t { kScatterAtomic = 0, kScatterPartials = 1, kScatterKeyBlock = 2 };
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
@@ -26,6 +31,10 @@ struct WorkspaceLayout {
   uint64_t sort_vals[2] = {0, 0};
   uint64_t sort_hist = 0;  // int32 (256, nblocks)
   uint64_t csr_off = 0;    // int32 (T2 + 1)
+  uint64_t qT = 0;         // 16-bit (chunk, 512 + Dr, Gp): per-token transposed Q|Qr
+  uint64_t oT = 0;         // 16-bit (chunk, 512, Gp): per-token transposed dO
+  uint64_t kb_part = 0;    // fp32 (nTR, T2, AW): per token-range partial sums
+  uint64_t kb_nonempty = 0;  // int32 (nTR, nKB)
   uint64_t total = 0;
 };
 
@@ -39,12 +48,19 @@ struct Dims {
   int64_t AW = 0;          // accumulator row width 2*D + Dr
   int64_t chunk = 0;       // tokens per chunk
   int32_t sort_bits = 0;   // bits of the CSR sort key (rows < T2, sentinel T2)
+  int32_t kb_sort_bits = 0;  // bits of the key-block sort key (sentinel nKB * chunk)
+  int64_t nKB = 0;         // key blocks of 128 rows
+  int64_t TR = 0;          // tokens per range of the key-block kernel
+  int64_t nTR = 0;         // token ranges per chunk
 };
 
 uint64_t align256(uint64_t x);
 
 // Workspace layout for `d` (chunk and flags already set).
-WorkspaceLayout layout_for(const Dims& d, bool partials);
+WorkspaceLayout layout_for(const Dims& d, int32_t scatter);
+
+// Key rows per block of the key-centric dK/dV contraction.
+constexpr int kKeyBlockRows = 128;
 
 // Radix-sort block geometry shared by host and kernels.
 constexpr int kSortThreads = 256;

@@ -123,10 +123,11 @@ __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx,
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void load_item(int64_t i, int pass, const int32_t* keys_in, const int32_t* vals_in,
                                           const int32_t* rows, const int32_t* nvalid, int64_t E, int32_t sentinel,
-                                          int32_t& key, int32_t& val) {
+                                          int32_t& key, int32_t& val, int key_mode, int64_t ntok) {
   if (pass == 0) {
     const int64_t tl = i / E, c = i - tl * E;
-    key = c < nvalid[tl] ? rows[i] : sentinel;
+    if (c < nvalid[tl]) key = key_mode == 0 ? rows[i] : (int32_t)((int64_t)(rows[i] / kKeyBlock) * ntok + tl);
+    else key = sentinel;
     val = (int32_t)i;
   } else {
     key = keys_in[i];
@@ -137,7 +138,8 @@ __device__ __forceinline__ void load_item(int64_t i, int pass, const int32_t* ke
 __global__ void __launch_bounds__(kSortThreads) k_sort_hist(int64_t n, int pass, const int32_t* keys_in,
                                                             const int32_t* vals_in, const int32_t* rows,
                                                             const int32_t* nvalid, int64_t E, int32_t sentinel,
-                                                            int32_t* __restrict__ hist, int64_t nblk) {
+                                                            int32_t* __restrict__ hist, int64_t nblk, int key_mode,
+                                                            int64_t ntok) {
   __shared__ int32_t h[256];
   h[threadIdx.x] = 0;
   __syncthreads();
@@ -146,7 +148,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_hist(int64_t n, int pass,
     const int64_t i = b0 + (int64_t)k * kSortThreads + threadIdx.x;
     if (i < n) {
       int32_t key, val;
-      load_item(i, pass, keys_in, vals_in, rows, nvalid, E, sentinel, key, val);
+      load_item(i, pass, keys_in, vals_in, rows, nvalid, E, sentinel, key, val, key_mode, ntok);
       atomicAdd(&h[(key >> (8 * pass)) & 255], 1);
     }
   }
@@ -182,7 +184,8 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_scatter(int64_t n, int pa
                                                                const int32_t* nvalid, int64_t E, int32_t sentinel,
                                                                const int32_t* __restrict__ hist, int64_t nblk,
                                                                int32_t* __restrict__ keys_out,
-                                                               int32_t* __restrict__ vals_out) {
+                                                               int32_t* __restrict__ vals_out, int key_mode,
+                                                               int64_t ntok) {
   __shared__ int32_t run[256];
   __shared__ int32_t cnt[kSortThreads / 64][256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -194,7 +197,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_scatter(int64_t n, int pa
     const int64_t i = b0 + (int64_t)k * kSortThreads + tid;
     const bool in = i < n;
     int32_t key = 0, val = 0;
-    if (in) load_item(i, pass, keys_in, vals_in, rows, nvalid, E, sentinel, key, val);
+    if (in) load_item(i, pass, keys_in, vals_in, rows, nvalid, E, sentinel, key, val, key_mode, ntok);
     const int d = in ? (key >> (8 * pass)) & 255 : 256;
     // lanes of this wave holding the same digit
     uint64_t peers = __ballot(in);
@@ -310,24 +313,28 @@ void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, 
 
 void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E, int64_t T2, int32_t sort_bits,
                 int32_t* keys[2], int32_t* vals[2], int32_t* hist, int32_t* csr_off, int32_t** sorted_vals,
-                hipStream_t s) {
+                hipStream_t s, int key_mode, int64_t ntok, int32_t** sorted_keys) {
   const int64_t nblk = (n + kSortBlock - 1) / kSortBlock;
   const int npass = (sort_bits + 7) / 8;
+  // key_mode 1 sorts by key block * ntok + token; its sentinel is past the last block
+  const int32_t sentinel = key_mode == 0 ? (int32_t)T2 : (int32_t)(((T2 + kKeyBlock - 1) / kKeyBlock) * ntok);
   int cur = 0;
   for (int pass = 0; pass < npass; ++pass) {
     const int32_t* kin = pass ? keys[cur] : nullptr;
     const int32_t* vin = pass ? vals[cur] : nullptr;
     const int nxt = pass ? cur ^ 1 : 0;
     hipLaunchKernelGGL(k_sort_hist, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows, nvalid,
-                       E, (int32_t)T2, hist, nblk);
+                       E, sentinel, hist, nblk, key_mode, ntok);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, 256 * nblk);
     hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows,
-                       nvalid, E, (int32_t)T2, hist, nblk, keys[nxt], vals[nxt]);
+                       nvalid, E, sentinel, hist, nblk, keys[nxt], vals[nxt], key_mode, ntok);
     cur = nxt;
   }
-  hipLaunchKernelGGL(k_csr_offsets, dim3(grid_for(T2 + 1, 256, 1u << 30)), dim3(256), 0, s, keys[cur], n, T2,
-                     csr_off);
+  if (csr_off)
+    hipLaunchKernelGGL(k_csr_offsets, dim3(grid_for(T2 + 1, 256, 1u << 30)), dim3(256), 0, s, keys[cur], n, T2,
+                       csr_off);
   *sorted_vals = vals[cur];
+  if (sorted_keys) *sorted_keys = keys[cur];
 }
 
 void launch_key_reduce(const int32_t* off, const int32_t* pairs, const float* part, int64_t AW, int64_t T2, float* acc,

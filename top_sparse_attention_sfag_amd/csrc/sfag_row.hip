@@ -1,0 +1,258 @@
+// Token-centric MFMA kernel: for one query token and a block of 64 of its
+// heads, recompute the logits of every selected key, form P, dP, dS
+// (operator page "aclnnSparseFlashAttentionGrad", 功能说明 stages 1-2) and
+// accumulate dQ = scale·dS·K_sel (stage 3).  P and dS leave as 16-bit
+// (token, position, head) rows for the head-contraction kernels.
+//
+// gfx950 mapping:
+//   * 4 waves, each owning 16 heads; v_mfma_f32_16x16x32 with the positions
+//     as M for Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ (B operands: the wave's Q / dO rows,
+//     resident in registers) and the heads as M for dQ (A operand: dS straight
+//     from the Sᵀ accumulator layout; B operand: K read transposed from LDS
+//     with ds_read_b64_tr_b16).  The fp32 dQ accumulator stays in registers.
+//   * The 32 gathered K | Krope | V rows of the next tile are fetched with
+//     global_load_lds_dwordx4 (global -> LDS without registers) into the other
+//     half of a double buffer while the current tile is computed.
+//   * LDS rows are stored with their 16-byte chunks XOR-swizzled by (row & 7)
+//     so that the 16 rows an MFMA operand reads at one column fall into
+//     different bank groups.
+//   * Work units are ordered so that each XCD (blockIdx % 8) takes runs of 16
+//     consecutive tokens: neighbouring tokens share many selected keys, which
+//     then hit in that XCD's L2.
+#include "sfag_device.h"
+#include "sfag_kernels.h"
+#include "sfag_plan.h"
+
+namespace sfag {
+
+namespace {
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+constexpr int kTile = 32;          // positions per tile
+constexpr int kXcds = 8;           // XCDs of an MI355X; blockIdx % 8 picks the XCD
+constexpr int kRun = 16;           // consecutive tokens per XCD run
+
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 16, 0, 0);
+}
+
+}  // namespace
+
+template <typename TT, int DR>
+__global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int KS_QK = DQK / 32;
+  constexpr int KS_V = 512 / 32;
+  constexpr int NB_Q = DQK / 16;
+  constexpr int KM_BYTES = kTile * 1024;        // K main part of a tile
+  constexpr int KR_BYTES = kTile * DR * 2;      // K rope part
+  constexpr int V_BYTES = kTile * 1024;
+  constexpr int BUF = KM_BYTES + KR_BYTES + V_BYTES;
+  constexpr int STAGE = kTile * 64 * 2;         // one 32 x 64 16-bit staging tile
+  typedef typename TT::vec8 V8;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF + 2 * STAGE];
+  unsigned char* stage_ds = smem + 2 * BUF;
+  unsigned char* stage_p = stage_ds + STAGE;
+
+  // ---- work unit: (token, head block), XCD-aware order ---------------------
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, u = b / kXcds;
+  const int hb = u % a.n_hb;
+  const int tq = u / a.n_hb;
+  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int h0 = hb * 64 + wave * 16;
+  const bool wave_on = h0 < a.Gp;
+  const int h = h0 + n;
+  const bool hv = h < a.G;
+
+  V8 Qf[KS_QK], dOf[KS_V];
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (wave_on && hv) {
+      if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
+      else v = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
+    }
+    Qf[ks] = as_vec8<V8>(v);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS_V; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (wave_on && hv) v = *(const uint4*)(a.dO + (t * a.G + h) * 512 + 32 * ks + 8 * g);
+    dOf[ks] = as_vec8<V8>(v);
+  }
+  float mlog = 0.f, inv_l = 0.f, dl = 0.f;
+  bool live = false;
+  if (wave_on && hv) {
+    const float m = a.smax[t * a.G + h], l = a.ssum[t * a.G + h];
+    live = l > 0.f;
+    inv_l = live ? 1.f / l : 0.f;
+    mlog = m * kLog2e;
+    dl = a.delta[t * a.G + h];
+  }
+  f32x4 acc[NB_Q];
+#pragma unroll
+  for (int i = 0; i < NB_Q; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+
+  // Gather the 32 rows of tile c0 into buffer `buf`; rows past nv repeat a
+  // valid row (their dS is exactly 0).  Wave w loads rows 8w..8w+7.
+  auto issue_tile = [&](int c0, int buf) {
+    unsigned char* base = smem + buf * BUF;
+    const int r_l = wave * 8 + (lane >> 3);  // rope row handled by this lane
+    const int c_l = c0 + r_l;
+    const int key_l = rt[c_l < nv ? c_l : 0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = wave * 8 + j;
+      const int64_t key = __builtin_amdgcn_readfirstlane(__shfl(key_l, j * 8, 64));
+      const int gc = lane ^ (r & 7);
+      lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
+      lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+    }
+    if (DR > 0) {
+      const int pc = lane & 7;
+      const int gc = pc ^ (r_l & 7);
+      lds_load16(a.kr + (int64_t)key_l * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
+    }
+  };
+
+  // Per-lane LDS byte offsets (relative to a buffer).  Chunk index c of row r
+  // sits at chunk (c & ~7) | ((c & 7) ^ (r & 7)); for the rows and chunks each
+  // lane touches this reduces to a few bases plus immediate offsets.
+  const int x = n & 7;                                 // (row & 7) of rows mb*16 + n
+  const int oA_even = n * 1024 + 16 * (g ^ x);         // chunk 4ks+g, ks even
+  const int oA_odd = n * 1024 + 16 * ((4 + g) ^ x);    // ks odd
+  const int oR_even = n * (DR * 2) + 16 * (g ^ x);     // rope chunk g
+  const int oR_odd = n * (DR * 2) + 16 * ((4 + g) ^ x);  // rope chunk 4+g
+  const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;       // dQ B operand rows r1, r1+16
+  const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
+  int oT[4], oTr[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    oT[w] = r1 * 1024 + 16 * ((2 * w + half) ^ x1) + hoff;
+    oTr[w] = r1 * (DR * 2) + 16 * ((2 * w + half) ^ x1) + hoff;
+  }
+
+  if (nv > 0) issue_tile(0, 0);
+  int cur = 0;
+  for (int c0 = 0; c0 < nv; c0 += kTile) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c0 + kTile < nv) issue_tile(c0 + kTile, cur ^ 1);
+    const unsigned char* Km = smem + cur * BUF;
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Vm = Km + KM_BYTES + KR_BYTES;
+    if (wave_on) {
+      f32x4 s[2], dp[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* ke = Km + oA_even + mb * 16384;
+        const unsigned char* ko = Km + oA_odd + mb * 16384;
+        const unsigned char* ve = Vm + oA_even + mb * 16384;
+        const unsigned char* vo = Vm + oA_odd + mb * 16384;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const unsigned char* p = ((ks & 1) ? ko : ke) + 128 * (ks >> 1);
+          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), Qf[ks], s[mb]);
+        }
+        if (DR > 0) {
+          const unsigned char* re = Kr + oR_even + mb * 16 * (DR * 2);
+          const unsigned char* ro = Kr + oR_odd + mb * 16 * (DR * 2);
+          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)re), Qf[KS_QK - 2], s[mb]);
+          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)ro), Qf[KS_QK - 1], s[mb]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS_V; ++ks) {
+          const unsigned char* p = ((ks & 1) ? vo : ve) + 128 * (ks >> 1);
+          dp[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), dOf[ks], dp[mb]);
+        }
+      }
+      // P = exp(scale·S − max)/sum and dS = P ∘ (dP − Delta) for head h and
+      // positions 4g+i (block 0) and 16+4g+i (block 1).
+      uint16_t pv[8], dsv[8];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = mb * 16 + 4 * g + i;
+          const bool ok = live && (c0 + j < nv);
+          const float p = ok ? exp2f(s[mb][i] * a.scale_log2 - mlog) * inv_l : 0.f;
+          const float ds = p * (dp[mb][i] - dl);
+          pv[mb * 4 + i] = TT::from_f(p);
+          dsv[mb * 4 + i] = TT::from_f(ds * a.ds_scale);
+          const int so = (j * 64 + wave * 16 + n) * 2;
+          *(uint16_t*)(stage_ds + so) = dsv[mb * 4 + i];
+          *(uint16_t*)(stage_p + so) = pv[mb * 4 + i];
+        }
+      }
+      const uint4 dsu = make_uint4(dsv[0] | ((uint32_t)dsv[1] << 16), dsv[2] | ((uint32_t)dsv[3] << 16),
+                                   dsv[4] | ((uint32_t)dsv[5] << 16), dsv[6] | ((uint32_t)dsv[7] << 16));
+      const V8 A8 = as_vec8<V8>(dsu);
+      // dQ += dS·K over the tile's 32 positions: B operand = K rows
+      // 4g..4g+3 and 16+4g..16+4g+3 of one column, read transposed.
+#pragma unroll
+      for (int nb = 0; nb < NB_Q; ++nb) {
+        const unsigned char* p1 = nb < 32 ? Km + oT[nb & 3] + 128 * (nb >> 2) : Kr + oTr[nb & 3];
+        const unsigned char* p2 = p1 + (nb < 32 ? 16 * 1024 : 16 * (DR * 2));
+        const V8 B8 = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)p2));
+        acc[nb] = TT::mfma(A8, B8, acc[nb]);
+      }
+    }
+    __syncthreads();
+    // P and dS of the tile: 32 positions x 64 heads each, one 16-byte chunk
+    // per thread and array.
+    {
+      const int j = tid >> 3, q = tid & 7;
+      const int hh = hb * 64 + q * 8;
+      if (c0 + j < nv && hh < a.Gp) {
+        const int64_t o = (tl * a.E + c0 + j) * a.Gp + hh;
+        *(uint4*)(a.ds_out + o) = *(const uint4*)(stage_ds + (j * 64 + q * 8) * 2);
+        *(uint4*)(a.p_out + o) = *(const uint4*)(stage_p + (j * 64 + q * 8) * 2);
+      }
+    }
+    cur ^= 1;
+  }
+  if (!wave_on) return;
+#pragma unroll
+  for (int nb = 0; nb < NB_Q; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = h0 + 4 * g + i;
+      if (hh < a.G) {
+        const int col = 16 * nb + n;
+        const uint16_t v = TT::from_f(acc[nb][i] * a.dq_mul);
+        if (col < 512) a.dq[(t * a.G + hh) * 512 + col] = v;
+        else a.dqr[(t * a.G + hh) * DR + (col - 512)] = v;
+      }
+    }
+  }
+}
+
+void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s) {
+  if (a.ntok == 0) return;
+  const int64_t per = (int64_t)kXcds * kRun;
+  const int64_t padded = (a.ntok + per - 1) / per * per;
+  const dim3 grid((unsigned)(padded * a.n_hb)), block(256);
+  if (dtype == SFAG_BF16) {
+    if (rope) hipLaunchKernelGGL((k_row<BF16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_row<BF16, 0>), grid, block, 0, s, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((k_row<FP16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_row<FP16, 0>), grid, block, 0, s, a);
+  }
+}
+
+}  // namespace sfag

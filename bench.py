@@ -55,6 +55,167 @@ def _alg_bytes(case, n_pairs):
     return T1 * per_token + n_pairs * per_pair + T2 * per_key
 
 
+# Algorithmic flops per valid (head, selected position) pair of each MFMA
+# kernel: S over D+Dr and dP over D (sdp); dQ over D+Dr (dq); both (row);
+# dK over D and dV over D (keyblock); dKrope over Dr (keyblock_rope); dK over
+# D+Dr and dV over D (col).
+def _unit_flops(case, kernel):
+    D, Dr = case.D, case.Dr
+    return {"sdp": 2 * (2 * D + Dr), "dq": 2 * (D + Dr), "row": 2 * (3 * D + 2 * Dr),
+            "keyblock": 2 * 2 * D, "keyblock_rope": 2 * Dr, "col": 2 * (2 * D + Dr)}.get(kernel)
+
+
+def _kernel_bytes(case, kernel, n_pairs):
+    """Algorithmic HBM bytes of one step of a kernel group: every operand read
+    once and every result written once (no re-reads)."""
+    e = 2
+    G, D, Dr, T1, T2 = case.G, case.D, case.Dr, case.T1, case.T2
+    if kernel == "row":
+        # Q, Qrope, dO, stats, indices in; dQ, dQrope out; per pair the
+        # gathered K|Krope|V row in and the 16-bit dS and P out.
+        return (T1 * (G * (2 * (D + Dr) + D) * e + G * 12 + case.Kent * 4)
+                + n_pairs * ((2 * D + Dr) * e + 2 * G * e))
+    if kernel == "keyblock":
+        # per pair dS and P in; per token Q and dO in; per key the fp32 dK|dV
+        # partial out.
+        return n_pairs * 2 * G * e + T1 * G * 2 * D * e + T2 * 2 * D * 4
+    return _alg_bytes(case, n_pairs)
+
+
+def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
+    uf = _unit_flops(case, kernel)
+    if uf is not None and case.G >= 32:
+        achieved = n_pairs * case.G * uf / launches_per_step / (kernel_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s")
+    else:
+        achieved = _kernel_bytes(case, kernel, n_pairs) / launches_per_step / (kernel_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return roof
+
+
+def _traffic(case, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary of
+    this workload (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
+    calibration), or None when there is none or the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    h = hashlib.sha256()
+    for src in k["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != k["sources_sha256"]:
+        return None
+    return k["bytes_per_launch"]
+
+
+# Kernel groups of the timing API and the kernels (by demangled name) and
+# sources each one stands for.
+_CSRC = "top_sparse_attention_sfag_amd/csrc/"
+_COMMON = [_CSRC + "sfag_kernels.h", _CSRC + "sfag_device.h", _CSRC + "sfag_plan.h",
+           "top_sparse_attention_sfag_amd/build.py"]
+_GROUPS = {
+    "sdp": (r"k_sdp<", [_CSRC + "sfag_sdp.hip"]),
+    "dq": (r"k_dq<", [_CSRC + "sfag_sdp.hip"]),
+    "row": (r"k_row<", [_CSRC + "sfag_row.hip"]),
+    "keyblock": (r"k_keyblock<[^,]*, 4>", [_CSRC + "sfag_keyblock.hip"]),
+    "keyblock_rope": (r"k_keyblock<[^,]*, 1>", [_CSRC + "sfag_keyblock.hip"]),
+    "transpose": (r"k_transpose", [_CSRC + "sfag_keyblock.hip"]),
+    "col": (r"k_col<", [_CSRC + "sfag_mfma.hip"]),
+}
+
+
+def _read_csvs(root, suffix):
+    import csv
+    rows = []
+    for dp, _dn, fn in os.walk(root):
+        for f in fn:
+            if f.endswith(suffix):
+                with open(os.path.join(dp, f), newline="") as fh:
+                    rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _summarize_profiles(d, config, calib_mb):
+    """Turn rocprofv3 CSV output (``-f csv``) into the committed summaries:
+    profiles/<workload>_kernel_stats.txt (kernel trace statistics) and
+    profiles/traffic_<workload>.json (HBM bytes per launch from FETCH_SIZE
+    and WRITE_SIZE, scaled by what the same counters read for one plain
+    elementwise copy of ``calib_mb`` MiB)."""
+    import hashlib
+    import re
+
+    import sfag_inputs as si
+    case = si.CONFIGS[config]
+    cmds = open(os.path.join(d, "commands.txt")).read().strip() if os.path.exists(
+        os.path.join(d, "commands.txt")) else "(commands not recorded)"
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+
+    stats = _read_csvs(os.path.join(d, "trace"), "kernel_stats.csv")
+    lines = [f"# rocprofv3 kernel statistics: {case.name}", "",
+             "Commands (from the repository root; OUT is an output directory):", "", cmds,
+             f"python3 bench.py --summarize-profiles $OUT --config {config} --calib-copy-mb {calib_mb}", "",
+             f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'total ms':>10} {'%':>6}"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        if "sfag" not in name:
+            continue
+        lines.append(f"{name[:72]:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f}")
+    with open(os.path.join(out_dir, f"{case.name}_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(kind):
+        acc = {}
+        for r in _read_csvs(os.path.join(d, kind), "counter_collection.csv"):
+            if r.get("Counter_Name") not in ("FETCH_SIZE", "WRITE_SIZE"):
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = per_kernel("fetch"), per_kernel("write")
+    traffic = {"workload": case.name, "commands": cmds, "calibration": None, "kernels": {}}
+    if calib_mb:
+        # the calibration copy: the elementwise add that bench.py launches
+        cand = [(max(v), k) for k, v in fetch.items() if "CUDAFunctorOnSelf_add<int>" in k]
+        wc = [(max(v), k) for k, v in write.items() if "CUDAFunctorOnSelf_add<int>" in k]
+        if cand and wc:
+            kib = calib_mb * 1024.0
+            ff, fk = max(cand)
+            wf, wk = max(wc)
+            traffic["calibration"] = dict(copy_MiB=calib_mb, kernel=fk[:120], fetch_KiB=ff, write_KiB=wf,
+                                          fetch_factor=kib / ff, write_factor=kib / wf)
+    cal = traffic["calibration"] or dict(fetch_factor=1.0, write_factor=1.0)
+    for g, (pat, srcs) in _GROUPS.items():
+        fv = [v for k, vs in fetch.items() if re.search(pat, k) for v in vs]
+        wv = [v for k, vs in write.items() if re.search(pat, k) for v in vs]
+        if not fv or not wv:
+            continue
+        h = hashlib.sha256()
+        for src in srcs + _COMMON:
+            with open(os.path.join(ROOT, src), "rb") as fh:
+                h.update(fh.read())
+        fb = sum(fv) / len(fv) * 1024 * cal["fetch_factor"]
+        wb = sum(wv) / len(wv) * 1024 * cal["write_factor"]
+        traffic["kernels"][g] = dict(dispatches=len(fv), fetch_bytes=fb, write_bytes=wb, bytes_per_launch=fb + wb,
+                                     sources=srcs + _COMMON, sources_sha256=h.hexdigest())
+    with open(os.path.join(out_dir, f"traffic_{case.name}.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+    print(json.dumps({g: round(v["bytes_per_launch"] / 1e9, 3) for g, v in traffic["kernels"].items()}))
+    return 0
+
+
 def _cpu_baseline(case, inp, seed, target_s=15.0):
     """The oracle as it stands, on one host thread, over a seeded sample of
     tokens: each sampled token's full backward (its dQ row and its dK/dV
@@ -107,7 +268,13 @@ def main(argv=None):
     ap.add_argument("--deterministic", choices=("config", "true", "false"), default="config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="summarize rocprofv3 CSV output under DIR/{trace,fetch,write} into profiles/ and exit")
     args = ap.parse_args(argv)
+    if args.summarize_profiles:
+        return _summarize_profiles(args.summarize_profiles, args.config, args.calib_copy_mb)
     if args.gpus != 1:
         print("bench.py measures a single GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -146,6 +313,14 @@ def main(argv=None):
     def step():
         sfag.backward(*args_pos, outputs=outs, workspace=ws, stream=stream, **kw)
 
+    if args.calib_copy_mb:
+        # one elementwise kernel that reads and writes calib_copy_mb MiB each
+        src = torch.ones((args.calib_copy_mb << 20) // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -172,19 +347,8 @@ def main(argv=None):
     dom = max(prof, key=lambda k: prof[k][0])
     dom_ms = prof[dom][0] / prof[dom][1]
     launches_per_step = prof[dom][1] / args.steps
-    if dom == "row":
-        unit_flops = 2 * (2 * (case.D + case.Dr) + case.D)       # S, dQ over D+Dr; dP over D
-        achieved = n_pairs * case.G * unit_flops / launches_per_step / (dom_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s")
-    elif dom == "col":
-        unit_flops = 2 * (2 * case.D + case.Dr)                  # dK over D+Dr, dV over D
-        achieved = n_pairs * case.G * unit_flops / launches_per_step / (dom_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s")
-    else:
-        achieved = alg_bytes / launches_per_step / (dom_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof = _roofline(case, dom, dom_ms, launches_per_step, n_pairs)
+    roof["traffic"] = _traffic(case, dom)
     roof["kernel"] = dom
     roof["kernel_ms"] = dom_ms
 

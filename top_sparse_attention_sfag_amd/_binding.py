@@ -81,8 +81,8 @@ def lib():
     return _lib
 
 
-KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "col", "csr", "key_reduce", "transpose", "kb_sort",
-                 "keyblock", "kb_reduce", "cast")
+KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "sdp", "dq", "col", "csr", "key_reduce", "transpose", "kb_sort",
+                 "keyblock", "keyblock_rope", "kb_reduce", "cast")
 
 
 def profile_enable(on: bool = True):

@@ -23,7 +23,15 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
-HIP_SOURCES = ["sfag_prep.hip", "sfag_row.hip", "sfag_mfma.hip", "sfag_keyblock.hip", "sfag_launch.hip"]
+# Per-file scheduling: the MFMA kernels fed from LDS schedule for
+# instruction-level parallelism (several operand reads in flight ahead of the
+# MFMAs that consume them); the register-bound k_row keeps the default.
+FILE_FLAGS = {
+    "sfag_sdp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "sfag_keyblock.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+HIP_SOURCES = ["sfag_prep.hip", "sfag_row.hip", "sfag_sdp.hip", "sfag_mfma.hip", "sfag_keyblock.hip",
+               "sfag_launch.hip"]
 HOST_SOURCES = ["sfag_host.cpp"]
 
 
@@ -48,7 +56,7 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        jobs.append([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *FILE_FLAGS.get(src, []), *inc, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():

@@ -49,7 +49,7 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter) {
     carve(c, w.sort_keys[1], n * 4);
     carve(c, w.sort_vals[0], n * 4);
     carve(c, w.sort_vals[1], n * 4);
-    carve(c, w.sort_hist, 256 * nblk * 4);
+    carve(c, w.sort_hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
     carve(c, w.csr_off, (uint64_t)(d.T2 + 1) * 4);
   }
   if (keyblock) {
@@ -59,7 +59,7 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter) {
     carve(c, w.sort_keys[1], n * 4);
     carve(c, w.sort_vals[0], n * 4);
     carve(c, w.sort_vals[1], n * 4);
-    carve(c, w.sort_hist, 256 * nblk * 4);
+    carve(c, w.sort_hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
     carve(c, w.qT, ch * (uint64_t)(d.D + d.Dr) * d.Gp * 2);
     carve(c, w.oT, ch * (uint64_t)d.D * d.Gp * 2);
     carve(c, w.kb_part, (uint64_t)d.nTR * d.T2 * d.AW * 4);
@@ -349,7 +349,7 @@ extern "C" int sfag_workspace_size(
       return fail(SFAG_ERR_TILING, "key-block sort key exceeds 31 bits; lower SFAG_WORKSPACE_BUDGET_MB");
     }
     int kbits = 1;
-    while (((int64_t)1 << kbits) <= sentinel) ++kbits;
+    while (((int64_t)1 << kbits) <= d.nKB) ++kbits;  // the sort runs over key-block ids only
     d.kb_sort_bits = kbits;
   }
   p->d = d;

@@ -66,9 +66,12 @@ void launch_key_reduce(const int32_t* off, const int32_t* pairs, const float* pa
 void launch_cast(int32_t dtype, const float* acc, int64_t T2, int32_t D, int32_t Dr, float kscale, void* dk, void* dkr,
                  void* dv, hipStream_t s);
 void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
+// N1 >= 32: the S/P/dP/dS kernel, then the dQ kernel (together they replace launch_row)
+void launch_sdp(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
+void launch_dq(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
 void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO, int64_t t0, int64_t ntok, int64_t G,
                       int64_t Gp, int32_t Dr, uint16_t* qT, uint16_t* oT, hipStream_t s);
-void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s);
+void launch_keyblock(int32_t dtype, const KbArgs& a, bool wide, hipStream_t s);
 void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
                       float* acc, hipStream_t s);
 void launch_col(int32_t dtype, bool rope, bool partial, const ColArgs& a, hipStream_t s);

@@ -100,6 +100,19 @@ __global__ void __launch_bounds__(256, 2) k_keyblock(KbArgs a) {
     // entries of one token are contiguous, so the group is a prefix of the
     // 256 candidates
     const int gs = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    // this token's Q (or dO) columns of the wave: B operands of every k-step,
+    // fetched now so that their latency overlaps the staging below
+    V8 Bp[4][NB];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int hq = 32 * ks + 8 * g;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ks < nks && hq < Gp) v = *(const uint4*)(Bsrc + ((tl * Bcols + colw + 16 * nb + n) * Gp + hq));
+        Bp[ks][nb] = as_vec8<V8>(v);
+      }
+    }
     bool more = true;
     while (more) {
       // zero the staged rows and the per-row owner flags
@@ -126,25 +139,22 @@ __global__ void __launch_bounds__(256, 2) k_keyblock(KbArgs a) {
         else s_more = 1;
       }
       // ---- C += A · B over the heads of this token ------------------------
-      for (int ks = 0; ks < nks; ++ks) {
-        const int hq = 32 * ks + 8 * g;
-        const bool hok = hq < Gp;
-        V8 B[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (hok) v = *(const uint4*)(Bsrc + ((tl * Bcols + colw + 16 * nb + n) * Gp + hq));
-          B[nb] = as_vec8<V8>(v);
-        }
-        const int q = 4 * ks + g;
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < nks) {
+          const int q = 4 * ks + g;
+          const bool hok = 32 * ks + 8 * g < Gp;
+          uint4 av[kMB];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          const int r = mb * 16 + n;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (hok) v = *(const uint4*)(As + r * RB + (((q & ~7) | ((q & 7) ^ (r & 7))) << 4));
-          const V8 A = as_vec8<V8>(v);
+          for (int mb = 0; mb < kMB; ++mb) {
+            const int r = mb * 16 + n;
+            av[mb] = hok ? *(const uint4*)(As + r * RB + (((q & ~7) | ((q & 7) ^ (r & 7))) << 4))
+                         : make_uint4(0, 0, 0, 0);
+          }
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) C[mb][nb] = TT::mfma(A, B[nb], C[mb][nb]);
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) C[mb][nb] = TT::mfma(as_vec8<V8>(av[mb]), Bp[ks][nb], C[mb][nb]);
         }
       }
       __syncthreads();
@@ -234,26 +244,23 @@ void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO,
   hipLaunchKernelGGL(k_transpose, dim3((unsigned)(ntok * nsl)), dim3(256), 0, s, q, qr, dO, t0, G, Gp, Dr, qT, oT);
 }
 
-void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s) {
-  // column blocks with 256 columns use NB = 4, the rope block NB = 1; they
-  // are launched separately so that each instance has a fixed register shape
+void launch_keyblock(int32_t dtype, const KbArgs& a, bool wide, hipStream_t s) {
+  // Column blocks 256 wide run with NB = 4, the 64-wide rope block with
+  // NB = 1; each call launches the blocks of one width, so that every kernel
+  // instance has a fixed register shape.
   KbArgs w = a;
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool wide = pass == 0;
-    int idx[kMaxColBlocks], m = 0;
-    for (int i = 0; i < a.nCB; ++i)
-      if ((a.cbs[i].width == 256) == wide) idx[m++] = i;
-    if (m == 0) continue;
-    for (int i = 0; i < m; ++i) w.cbs[i] = a.cbs[idx[i]];
-    w.nCB = m;
-    const dim3 grid((unsigned)(w.nTR * w.nKB * w.nCB)), block(256);
-    if (dtype == SFAG_BF16) {
-      if (wide) hipLaunchKernelGGL((k_keyblock<BF16, 4>), grid, block, 0, s, w);
-      else hipLaunchKernelGGL((k_keyblock<BF16, 1>), grid, block, 0, s, w);
-    } else {
-      if (wide) hipLaunchKernelGGL((k_keyblock<FP16, 4>), grid, block, 0, s, w);
-      else hipLaunchKernelGGL((k_keyblock<FP16, 1>), grid, block, 0, s, w);
-    }
+  int m = 0;
+  for (int i = 0; i < a.nCB; ++i)
+    if ((a.cbs[i].width == 256) == wide) w.cbs[m++] = a.cbs[i];
+  if (m == 0) return;
+  w.nCB = m;
+  const dim3 grid((unsigned)(w.nTR * w.nKB * w.nCB)), block(256);
+  if (dtype == SFAG_BF16) {
+    if (wide) hipLaunchKernelGGL((k_keyblock<BF16, 4>), grid, block, 0, s, w);
+    else hipLaunchKernelGGL((k_keyblock<BF16, 1>), grid, block, 0, s, w);
+  } else {
+    if (wide) hipLaunchKernelGGL((k_keyblock<FP16, 4>), grid, block, 0, s, w);
+    else hipLaunchKernelGGL((k_keyblock<FP16, 1>), grid, block, 0, s, w);
   }
 }
 

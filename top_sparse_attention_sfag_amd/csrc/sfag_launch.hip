@@ -207,7 +207,14 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
     }
     ra.t0 = ca.t0 = t0;
     ra.ntok = ca.ntok = ntok;
-    {
+    if (d.Gp >= 32) {
+      {
+        TimedScope ts("sdp", s);
+        launch_sdp(plan->dtype, rope, ra, s);
+      }
+      TimedScope ts("dq", s);
+      launch_dq(plan->dtype, rope, ra, s);
+    } else {
       TimedScope ts("row", s);
       launch_row(plan->dtype, rope, ra, s);
     }
@@ -255,7 +262,11 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
         ka.nCB = m;
         {
           TimedScope ts("keyblock", s);
-          launch_keyblock(plan->dtype, ka, s);
+          launch_keyblock(plan->dtype, ka, true, s);
+        }
+        if (rope) {
+          TimedScope ts("keyblock_rope", s);
+          launch_keyblock(plan->dtype, ka, false, s);
         }
         {
           TimedScope ts("kb_reduce", s);
@@ -308,7 +319,7 @@ IndexLayout index_layout(int64_t T1, int64_t E) {
   carve(L.keys1, n * 4);
   carve(L.vals0, n * 4);
   carve(L.vals1, n * 4);
-  carve(L.hist, 256 * nblk * 4 + 4);
+  carve(L.hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
   L.total = c;
   return L;
 }

@@ -126,7 +126,7 @@ __device__ __forceinline__ void load_item(int64_t i, int pass, const int32_t* ke
                                           int32_t& key, int32_t& val, int key_mode, int64_t ntok) {
   if (pass == 0) {
     const int64_t tl = i / E, c = i - tl * E;
-    if (c < nvalid[tl]) key = key_mode == 0 ? rows[i] : (int32_t)((int64_t)(rows[i] / kKeyBlock) * ntok + tl);
+    if (c < nvalid[tl]) key = key_mode == 0 ? rows[i] : rows[i] / kKeyBlock;
     else key = sentinel;
     val = (int32_t)i;
   } else {
@@ -156,7 +156,58 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_hist(int64_t n, int pass,
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
 }
 
-// Exclusive scan of n int32 counts in place (one block of 1024 threads).
+// Exclusive scan of n int32 counts in place, in three phases: per-segment
+// sums, a scan of the segment sums, and per-segment scans with their offsets.
+constexpr int kScanSeg = 4096;  // elements per segment (256 threads x 16)
+
+__device__ __forceinline__ int32_t block_exclusive_scan256(int32_t v, int32_t* sh, int32_t& total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  int32_t off = 0;
+  for (int i = 0; i < w; ++i) off += sh[i];
+  total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return off + x - v;
+}
+
+__global__ void __launch_bounds__(256) k_scan_sums(const int32_t* __restrict__ a, int64_t n, int32_t* __restrict__ sums) {
+  __shared__ int32_t sh[4];
+  const int64_t base = (int64_t)blockIdx.x * kScanSeg;
+  int32_t s = 0;
+  for (int i = threadIdx.x; i < kScanSeg; i += 256)
+    if (base + i < n) s += a[base + i];
+  int32_t total;
+  block_exclusive_scan256(s, sh, total);
+  if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(256) k_scan_segments(int32_t* __restrict__ a, int64_t n,
+                                                       const int32_t* __restrict__ offs) {
+  __shared__ int32_t sh[4];
+  const int64_t base = (int64_t)blockIdx.x * kScanSeg + threadIdx.x * 16;
+  int32_t v[16], s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = base + i < n ? a[base + i] : 0;
+    s += v[i];
+  }
+  int32_t total;
+  int32_t run = block_exclusive_scan256(s, sh, total) + offs[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (base + i < n) a[base + i] = run;
+    run += v[i];
+  }
+}
+
+// Single-block exclusive scan (for the segment sums).
 __global__ void __launch_bounds__(1024) k_scan(int32_t* __restrict__ a, int64_t n) {
   __shared__ int32_t part[1024];
   const int64_t per = (n + 1023) / 1024;
@@ -226,6 +277,16 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_scatter(int64_t n, int pa
   }
 }
 
+// Composite key of the key-block order: block * ntok + token (sentinel past the end).
+__global__ void __launch_bounds__(256) k_kb_keys(const int32_t* __restrict__ kb, const int32_t* __restrict__ vals,
+                                                 int64_t n, int64_t E, int64_t ntok, int32_t nkb,
+                                                 int32_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t b = kb[i];
+  out[i] = b < nkb ? (int32_t)((int64_t)b * ntok + vals[i] / E) : (int32_t)((int64_t)nkb * ntok);
+}
+
 // csr_off[p] = number of sorted keys < p, p in [0, T2].
 __global__ void __launch_bounds__(256) k_csr_offsets(const int32_t* __restrict__ keys, int64_t n, int64_t T2,
                                                      int32_t* __restrict__ off) {
@@ -285,6 +346,18 @@ static inline unsigned grid_for(uint64_t n, unsigned per_block, unsigned cap = 6
   return (unsigned)g;
 }
 
+// In-place exclusive scan of n counts; tmp holds ceil(n / kScanSeg) ints.
+static void launch_scan(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s) {
+  const int64_t nseg = (n + kScanSeg - 1) / kScanSeg;
+  if (nseg <= 1) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, a, n);
+    return;
+  }
+  hipLaunchKernelGGL(k_scan_sums, dim3((unsigned)nseg), dim3(256), 0, s, a, n, tmp);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, tmp, nseg);
+  hipLaunchKernelGGL(k_scan_segments, dim3((unsigned)nseg), dim3(256), 0, s, a, n, tmp);
+}
+
 void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int32_t* q_off, int32_t* kv_off,
                         hipStream_t s) {
   hipLaunchKernelGGL(k_seq_offsets, dim3(1), dim3(256), 0, s, lq, lk, B, q_off, kv_off);
@@ -316,8 +389,11 @@ void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E
                 hipStream_t s, int key_mode, int64_t ntok, int32_t** sorted_keys) {
   const int64_t nblk = (n + kSortBlock - 1) / kSortBlock;
   const int npass = (sort_bits + 7) / 8;
-  // key_mode 1 sorts by key block * ntok + token; its sentinel is past the last block
-  const int32_t sentinel = key_mode == 0 ? (int32_t)T2 : (int32_t)(((T2 + kKeyBlock - 1) / kKeyBlock) * ntok);
+  int32_t* scan_tmp = hist + 256 * nblk;  // the histogram region reserves room for the segment sums
+  // key_mode 1 sorts by key block only: items enter in (token, position) order
+  // and the sort is stable, so each block's items stay in token order.
+  const int32_t nkb = (int32_t)((T2 + kKeyBlock - 1) / kKeyBlock);
+  const int32_t sentinel = key_mode == 0 ? (int32_t)T2 : nkb;
   int cur = 0;
   for (int pass = 0; pass < npass; ++pass) {
     const int32_t* kin = pass ? keys[cur] : nullptr;
@@ -325,7 +401,7 @@ void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E
     const int nxt = pass ? cur ^ 1 : 0;
     hipLaunchKernelGGL(k_sort_hist, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows, nvalid,
                        E, sentinel, hist, nblk, key_mode, ntok);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, hist, 256 * nblk);
+    launch_scan(hist, 256 * nblk, scan_tmp, s);
     hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows,
                        nvalid, E, sentinel, hist, nblk, keys[nxt], vals[nxt], key_mode, ntok);
     cur = nxt;
@@ -334,6 +410,13 @@ void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E
     hipLaunchKernelGGL(k_csr_offsets, dim3(grid_for(T2 + 1, 256, 1u << 30)), dim3(256), 0, s, keys[cur], n, T2,
                        csr_off);
   *sorted_vals = vals[cur];
+  if (key_mode == 1) {
+    // composite keys block * ntok + token for the range lookups
+    int32_t* ck = keys[cur ^ 1];
+    hipLaunchKernelGGL(k_kb_keys, dim3(grid_for(n, 256, 1u << 30)), dim3(256), 0, s, keys[cur], vals[cur], n, E, ntok,
+                       nkb, ck);
+    cur ^= 1;
+  }
   if (sorted_keys) *sorted_keys = keys[cur];
 }
 

@@ -1,0 +1,394 @@
+// Token-centric kernels for N1 >= 32 heads (operator page
+// "aclnnSparseFlashAttentionGrad", 功能说明 stages 1-3), split so that neither
+// holds more registers than the matrix cores can be fed from:
+//
+//   k_sdp  (token x up to 128 heads): Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ with
+//          v_mfma_f32_32x32x16 (32 positions x 32 heads per wave), then
+//          P = exp(scale·S − max)/sum and dS = P ∘ (dP − Delta), stored as
+//          16-bit (token, position, head) rows.  Each wave keeps its 32 heads'
+//          Q and dO fragments in registers; the 32 gathered K|Krope|V rows of
+//          a tile arrive in LDS through global_load_lds_dwordx4, double
+//          buffered, 16-byte chunks XOR-swizzled by row.
+//   k_dq   (token x 64 heads): dQ = scale·dS·K_sel.  Each wave owns every
+//          fourth 16-column block of dQ|dQrope for all 64 heads, so a tile's K rows
+//          and dS rows are both read once per wave: K columns and dS head
+//          groups come out of LDS transposed with ds_read_b64_tr_b16.
+#include <algorithm>
+
+#include "sfag_device.h"
+#include "sfag_kernels.h"
+#include "sfag_plan.h"
+
+namespace sfag {
+
+namespace {
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 32;
+constexpr int kXcds = 8;
+constexpr int kRun = 16;
+
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 16, 0, 0);
+}
+
+template <typename TT>
+__device__ __forceinline__ f32x16 mfma32(typename TT::vec8 a, typename TT::vec8 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<BF16>(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<FP16>(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Maps a block index to (token of the chunk, head block): each XCD takes runs
+// of kRun consecutive tokens.
+__device__ __forceinline__ int64_t unit_token(int b, int n_hb, int& hb) {
+  const int xcd = b % kXcds, u = b / kXcds;
+  hb = u % n_hb;
+  const int tq = u / n_hb;
+  return ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+}
+
+// Issue the async gather of one tile: rows c0 .. c0+31 of the token (rows past
+// nv repeat row 0; their P and dS are 0).  K main rows (1024 B) and, when
+// WITH_V, V rows go one row per instruction; rope rows (DR*2 bytes) go 8 per
+// instruction.  Every wave of the block takes a share.
+template <int DR, bool WITH_V>
+__device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr, const uint16_t* v,
+                                           const int32_t* rt, int nv, int c0, unsigned char* base, int km_bytes,
+                                           int kr_bytes, int wave, int nw, int lane) {
+  for (int r = wave; r < kTile; r += nw) {
+    const int c = c0 + r;
+    const int64_t key = __builtin_amdgcn_readfirstlane(rt[c < nv ? c : 0]);
+    const int gc = lane ^ (r & 7);
+    lds_load16(k + key * 512 + gc * 8, base + r * 1024);
+    if (WITH_V) lds_load16(v + key * 512 + gc * 8, base + km_bytes + kr_bytes + r * 1024);
+  }
+  if (DR > 0) {
+    for (int gi = wave; gi < kTile / 8; gi += nw) {
+      const int r = gi * 8 + (lane >> 3);
+      const int c = c0 + r;
+      const int64_t key = rt[c < nv ? c : 0];
+      const int gc = (lane & 7) ^ (r & 7);
+      lds_load16(kr + key * DR + gc * 8, base + km_bytes + gi * 8 * (DR * 2));
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// k_sdp: blockDim = 64 * nw, nw = min(4, Gp / 32); head block = 32 * nw heads.
+// ---------------------------------------------------------------------------
+template <typename TT, int DR>
+__global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int KS_QK = DQK / 16;   // k-steps of 16 along D+Dr
+  constexpr int KS_V = 512 / 16;
+  constexpr int KM_BYTES = kTile * 1024;
+  constexpr int KR_BYTES = kTile * DR * 2;
+  constexpr int BUF = KM_BYTES + KR_BYTES + kTile * 1024;
+  constexpr int STAGE = kTile * 128 * 2;  // 32 positions x up to 128 heads, 16-bit
+  typedef typename TT::vec8 V8;
+
+  // Two tile buffers as separate LDS objects: the compiler then knows that
+  // the asynchronous fills of one do not alias reads of the other.
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_ds[STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_p[STAGE];
+
+  const int nw = blockDim.x >> 6;
+  const int HB = 32 * nw;
+  int hb;
+  const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = lane & 31, kg = lane >> 5;   // head within the wave, k-group
+  const int h0 = hb * HB + wave * 32;
+  const int h = h0 + hi;
+  const bool hv = h < a.G;
+
+  // B operands: Q and dO rows of head h, 8 consecutive columns per k-step.
+  V8 Qf[KS_QK], dOf[KS_V];
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) {
+    const int d0 = 16 * ks + 8 * kg;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hv) {
+      if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
+      else v = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
+    }
+    Qf[ks] = as_vec8<V8>(v);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS_V; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hv) v = *(const uint4*)(a.dO + (t * a.G + h) * 512 + 16 * ks + 8 * kg);
+    dOf[ks] = as_vec8<V8>(v);
+  }
+  float mlog = 0.f, inv_l = 0.f, dl = 0.f;
+  bool live = false;
+  if (hv) {
+    const float m = a.smax[t * a.G + h], l = a.ssum[t * a.G + h];
+    live = l > 0.f;
+    inv_l = live ? 1.f / l : 0.f;
+    mlog = m * kLog2e;
+    dl = a.delta[t * a.G + h];
+  }
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+  // A operand rows: position m = lane & 31 of the tile, chunk 2ks + kg.
+  const int m = hi;
+  const int x = m & 7;
+  const int oK = m * 1024;
+  const int oR = m * (DR * 2);
+
+  auto tile = [&](int c0, const unsigned char* Km, unsigned char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c0 + kTile < nv)
+      issue_rows<DR, true>(a.k, a.kr, a.v, rt, nv, c0 + kTile, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Vm = Kr + KR_BYTES;
+    f32x16 S, P;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = P[i] = 0.f;
+    // Sᵀ over D (then Dr): batches of 4 operand reads ahead of their MFMAs
+#pragma unroll
+    for (int k0 = 0; k0 < 32; k0 += 4) {
+      uint4 av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch = 2 * (k0 + j) + kg;
+        av[j] = *(const uint4*)(Km + oK + (((ch & ~7) | ((ch & 7) ^ x)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S = mfma32<TT>(as_vec8<V8>(av[j]), Qf[k0 + j], S);
+    }
+    if (DR > 0) {
+      uint4 av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch = 2 * j + kg;
+        av[j] = *(const uint4*)(Kr + oR + ((ch ^ x) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S = mfma32<TT>(as_vec8<V8>(av[j]), Qf[32 + j], S);
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < KS_V; k0 += 4) {
+      uint4 av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch = 2 * (k0 + j) + kg;
+        av[j] = *(const uint4*)(Vm + oK + (((ch & ~7) | ((ch & 7) ^ x)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P = mfma32<TT>(as_vec8<V8>(av[j]), dOf[k0 + j], P);
+    }
+    // P, dS for head h and positions 8(i/4) + 4kg + (i%4)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 8 * (i >> 2) + 4 * kg + (i & 3);
+      const bool ok = live && (c0 + j < nv);
+      const float p = ok ? exp2f(S[i] * a.scale_log2 - mlog) * inv_l : 0.f;
+      const float ds = p * (P[i] - dl);
+      const int so = (j * 128 + wave * 32 + hi) * 2;
+      *(uint16_t*)(stage_ds + so) = TT::from_f(ds * a.ds_scale);
+      *(uint16_t*)(stage_p + so) = TT::from_f(p);
+    }
+    __syncthreads();
+    // 32 positions x HB heads of each array, 16-byte chunks
+    const int cpr = HB / 8;  // chunks per row
+    for (int q = tid; q < kTile * cpr; q += blockDim.x) {
+      const int j = q / cpr, ch = q - j * cpr;
+      const int hh = hb * HB + ch * 8;
+      if (c0 + j < nv && hh < a.Gp) {
+        const int64_t o = (tl * a.E + c0 + j) * a.Gp + hh;
+        *(uint4*)(a.ds_out + o) = *(const uint4*)(stage_ds + (j * 128 + ch * 8) * 2);
+        *(uint4*)(a.p_out + o) = *(const uint4*)(stage_p + (j * 128 + ch * 8) * 2);
+      }
+    }
+  };
+
+  if (nv > 0) issue_rows<DR, true>(a.k, a.kr, a.v, rt, nv, 0, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
+  for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
+    tile(c0, buf0, buf1);
+    if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_dq: 256 threads; head block of 64 heads; wave w owns the 16-column blocks
+// w, w+4, w+8, ... of dQ|dQrope (blocks 32..35 are the rope columns).
+// ---------------------------------------------------------------------------
+template <typename TT, int DR>
+__global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int NB = DQK / 64;             // column blocks per wave
+  constexpr int KM_BYTES = kTile * 1024;
+  constexpr int KR_BYTES = kTile * DR * 2;
+  constexpr int DS_BYTES = kTile * 128;     // 32 positions x 64 heads, 16-bit
+  constexpr int BUF = KM_BYTES + KR_BYTES + DS_BYTES;
+  typedef typename TT::vec8 V8;
+
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
+
+  int hb;
+  const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int hmax = (int)(a.Gp - hb * 64);   // heads of this block present in the dS rows
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // dS rows of the tile (64 heads = 128 bytes each), 8 rows per instruction;
+  // rows past nv are zero-filled instead.
+  auto issue_tile = [&](int c0, unsigned char* base) {
+    unsigned char* dsb = base + KM_BYTES + KR_BYTES;
+    const int r = wave * 8 + (lane >> 3);
+    const int c = c0 + r;
+    const bool live = c < nv && (lane & 7) * 8 < hmax;
+    // Zero fill before any asynchronous copy is issued, so that no plain LDS
+    // store follows an asynchronous one into the same buffer.
+    if (!live) *(uint4*)(dsb + r * 128 + (lane & 7) * 16) = make_uint4(0, 0, 0, 0);
+    issue_rows<DR, false>(a.k, a.kr, nullptr, rt, nv, c0, base, KM_BYTES, KR_BYTES, wave, 4, lane);
+    if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * 64 + (lane & 7) * 8, dsb + wave * 8 * 128);
+  };
+
+  // Transposed-read offsets (see lds_read_tr): K rows 4g+(n>>2) and +16, dS
+  // rows likewise.  Wave w owns the 16-column blocks w, w+4, w+8, ..., so
+  // block j of the wave starts at 16-byte chunk 2w + 8j of a K row and the
+  // XOR swizzle touches only the low three chunk bits: every read is one
+  // per-lane base plus a compile-time offset.
+  const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;
+  const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
+  const int sw = ((2 * wave + half) ^ x1) << 4;
+  const int offM = r1 * 1024 + sw + hoff;
+  const int offR = r1 * (DR * 2) + sw + hoff;
+  const int offD = r1 * 128 + 8 * (n & 3);
+
+  auto tile = [&](int c0, int cend, const unsigned char* Km, unsigned char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c0 + kTile < cend) issue_tile(c0 + kTile, nxt);
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Ds = Kr + KR_BYTES;
+    // A operands: dS of heads 16s + n at positions 4g+i and 16+4g+i
+    V8 A[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const unsigned char* p1 = Ds + offD + s * 32;
+      A[s] = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 128)));
+    }
+#pragma unroll
+    for (int nb0 = 0; nb0 < NB; nb0 += 3) {
+      s16x4 t1[3], t2[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int nb = nb0 + j;
+        if (nb < NB) {
+          const unsigned char* p1;
+          int rs;
+          if (nb < 8) {           // K columns 16(w + 4nb) ..
+            p1 = Km + offM + nb * 128;
+            rs = 16 * 1024;
+          } else {                // rope columns 16w ..
+            p1 = Kr + offR;
+            rs = 16 * (DR * 2);
+          }
+          t1[j] = lds_read_tr((const uint16_t*)p1);
+          t2[j] = lds_read_tr((const uint16_t*)(p1 + rs));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (nb0 + j < NB) {
+          const V8 B = join_tr<V8>(t1[j], t2[j]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc[s][nb0 + j] = TT::mfma(A[s], B, acc[s][nb0 + j]);
+        }
+      }
+    }
+  };
+
+  // Tiles go in pairs (one per buffer); a trailing tile past nv has zero dS
+  // and adds nothing.  An unconditional pair keeps the accumulators in one
+  // register form across the loop.
+  const int nv2 = (nv + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
+  if (nv > 0) issue_tile(0, buf0);
+  for (int c0 = 0; c0 < nv2; c0 += 2 * kTile) {
+    tile(c0, nv2, buf0, buf1);
+    tile(c0 + kTile, nv2, buf1, buf0);
+  }
+  // dQ[t][h][col] = scale * acc / ds_scale; lane holds heads 16s + 4g + i, column n
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = 16 * (wave + 4 * nb) + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = hb * 64 + 16 * s + 4 * g + i;
+        if (hh < a.G) {
+          const uint16_t v = TT::from_f(acc[s][nb][i] * a.dq_mul);
+          if (col < 512) a.dq[(t * a.G + hh) * 512 + col] = v;
+          else a.dqr[(t * a.G + hh) * DR + (col - 512)] = v;
+        }
+      }
+    }
+  }
+}
+
+void launch_sdp(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
+  if (a_in.ntok == 0) return;
+  const int64_t per = (int64_t)kXcds * kRun;
+  const int64_t padded = (a_in.ntok + per - 1) / per * per;
+  RowArgs a = a_in;
+  // k_sdp: up to 128 heads per block, 32 per wave
+  const int nw = (int)std::min<int64_t>(4, a.Gp / 32);
+  a.n_hb = (int32_t)((a.Gp + 32 * nw - 1) / (32 * nw));
+  const dim3 g1((unsigned)(padded * a.n_hb)), b1(64 * nw);
+  if (dtype == SFAG_BF16) {
+    if (rope) hipLaunchKernelGGL((k_sdp<BF16, 64>), g1, b1, 0, s, a);
+    else hipLaunchKernelGGL((k_sdp<BF16, 0>), g1, b1, 0, s, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((k_sdp<FP16, 64>), g1, b1, 0, s, a);
+    else hipLaunchKernelGGL((k_sdp<FP16, 0>), g1, b1, 0, s, a);
+  }
+}
+
+void launch_dq(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
+  if (a_in.ntok == 0) return;
+  const int64_t per = (int64_t)kXcds * kRun;
+  const int64_t padded = (a_in.ntok + per - 1) / per * per;
+  RowArgs a = a_in;
+  // k_dq: 64 heads per block
+  a.n_hb = (int32_t)((a.Gp + 63) / 64);
+  const dim3 g2((unsigned)(padded * a.n_hb)), b2(256);
+  if (dtype == SFAG_BF16) {
+    if (rope) hipLaunchKernelGGL((k_dq<BF16, 64>), g2, b2, 0, s, a);
+    else hipLaunchKernelGGL((k_dq<BF16, 0>), g2, b2, 0, s, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((k_dq<FP16, 64>), g2, b2, 0, s, a);
+    else hipLaunchKernelGGL((k_dq<FP16, 0>), g2, b2, 0, s, a);
+  }
+}
+
+}  // namespace sfag

@@ -57,12 +57,11 @@ def _alg_bytes(case, n_pairs):
 
 # Algorithmic flops per valid (head, selected position) pair of each MFMA
 # kernel: S over D+Dr and dP over D (sdp); dQ over D+Dr (dq); both (row);
-# dK over D and dV over D (keyblock); dKrope over Dr (keyblock_rope); dK over
-# D+Dr and dV over D (col).
+# dK over D+Dr and dV over D (keyblock, col).
 def _unit_flops(case, kernel):
     D, Dr = case.D, case.Dr
     return {"sdp": 2 * (2 * D + Dr), "dq": 2 * (D + Dr), "row": 2 * (3 * D + 2 * Dr),
-            "keyblock": 2 * 2 * D, "keyblock_rope": 2 * Dr, "col": 2 * (2 * D + Dr)}.get(kernel)
+            "keyblock": 2 * (2 * D + Dr), "col": 2 * (2 * D + Dr)}.get(kernel)
 
 
 def _kernel_bytes(case, kernel, n_pairs):
@@ -76,9 +75,9 @@ def _kernel_bytes(case, kernel, n_pairs):
         return (T1 * (G * (2 * (D + Dr) + D) * e + G * 12 + case.Kent * 4)
                 + n_pairs * ((2 * D + Dr) * e + 2 * G * e))
     if kernel == "keyblock":
-        # per pair dS and P in; per token Q and dO in; per key the fp32 dK|dV
-        # partial out.
-        return n_pairs * 2 * G * e + T1 * G * 2 * D * e + T2 * 2 * D * 4
+        # per pair dS and P in; per token Q|Qrope and dO in; per key the fp32
+        # dK|dKrope|dV partial out.
+        return n_pairs * 2 * G * e + T1 * G * (2 * D + Dr) * e + T2 * (2 * D + Dr) * 4
     return _alg_bytes(case, n_pairs)
 
 
@@ -126,8 +125,7 @@ _GROUPS = {
     "sdp": (r"k_sdp<", [_CSRC + "sfag_sdp.hip"]),
     "dq": (r"k_dq<", [_CSRC + "sfag_sdp.hip"]),
     "row": (r"k_row<", [_CSRC + "sfag_row.hip"]),
-    "keyblock": (r"k_keyblock<[^,]*, 4>", [_CSRC + "sfag_keyblock.hip"]),
-    "keyblock_rope": (r"k_keyblock<[^,]*, 1>", [_CSRC + "sfag_keyblock.hip"]),
+    "keyblock": (r"k_keyblock<", [_CSRC + "sfag_keyblock.hip"]),
     "transpose": (r"k_transpose", [_CSRC + "sfag_keyblock.hip"]),
     "col": (r"k_col<", [_CSRC + "sfag_mfma.hip"]),
 }

@@ -82,7 +82,7 @@ def lib():
 
 
 KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "sdp", "dq", "col", "csr", "key_reduce", "transpose", "kb_sort",
-                 "keyblock", "keyblock_rope", "kb_reduce", "cast")
+                 "keyblock", "kb_reduce", "cast")
 
 
 def profile_enable(on: bool = True):

@@ -23,12 +23,12 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
-# Per-file scheduling: the MFMA kernels fed from LDS schedule for
+# Per-file scheduling: the token kernels (k_sdp, k_dq) schedule for
 # instruction-level parallelism (several operand reads in flight ahead of the
-# MFMAs that consume them); the register-bound k_row keeps the default.
+# MFMAs that consume them); k_row and the key-block kernel, which use every
+# register they have, keep the default.
 FILE_FLAGS = {
     "sfag_sdp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-    "sfag_keyblock.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 HIP_SOURCES = ["sfag_prep.hip", "sfag_row.hip", "sfag_sdp.hip", "sfag_mfma.hip", "sfag_keyblock.hip",
                "sfag_launch.hip"]

@@ -64,6 +64,11 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter) {
     carve(c, w.oT, ch * (uint64_t)d.D * d.Gp * 2);
     carve(c, w.kb_part, (uint64_t)d.nTR * d.T2 * d.AW * 4);
     carve(c, w.kb_nonempty, (uint64_t)d.nTR * d.nKB * 4);
+    carve(c, w.vis_flags, n * 4);
+    carve(c, w.vis_start, (n + 1) * 4);
+    carve(c, w.vis_key, n * 4);
+    carve(c, w.vis_er, n * 4);
+    carve(c, w.vis_n, 4);
   }
   w.total = c;
   return w;
@@ -325,7 +330,7 @@ extern "C" int sfag_workspace_size(
   // partials scatter the partial rows and the sort buffers) within a budget.
   uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
   if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
-  if (keyblock) per_tok += 4 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
+  if (keyblock) per_tok += 8 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
   const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 16384);
   int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
   const int64_t forced = env_i64("SFAG_CHUNK_TOKENS", 0);

@@ -33,11 +33,12 @@ struct ColBlock {
 struct KbArgs {
   const uint16_t *qT, *oT;     // (ntok, 512+Dr, Gp) and (ntok, 512, Gp) transposed Q|Qr and dO
   const uint16_t *ds, *p;      // (ntok, E, Gp)
-  const int32_t *rows;         // (ntok, E) key row of each valid position
-  const int32_t *skeys, *svals;  // pairs sorted by key block * ntok + token, pair ids
+  const int32_t* svals;        // pair ids sorted by (key block, token)
+  const int32_t* er;           // key row within its block of each sorted pair
+  const int32_t *vis_start, *vis_key, *n_vis;  // visits: first sorted pair, composite key; count
   int32_t* nonempty;           // (nTR, nKB) flags
   float* part;                 // (nTR, T2, AW) partial sums per token range
-  int64_t n, ntok, Gp, T2, AW, TR, Dq;
+  int64_t ntok, E, Gp, T2, AW, TR, Dq;
   int32_t nKB, nTR, nCB;
   ColBlock cbs[kMaxColBlocks];
 };
@@ -71,7 +72,11 @@ void launch_sdp(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
 void launch_dq(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
 void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO, int64_t t0, int64_t ntok, int64_t G,
                       int64_t Gp, int32_t Dr, uint16_t* qT, uint16_t* oT, hipStream_t s);
-void launch_keyblock(int32_t dtype, const KbArgs& a, bool wide, hipStream_t s);
+void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s);
+void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows, int64_t n, int64_t ntok,
+                   int32_t nkb, int32_t* flags, int32_t* scan_tmp, int32_t* vis_start, int32_t* vis_key, int32_t* er,
+                   int32_t* n_vis, hipStream_t s);
+void launch_scan_i32(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s);
 void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
                       float* acc, hipStream_t s);
 void launch_col(int32_t dtype, bool rope, bool partial, const ColArgs& a, hipStream_t s);

@@ -3,19 +3,31 @@
 // dK = scale·dSᵀ·Q, summed over every (token, position) selecting the key).
 //
 // Instead of scattering one partial row per (token, position) with atomics,
-// a workgroup owns a block of 128 consecutive key rows and a block of output
+// a workgroup owns a block of 256 consecutive key rows and a block of output
 // columns, and walks, in token order, the tokens of one token range that
-// select any of its keys (the pairs are sorted by (key block, token): an
-// inversion of the indices at key-block granularity).  For each such token
-// it stages that token's P or dS rows for the block's keys in LDS (rows of
-// unselected keys are zero) and accumulates
+// select any of its keys.  The pairs are sorted by (key block, token), and a
+// "visit" is the run of one token's pairs inside one key block.  For each
+// visit the workgroup accumulates
 //     C[key][col] += Σ_h A[key][h] · B[h][col]
-// with v_mfma_f32_16x16x32, where B is the token's Q (or dO) read from a
-// per-token transposed copy so that each lane's 8 consecutive heads of one
-// column are one 16-byte load.  C stays in registers for the whole range and
-// is written once as an fp32 partial of that token range; a second kernel
-// adds the partials of the ranges in ascending order.  Every sum runs in a
-// fixed order, so the result is bitwise reproducible.
+// with v_mfma_f32_16x16x32, where A holds the token's dS (or P) rows placed
+// at their key rows (rows the token does not select read a zero row) and B is
+// the token's Q|Qrope (or dO) from a per-token transposed copy, so that 8
+// consecutive heads of one column are 16 contiguous bytes.
+//
+// A visit runs in four stages, one per 32-head step.  Both operands of a
+// stage reach LDS through global_load_lds, three stages ahead of their use
+// (four stage buffers), so the only waits on memory are explicit ones on
+// copies issued about three stages earlier.  The key-row slot map of a visit
+// (which rows its token selects, how often, and which pair supplies each
+// row) is built two visits ahead with LDS atomics from the visit's pairs,
+// which are themselves copied into LDS a visit ahead.  A key listed k times
+// by one token has k identical dS/P rows (same token, same key), so each
+// stage of that visit runs k rounds over the row.
+//
+// C stays in registers (AGPRs; one wave per SIMD) for the whole token range
+// and is written once as an fp32 partial of that range; a second kernel adds
+// the partials of the ranges in ascending order.  Every sum runs in a fixed
+// order, so the result is bitwise reproducible.
 #include "sfag_device.h"
 #include "sfag_kernels.h"
 #include "sfag_plan.h"
@@ -24,9 +36,31 @@ namespace sfag {
 
 namespace {
 
-constexpr int kKB = kKeyBlock;   // key rows per block (128)
-constexpr int kMB = kKB / 16;    // 16-row MFMA blocks per key block
-constexpr int kMaxGroup = 256;   // entries staged per pass (one per thread)
+constexpr int kKB = kKeyBlock;             // key rows per block (256)
+constexpr int kThreads = 256;              // 4 waves, one per SIMD
+constexpr int kStageA = kKB * 64;          // 256 rows x 32 heads, 16-bit
+constexpr int kZeroA = kStageA;            // a zero row after the rows
+constexpr int kStageB = 256 * 64;          // up to 256 columns x 32 heads
+constexpr int kStageBytes = kStageA + 64 + kStageB;
+constexpr int kWin = 256;                  // visits whose metadata sit in LDS at a time
+constexpr int kEnt = 256;                  // pairs of a visit copied into LDS
+
+// Asynchronous global -> LDS copies (lane l of the wave writes 16 or 4 bytes
+// at the wave-uniform LDS address l_base + l * size).  Written as inline asm
+// on purpose: the compiler then does not track them, so it inserts no waits
+// of its own for them before unrelated LDS reads; every read of copied data
+// is preceded by an explicit wait on the copy (wait_vm) and a barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
+}
+__device__ __forceinline__ void dma16(const void* g, const void* l) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, const void* l) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
+               : "memory");
+}
 
 __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int64_t v) {
   int64_t lo = 0, hi = n;
@@ -38,144 +72,347 @@ __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, 
   return lo;
 }
 
+// Workgroup barrier for LDS data: waits for this wave's LDS operations only,
+// not for its outstanding global loads and copies (a fence would wait for
+// those as well, draining the copies that are meant to stay in flight).
+// The signal fences keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+struct KbShared {
+  int32_t cnt[3][kKB];       // per key row: how often the visit's token lists it
+  int32_t prim[3][kKB];      // per key row: the pair whose dS/P row is staged
+  int32_t rounds[3];         // max over rows of cnt (at least 1)
+  int32_t vstart[kWin + 3];  // first sorted pair of visits wb .. wb + kWin + 2
+  int32_t vkey[kWin + 2];    // their composite keys
+};
+
+// One column block: NB 16-column MFMA blocks per wave (4 for 256 columns,
+// 3 for 192).  Wave w: all 256 key rows (16 MFMA row blocks), columns
+// w * 16 * NB .. of the block.  GP is the padded head count when it is 128
+// (all strides compile-time), else 0 (taken from the args).
+template <typename TT, int NB, int GP>
+__device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int tr, int kb, int64_t vlo,
+                                         int64_t vhi, unsigned char* __restrict__ st0,
+                                         unsigned char* __restrict__ st1, unsigned char* __restrict__ st2,
+                                         unsigned char* __restrict__ st3, KbShared* __restrict__ shp,
+                                         int32_t* __restrict__ e_pair, int32_t* __restrict__ e_row) {
+  // (restrict: lets the compiler tell the asynchronous LDS copies into one
+  // buffer from the reads of another, so that those reads need no wait)
+  KbShared& sh = *shp;
+  typedef typename TT::vec8 V8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int Gp = GP ? GP : (int)a.Gp, nks = (Gp + 31) >> 5;
+  const uint16_t* Bsrc = c.src == 0 ? a.qT : a.oT;
+  const int64_t Bcols = c.src == 0 ? a.Dq : 512;
+  const uint16_t* Asrc = c.src == 0 ? a.ds : a.p;
+  const int64_t kbase = (int64_t)kb * a.ntok;
+  constexpr int K = 4 + NB;   // copy instructions per wave and stage (A, B)
+
+  // ---- visit metadata, staged in LDS for a window of visits from wb ------
+  int64_t wb = vlo;
+  auto load_window = [&]() {
+    for (int j = tid; j < kWin + 3; j += kThreads) {
+      const int64_t x = wb + j;
+      sh.vstart[j] = x <= vhi ? a.vis_start[x] : 0;
+      if (j < kWin + 2) sh.vkey[j] = x < vhi ? a.vis_key[x] : 0;
+    }
+  };
+  auto v_start = [&](int64_t v) -> int64_t { return (int64_t)sh.vstart[v - wb]; };
+  auto v_count = [&](int64_t v) -> int { return sh.vstart[v + 1 - wb] - sh.vstart[v - wb]; };
+  auto v_token = [&](int64_t v) -> int64_t { return (int64_t)sh.vkey[v - wb] - kbase; };
+
+  f32x4 C[16][NB];
+#pragma unroll
+  for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) C[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- slot maps ----------------------------------------------------------
+  auto reset = [&](int b) {
+    sh.cnt[b][tid] = 0;
+    sh.prim[b][tid] = -1;
+    if (tid == 0) sh.rounds[b] = 1;
+  };
+  auto add_entry = [&](int b, int32_t pair, int row) {
+    const int o = atomicAdd(&sh.cnt[b][row], 1);
+    if (o == 0) sh.prim[b][row] = pair;
+    else atomicMax(&sh.rounds[b], o + 1);
+  };
+  // map of visit v from its pairs: the first kEnt from the LDS copy, the
+  // rest (only with duplicated keys) straight from memory
+  auto build = [&](int b, int64_t v) {
+    const int cnt = v_count(v);
+    if (tid < cnt && tid < kEnt) add_entry(b, e_pair[tid], e_row[tid]);
+    const int64_t s0 = v_start(v);
+    for (int j = tid + kEnt; j < cnt; j += kThreads) add_entry(b, a.svals[s0 + j], a.er[s0 + j]);
+  };
+  // copy of visit v's first kEnt pairs (ids and key rows) into LDS: 8
+  // dword-copy instructions, two per wave; lanes past the visit re-read
+  // its first pair
+  auto issue_entries = [&](int64_t v) {
+    const int64_t s0 = v_start(v);
+    const int cnt = v_count(v);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int ins = wave * 2 + k;          // 0..3 pair ids, 4..7 key rows
+      const int part = ins & 3;
+      const int e = part * 64 + lane;
+      const int64_t src = s0 + (e < cnt ? e : 0);
+      if (ins < 4) dma4(a.svals + src, &e_pair[part * 64]);
+      else dma4(a.er + src, &e_row[part * 64]);
+    }
+  };
+
+  // ---- stage copies -------------------------------------------------------
+  // A of stage (visit, ks): 256 rows x 4 chunks (heads 32ks + 8q .. +8), 16
+  // instructions, wave w issuing w, w+4, w+8, w+12; the lane writing position
+  // p of row r fetches chunk p ^ ((r >> 2) & 3).  Rows not selected (and
+  // chunks past the heads) re-read the token's first row into slots that are
+  // never read.  B: the block's columns x 4 chunks likewise, NB per wave.
+  auto issue_stage = [&](int b, int64_t tl, int ks, unsigned char* st) {
+    const uint16_t* arow0 = Asrc + tl * a.E * Gp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = wave + 4 * k;
+      const int row = 16 * i + (lane >> 2);
+      const int q = (lane & 3) ^ ((row >> 2) & 3);
+      const int hq = 32 * ks + 8 * q;
+      const int32_t pr = sh.prim[b][row];
+      const uint16_t* src = (pr >= 0 && hq < Gp) ? Asrc + (int64_t)pr * Gp + hq : arow0;
+      dma16(src, st + i * 1024);
+    }
+    const uint16_t* bcol0 = Bsrc + (tl * Bcols + c.tcol0) * Gp;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int i = wave + 4 * k;
+      const int col = 16 * i + (lane >> 2);
+      const int q = (lane & 3) ^ ((col >> 2) & 3);
+      const int hq = 32 * ks + 8 * q;
+      const uint16_t* src = hq < Gp ? bcol0 + (int64_t)col * Gp + hq : bcol0;
+      dma16(src, st + kStageA + 64 + i * 1024);
+    }
+  };
+  // bit mb: this lane's row of MFMA block mb is listed more than r times
+  auto selmask = [&](int b, int r) -> unsigned {
+    unsigned m = 0;
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) m |= (sh.cnt[b][mb * 16 + n] > r ? 1u : 0u) << mb;
+    return m;
+  };
+  // C += A · B over the 32 heads of one stage
+  const int bcol = wave * 16 * NB + n;
+  auto compute = [&](const unsigned char* st, unsigned sel, int ks) {
+    const bool qok = 32 * ks + 8 * g < Gp;
+    const int po = (g ^ (n >> 2)) << 4;          // rows mb*16 + n: (r >> 2) & 3 = n >> 2
+    V8 Bf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = bcol + 16 * nb;
+      Bf[nb] = as_vec8<V8>(*(const uint4*)(st + kStageA + 64 + col * 64 + ((g ^ ((col >> 2) & 3)) << 4)));
+    }
+    uint4 av[2][4];
+    auto rd = [&](int h, uint4 (&dst)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mb = 4 * h + j;
+        const int ro = (qok && ((sel >> mb) & 1)) ? (mb * 16 + n) * 64 : kZeroA;
+        dst[j] = *(const uint4*)(st + ro + po);
+      }
+    };
+    rd(0, av[0]);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (h + 1 < 4) rd(h + 1, av[(h + 1) & 1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          C[4 * h + j][nb] = TT::mfma(as_vec8<V8>(av[h & 1][j]), Bf[nb], C[4 * h + j][nb]);
+    }
+  };
+
+  const int64_t nst = 4 * (vhi - vlo);   // stages
+  // before stage s: wait for its copies; everything issued after them is the
+  // copies of the (up to) two following stages and pair copies
+  auto wait_stage = [&](int64_t s) {
+    const int later = (s + 1 < nst ? 1 : 0) + (s + 2 < nst ? 1 : 0);
+    if (GP == 0 || later == 0) wait_vm<0>();
+    else if (later == 2) wait_vm<2 * K>();
+    else wait_vm<K>();
+  };
+  auto stage_buf = [&](int ks) -> unsigned char* { return ks == 0 ? st0 : ks == 1 ? st1 : ks == 2 ? st2 : st3; };
+
+  // ---- prologue ------------------------------------------------------------
+  for (int b = 0; b < 3; ++b) reset(b);
+  load_window();
+  __syncthreads();
+  for (int x = 0; x < 2; ++x) {
+    const int64_t v = vlo + x;
+    if (v < vhi) {
+      const int64_t s0 = v_start(v);
+      const int cnt = v_count(v);
+      for (int j = tid; j < cnt; j += kThreads) add_entry(x, a.svals[s0 + j], a.er[s0 + j]);
+    }
+  }
+  if (tid < 4) *(uint4*)(st0 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
+  if (tid < 4) *(uint4*)(st1 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
+  if (tid < 4) *(uint4*)(st2 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
+  if (tid < 4) *(uint4*)(st3 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  {
+    const int64_t tl = v_token(vlo);
+    issue_stage(0, tl, 0, st0);
+    if (nks > 1) issue_stage(0, tl, 1, st1);
+    if (nks > 2) issue_stage(0, tl, 2, st2);
+  }
+
+  // ---- one visit per iteration, four stages ---------------------------------
+  for (int64_t v = vlo; v < vhi; ++v) {
+    const int u = (int)((v - vlo) % 3);
+    const int u1 = u == 2 ? 0 : u + 1, u2 = u == 0 ? 2 : u - 1;
+    const int64_t s = 4 * (v - vlo);
+    if (v - wb + 2 > kWin) {   // visits v .. v + 2 leave the window
+      __syncthreads();
+      wb = v;
+      load_window();
+      __syncthreads();
+    }
+    const int64_t tl = v_token(v);
+    const bool more = v + 1 < vhi;
+    const int64_t tl1 = more ? v_token(v + 1) : 0;
+    // stage 0
+    wait_stage(s);
+    bar();
+    unsigned sel = selmask(u, 0);
+    const int R = sh.rounds[u];
+    reset(u2);
+    if (v + 2 < vhi) issue_entries(v + 2);
+    if (nks > 3) issue_stage(u, tl, 3, st3);
+    for (int r = 0; r < R; ++r) {
+      if (r) sel = selmask(u, r);
+      compute(st0, sel, 0);
+    }
+    // stages 1 .. 3: each issues the copy of the next visit's stage ks - 1
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks) {
+      if (ks < nks || GP == 0) {
+        wait_stage(s + ks);
+        bar();
+        // map of visit v + 2: its pairs were copied during stage 0, before
+        // the copies waited for above
+        if (ks == 3 && v + 2 < vhi) build(u2, v + 2);
+        if (more) issue_stage(u1, tl1, ks - 1, stage_buf(ks - 1));
+        if (ks < nks) {
+          for (int r = 0; r < R; ++r) {
+            if (r) sel = selmask(u, r);
+            compute(stage_buf(ks), sel, ks);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- partial of this token range ----------------------------------------
+  float* out = a.part + (int64_t)tr * a.T2 * a.AW;
+  const int ocol = c.ocol0 + wave * 16 * NB + n;
+#pragma unroll
+  for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = (int64_t)kb * kKB + mb * 16 + 4 * g + i;
+      if (row < a.T2) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) out[row * a.AW + ocol + 16 * nb] = C[mb][nb][i];
+      }
+    }
+  }
+}
+
 }  // namespace
 
-// NB: 16-column MFMA blocks per wave (4 for a 256-column block, 1 for the
-// 64-column rope block).
-template <typename TT, int NB>
-__global__ void __launch_bounds__(256, 2) k_keyblock(KbArgs a) {
-  typedef typename TT::vec8 V8;
-  constexpr int RB = 256;  // LDS bytes per staged row (up to 128 heads)
-  __shared__ __attribute__((aligned(16))) unsigned char As[kKB * RB];
-  __shared__ int32_t flag[kKB];
-  __shared__ int32_t e_row[kMaxGroup];
-  __shared__ int32_t e_pair[kMaxGroup];
-  __shared__ int32_t e_pending[kMaxGroup];
-  __shared__ int32_t s_cnt[4], s_more;
+template <typename TT>
+__global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char st0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[kStageBytes];
+  __shared__ KbShared sh;
+  __shared__ int32_t e_pair[kEnt];   // pairs of the visit whose map is built next
+  __shared__ int32_t e_row[kEnt];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
   // unit order: token range major, then key block, then column block
   const int cb = blockIdx.x % a.nCB;
   const int kb = (blockIdx.x / a.nCB) % a.nKB;
   const int tr = blockIdx.x / (a.nCB * a.nKB);
   const ColBlock c = a.cbs[cb];
   const int64_t t_lo = (int64_t)tr * a.TR, t_hi = min<int64_t>(t_lo + a.TR, a.ntok);
-  const int64_t lo = lower_bound_i32(a.skeys, a.n, (int64_t)kb * a.ntok + t_lo);
-  const int64_t hi = lower_bound_i32(a.skeys, a.n, (int64_t)kb * a.ntok + t_hi);
-  if (tid == 0 && cb == 0) a.nonempty[(int64_t)tr * a.nKB + kb] = hi > lo ? 1 : 0;
-  if (hi <= lo) return;
-
-  const int Gp = (int)a.Gp;
-  const int nks = (Gp + 31) / 32;
-  const uint16_t* Bsrc = c.src == 0 ? a.qT : a.oT;
-  const int64_t Bcols = c.src == 0 ? a.Dq : 512;
-  const uint16_t* Asrc = c.src == 0 ? a.ds : a.p;
-  const int colw = c.tcol0 + wave * 16 * NB;  // first source column of this wave
-
-  f32x4 C[kMB][NB];
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) C[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t kb_row0 = (int64_t)kb * kKB;
-  int64_t i = lo;
-  while (i < hi) {
-    // ---- the next group: up to 256 consecutive entries of one token -------
-    const int32_t key0 = a.skeys[i];
-    const int64_t tl = key0 - (int64_t)kb * a.ntok;
-    const int64_t ie = i + tid;
-    const bool in = ie < hi && a.skeys[ie] == key0;
-    const uint64_t bal = __ballot(in);
-    if (lane == 0) s_cnt[wave] = __popcll(bal);
-    int32_t pr = 0, rw = 0;
-    if (in) {
-      pr = a.svals[ie];
-      rw = (int32_t)(a.rows[pr] - kb_row0);
-      e_row[tid] = rw;
-      e_pair[tid] = pr;
-      e_pending[tid] = 1;
-    }
-    __syncthreads();
-    // entries of one token are contiguous, so the group is a prefix of the
-    // 256 candidates
-    const int gs = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-    // this token's Q (or dO) columns of the wave: B operands of every k-step,
-    // fetched now so that their latency overlaps the staging below
-    V8 Bp[4][NB];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int hq = 32 * ks + 8 * g;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (ks < nks && hq < Gp) v = *(const uint4*)(Bsrc + ((tl * Bcols + colw + 16 * nb + n) * Gp + hq));
-        Bp[ks][nb] = as_vec8<V8>(v);
-      }
-    }
-    bool more = true;
-    while (more) {
-      // zero the staged rows and the per-row owner flags
-      for (int x = tid; x < kKB * RB / 16; x += 256) *(uint4*)(As + x * 16) = make_uint4(0, 0, 0, 0);
-      if (tid < kKB) flag[tid] = 0x7fffffff;
-      if (tid == 0) s_more = 0;
-      __syncthreads();
-      // a key listed twice by the token: the earliest pending entry goes first
-      if (tid < gs && e_pending[tid]) atomicMin(&flag[e_row[tid]], tid);
-      __syncthreads();
-      // copy the owners' rows (16-byte chunks, XOR-swizzled by row & 7)
-      const int CH = Gp / 8;
-      for (int x = tid; x < gs * CH; x += 256) {
-        const int e = x / CH, q = x - e * CH;
-        if (e_pending[e] && flag[e_row[e]] == e) {
-          const int r = e_row[e];
-          const uint4 v = *(const uint4*)(Asrc + (int64_t)e_pair[e] * Gp + q * 8);
-          *(uint4*)(As + r * RB + (((q & ~7) | ((q & 7) ^ (r & 7))) << 4)) = v;
-        }
-      }
-      __syncthreads();
-      if (tid < gs && e_pending[tid]) {
-        if (flag[e_row[tid]] == tid) e_pending[tid] = 0;
-        else s_more = 1;
-      }
-      // ---- C += A · B over the heads of this token ------------------------
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < nks) {
-          const int q = 4 * ks + g;
-          const bool hok = 32 * ks + 8 * g < Gp;
-          uint4 av[kMB];
-#pragma unroll
-          for (int mb = 0; mb < kMB; ++mb) {
-            const int r = mb * 16 + n;
-            av[mb] = hok ? *(const uint4*)(As + r * RB + (((q & ~7) | ((q & 7) ^ (r & 7))) << 4))
-                         : make_uint4(0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) C[mb][nb] = TT::mfma(as_vec8<V8>(av[mb]), Bp[ks][nb], C[mb][nb]);
-        }
-      }
-      __syncthreads();
-      more = s_more != 0;
-      __syncthreads();
-    }
-    i += gs;
+  const int64_t nvis = *a.n_vis;
+  const int64_t vlo = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_lo));
+  const int64_t vhi = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_hi));
+  if (threadIdx.x == 0 && cb == 0) a.nonempty[(int64_t)tr * a.nKB + kb] = vhi > vlo ? 1 : 0;
+  if (vhi <= vlo) return;
+  if (a.Gp == 128) {
+    if (c.width == 256) kb_block<TT, 4, 128>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 128>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+  } else {
+    if (c.width == 256) kb_block<TT, 4, 0>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 0>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   }
-  // ---- partial of this token range ----------------------------------------
-  float* out = a.part + (int64_t)tr * a.T2 * a.AW;
-  const int ocol = c.ocol0 + wave * 16 * NB + n;
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t row = kb_row0 + mb * 16 + 4 * g + k;
-      if (row < a.T2) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) out[row * a.AW + ocol + 16 * nb] = C[mb][nb][k];
-      }
+}
+
+// Visits of the sorted pairs: a visit starts where the composite key
+// (key block * ntok + token) changes.
+__global__ void __launch_bounds__(256) k_vis_flags(const int32_t* __restrict__ ck, int64_t n, int32_t sentinel,
+                                                   int32_t* __restrict__ flags) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t k = ck[i];
+  flags[i] = (k < sentinel && (i == 0 || ck[i - 1] != k)) ? 1 : 0;
+}
+
+// vis_start / vis_key of each visit (from the scanned flags), the key row
+// within its block of each sorted pair, and the visit count; vis_start[nvis]
+// is the number of valid pairs.
+__global__ void __launch_bounds__(256) k_vis_write(const int32_t* __restrict__ ck, const int32_t* __restrict__ svals,
+                                                   const int32_t* __restrict__ rows, int64_t n, int64_t ntok,
+                                                   int32_t sentinel, const int32_t* __restrict__ scan,
+                                                   int32_t* __restrict__ vis_start, int32_t* __restrict__ vis_key,
+                                                   int32_t* __restrict__ er, int32_t* __restrict__ n_vis) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t k = ck[i];
+  if (k >= sentinel) {
+    if (i == 0) {
+      *n_vis = 0;
+      vis_start[0] = 0;
     }
+    return;
+  }
+  const int32_t kb = (int32_t)(k / ntok);
+  er[i] = rows[svals[i]] - kb * kKB;
+  const bool st = i == 0 || ck[i - 1] != k;
+  const int32_t idx = scan[i];
+  if (st) {
+    vis_start[idx] = (int32_t)i;
+    vis_key[idx] = k;
+  }
+  if (i + 1 == n || ck[i + 1] >= sentinel) {
+    const int32_t nv = idx + (st ? 1 : 0);
+    vis_start[nv] = (int32_t)(i + 1);
+    *n_vis = nv;
   }
 }
 
@@ -244,24 +481,21 @@ void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO,
   hipLaunchKernelGGL(k_transpose, dim3((unsigned)(ntok * nsl)), dim3(256), 0, s, q, qr, dO, t0, G, Gp, Dr, qT, oT);
 }
 
-void launch_keyblock(int32_t dtype, const KbArgs& a, bool wide, hipStream_t s) {
-  // Column blocks 256 wide run with NB = 4, the 64-wide rope block with
-  // NB = 1; each call launches the blocks of one width, so that every kernel
-  // instance has a fixed register shape.
-  KbArgs w = a;
-  int m = 0;
-  for (int i = 0; i < a.nCB; ++i)
-    if ((a.cbs[i].width == 256) == wide) w.cbs[m++] = a.cbs[i];
-  if (m == 0) return;
-  w.nCB = m;
-  const dim3 grid((unsigned)(w.nTR * w.nKB * w.nCB)), block(256);
-  if (dtype == SFAG_BF16) {
-    if (wide) hipLaunchKernelGGL((k_keyblock<BF16, 4>), grid, block, 0, s, w);
-    else hipLaunchKernelGGL((k_keyblock<BF16, 1>), grid, block, 0, s, w);
-  } else {
-    if (wide) hipLaunchKernelGGL((k_keyblock<FP16, 4>), grid, block, 0, s, w);
-    else hipLaunchKernelGGL((k_keyblock<FP16, 1>), grid, block, 0, s, w);
-  }
+void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.nTR * a.nKB * a.nCB)), block(kThreads);
+  if (dtype == SFAG_BF16) hipLaunchKernelGGL(k_keyblock<BF16>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_keyblock<FP16>, grid, block, 0, s, a);
+}
+
+void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows, int64_t n, int64_t ntok,
+                   int32_t nkb, int32_t* flags, int32_t* scan_tmp, int32_t* vis_start, int32_t* vis_key, int32_t* er,
+                   int32_t* n_vis, hipStream_t s) {
+  const int32_t sentinel = (int32_t)((int64_t)nkb * ntok);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(k_vis_flags, dim3(grid), dim3(256), 0, s, ck, n, sentinel, flags);
+  launch_scan_i32(flags, n, scan_tmp, s);
+  hipLaunchKernelGGL(k_vis_write, dim3(grid), dim3(256), 0, s, ck, svals, rows, n, ntok, sentinel, flags, vis_start,
+                     vis_key, er, n_vis);
 }
 
 void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,

@@ -228,23 +228,30 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
         }
         int32_t* skeys = nullptr;
         int32_t* svals = nullptr;
+        const int64_t n = ntok * d.E;
         {
           TimedScope ts("kb_sort", s);
-          launch_csr(ntok * d.E, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals,
-                     at<int32_t>(workspace, w.sort_hist), nullptr, &svals, s, 1, ntok, &skeys);
+          launch_csr(n, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals, at<int32_t>(workspace, w.sort_hist),
+                     nullptr, &svals, s, 1, ntok, &skeys);
+          launch_visits(skeys, svals, rows, n, ntok, (int32_t)d.nKB, at<int32_t>(workspace, w.vis_flags),
+                        at<int32_t>(workspace, w.sort_hist), at<int32_t>(workspace, w.vis_start),
+                        at<int32_t>(workspace, w.vis_key), at<int32_t>(workspace, w.vis_er),
+                        at<int32_t>(workspace, w.vis_n), s);
         }
         KbArgs ka;
         ka.qT = qT;
         ka.oT = oT;
         ka.ds = ds;
         ka.p = pb;
-        ka.rows = rows;
-        ka.skeys = skeys;
         ka.svals = svals;
+        ka.er = at<int32_t>(workspace, w.vis_er);
+        ka.vis_start = at<int32_t>(workspace, w.vis_start);
+        ka.vis_key = at<int32_t>(workspace, w.vis_key);
+        ka.n_vis = at<int32_t>(workspace, w.vis_n);
         ka.nonempty = at<int32_t>(workspace, w.kb_nonempty);
         ka.part = at<float>(workspace, w.kb_part);
-        ka.n = ntok * d.E;
         ka.ntok = ntok;
+        ka.E = d.E;
         ka.Gp = d.Gp;
         ka.T2 = d.T2;
         ka.AW = d.AW;
@@ -252,21 +259,18 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
         ka.Dq = d.D + d.Dr;
         ka.nKB = (int32_t)d.nKB;
         ka.nTR = (int32_t)((ntok + d.TR - 1) / d.TR);
-        // column blocks: dK (two of 256), dKrope (64), dV (two of 256)
+        // column blocks: dK|dKrope (three of 192 with rope, two of 256
+        // without), dV (two of 256)
         int m = 0;
-        ka.cbs[m++] = ColBlock{0, 0, 0, 256};
-        ka.cbs[m++] = ColBlock{0, 256, 256, 256};
-        if (rope) ka.cbs[m++] = ColBlock{0, 512, 512, 64};
-        ka.cbs[m++] = ColBlock{1, 0, (int32_t)(d.D + d.Dr), 256};
-        ka.cbs[m++] = ColBlock{1, 256, (int32_t)(d.D + d.Dr) + 256, 256};
+        const int32_t dq = (int32_t)(d.D + d.Dr);
+        const int32_t wk = rope ? 192 : 256;
+        for (int32_t c0 = 0; c0 < dq; c0 += wk) ka.cbs[m++] = ColBlock{0, c0, c0, wk};
+        ka.cbs[m++] = ColBlock{1, 0, dq, 256};
+        ka.cbs[m++] = ColBlock{1, 256, dq + 256, 256};
         ka.nCB = m;
         {
           TimedScope ts("keyblock", s);
-          launch_keyblock(plan->dtype, ka, true, s);
-        }
-        if (rope) {
-          TimedScope ts("keyblock_rope", s);
-          launch_keyblock(plan->dtype, ka, false, s);
+          launch_keyblock(plan->dtype, ka, s);
         }
         {
           TimedScope ts("kb_reduce", s);

@@ -13,7 +13,7 @@ namespace sfag {
 // How the per-(token, position) dK/dV contributions reach the key rows:
 //   kScatterAtomic   fp32 atomic adds of each pair's row into the accumulators;
 //   kScatterPartials each pair's row stored, then summed per key in CSR order;
-//   kScatterKeyBlock contraction per block of 128 key rows over the tokens
+//   kScatterKeyBlock contraction per block of 256 key rows over the tokens
 //                    selecting them (pairs sorted by key block and token).
 enum Scatter : int32_t { kScatterAtomic = 0, kScatterPartials = 1, kScatterKeyBlock = 2 };
 
@@ -35,6 +35,11 @@ struct WorkspaceLayout {
   uint64_t oT = 0;         // 16-bit (chunk, 512, Gp): per-token transposed dO
   uint64_t kb_part = 0;    // fp32 (nTR, T2, AW): per token-range partial sums
   uint64_t kb_nonempty = 0;  // int32 (nTR, nKB)
+  uint64_t vis_flags = 0;  // int32 (chunk*E): visit starts, scanned in place
+  uint64_t vis_start = 0;  // int32 (chunk*E + 1): first sorted pair of each visit
+  uint64_t vis_key = 0;    // int32 (chunk*E): composite key of each visit
+  uint64_t vis_er = 0;     // int32 (chunk*E): key row within its block of each sorted pair
+  uint64_t vis_n = 0;      // int32: number of visits
   uint64_t total = 0;
 };
 
@@ -49,7 +54,7 @@ struct Dims {
   int64_t chunk = 0;       // tokens per chunk
   int32_t sort_bits = 0;   // bits of the CSR sort key (rows < T2, sentinel T2)
   int32_t kb_sort_bits = 0;  // bits of the key-block sort key (sentinel nKB * chunk)
-  int64_t nKB = 0;         // key blocks of 128 rows
+  int64_t nKB = 0;         // key blocks of kKeyBlockRows rows
   int64_t TR = 0;          // tokens per range of the key-block kernel
   int64_t nTR = 0;         // token ranges per chunk
 };
@@ -60,7 +65,7 @@ uint64_t align256(uint64_t x);
 WorkspaceLayout layout_for(const Dims& d, int32_t scatter);
 
 // Key rows per block of the key-centric dK/dV contraction.
-constexpr int kKeyBlockRows = 128;
+constexpr int kKeyBlockRows = 256;
 
 // Radix-sort block geometry shared by host and kernels.
 constexpr int kSortThreads = 256;

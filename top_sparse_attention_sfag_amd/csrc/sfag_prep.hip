@@ -347,7 +347,7 @@ static inline unsigned grid_for(uint64_t n, unsigned per_block, unsigned cap = 6
 }
 
 // In-place exclusive scan of n counts; tmp holds ceil(n / kScanSeg) ints.
-static void launch_scan(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s) {
+void launch_scan_i32(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s) {
   const int64_t nseg = (n + kScanSeg - 1) / kScanSeg;
   if (nseg <= 1) {
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, a, n);
@@ -401,7 +401,7 @@ void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E
     const int nxt = pass ? cur ^ 1 : 0;
     hipLaunchKernelGGL(k_sort_hist, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows, nvalid,
                        E, sentinel, hist, nblk, key_mode, ntok);
-    launch_scan(hist, 256 * nblk, scan_tmp, s);
+    launch_scan_i32(hist, 256 * nblk, scan_tmp, s);
     hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)nblk), dim3(kSortThreads), 0, s, n, pass, kin, vin, rows,
                        nvalid, E, sentinel, hist, nblk, keys[nxt], vals[nxt], key_mode, ntok);
     cur = nxt;

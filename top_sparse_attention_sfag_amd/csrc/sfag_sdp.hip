@@ -31,8 +31,24 @@ constexpr int kTile = 32;
 constexpr int kXcds = 8;
 constexpr int kRun = 16;
 
-__device__ __forceinline__ void lds_load16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 16, 0, 0);
+// Asynchronous global -> LDS copy of 16 bytes per lane (lane l writes at the
+// wave-uniform LDS address l_base + 16 l).  Inline asm on purpose: the
+// compiler does not track it, so it adds no waits of its own before LDS reads
+// of the other buffer; reads of copied data follow an explicit s_waitcnt and
+// a barrier.
+__device__ __forceinline__ void lds_load16(const void* g, const void* l) {
+  const uint32_t la = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not for its outstanding copies; the signal fences keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4));   // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <typename TT>
@@ -55,17 +71,24 @@ __device__ __forceinline__ int64_t unit_token(int b, int n_hb, int& hb) {
   return ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
 }
 
-// Issue the async gather of one tile: rows c0 .. c0+31 of the token (rows past
-// nv repeat row 0; their P and dS are 0).  K main rows (1024 B) and, when
-// WITH_V, V rows go one row per instruction; rope rows (DR*2 bytes) go 8 per
-// instruction.  Every wave of the block takes a share.
+// Row indices of a tile: lane r & 31 holds the key row of position c0 + r
+// (positions past nv repeat position 0; their P and dS are 0).  Loaded a
+// tile ahead of the gather that uses them.
+__device__ __forceinline__ int32_t tile_keys(const int32_t* rt, int nv, int c0, int lane) {
+  const int cl = c0 + (lane & 31);
+  return cl < nv ? rt[cl] : (nv > 0 ? rt[0] : 0);
+}
+
+// Issue the async gather of one tile (rows of keyv, see tile_keys).  K main
+// rows (1024 B) and, when WITH_V, V rows go one row per instruction; rope
+// rows (DR*2 bytes) go 8 per instruction.  Every wave of the block takes a
+// share.
 template <int DR, bool WITH_V>
-__device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr, const uint16_t* v,
-                                           const int32_t* rt, int nv, int c0, unsigned char* base, int km_bytes,
-                                           int kr_bytes, int wave, int nw, int lane) {
+__device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr, const uint16_t* v, int32_t keyv,
+                                           unsigned char* base, int km_bytes, int kr_bytes, int wave, int nw,
+                                           int lane) {
   for (int r = wave; r < kTile; r += nw) {
-    const int c = c0 + r;
-    const int64_t key = __builtin_amdgcn_readfirstlane(rt[c < nv ? c : 0]);
+    const int64_t key = __builtin_amdgcn_readlane(keyv, r);
     const int gc = lane ^ (r & 7);
     lds_load16(k + key * 512 + gc * 8, base + r * 1024);
     if (WITH_V) lds_load16(v + key * 512 + gc * 8, base + km_bytes + kr_bytes + r * 1024);
@@ -73,8 +96,7 @@ __device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr
   if (DR > 0) {
     for (int gi = wave; gi < kTile / 8; gi += nw) {
       const int r = gi * 8 + (lane >> 3);
-      const int c = c0 + r;
-      const int64_t key = rt[c < nv ? c : 0];
+      const int64_t key = __shfl(keyv, r);
       const int gc = (lane & 7) ^ (r & 7);
       lds_load16(kr + key * DR + gc * 8, base + km_bytes + gi * 8 * (DR * 2));
     }
@@ -151,11 +173,30 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   const int oK = m * 1024;
   const int oR = m * (DR * 2);
 
+  int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
+  // 32 positions x HB heads of each staged array to dS / P, 16-byte chunks
+  const int cpr = HB / 8;  // chunks per row
+  auto copy_out = [&](int c0) {
+    for (int q = tid; q < kTile * cpr; q += blockDim.x) {
+      const int j = q / cpr, ch = q - j * cpr;
+      const int hh = hb * HB + ch * 8;
+      if (c0 + j < nv && hh < a.Gp) {
+        const int64_t o = (tl * a.E + c0 + j) * a.Gp + hh;
+        *(uint4*)(a.ds_out + o) = *(const uint4*)(stage_ds + (j * 128 + ch * 8) * 2);
+        *(uint4*)(a.p_out + o) = *(const uint4*)(stage_p + (j * 128 + ch * 8) * 2);
+      }
+    }
+  };
+
+  // One tile: the stores of the previous tile's dS/P go out first, then the
+  // gather of the next tile, so that waiting for that gather at the next tile
+  // also covers those stores, issued a whole tile earlier.
   auto tile = [&](int c0, const unsigned char* Km, unsigned char* nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (c0 + kTile < nv)
-      issue_rows<DR, true>(a.k, a.kr, a.v, rt, nv, c0 + kTile, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    if (c0 + kTile < nv) issue_rows<DR, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
+    if (c0 > 0) copy_out(c0 - kTile);
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = Kr + KR_BYTES;
     f32x16 S, P;
@@ -194,6 +235,8 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) P = mfma32<TT>(as_vec8<V8>(av[j]), dOf[k0 + j], P);
     }
+    // every wave is done reading the staged previous tile
+    bar();
     // P, dS for head h and positions 8(i/4) + 4kg + (i%4)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -205,24 +248,17 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
       *(uint16_t*)(stage_ds + so) = TT::from_f(ds * a.ds_scale);
       *(uint16_t*)(stage_p + so) = TT::from_f(p);
     }
-    __syncthreads();
-    // 32 positions x HB heads of each array, 16-byte chunks
-    const int cpr = HB / 8;  // chunks per row
-    for (int q = tid; q < kTile * cpr; q += blockDim.x) {
-      const int j = q / cpr, ch = q - j * cpr;
-      const int hh = hb * HB + ch * 8;
-      if (c0 + j < nv && hh < a.Gp) {
-        const int64_t o = (tl * a.E + c0 + j) * a.Gp + hh;
-        *(uint4*)(a.ds_out + o) = *(const uint4*)(stage_ds + (j * 128 + ch * 8) * 2);
-        *(uint4*)(a.p_out + o) = *(const uint4*)(stage_p + (j * 128 + ch * 8) * 2);
-      }
-    }
   };
 
-  if (nv > 0) issue_rows<DR, true>(a.k, a.kr, a.v, rt, nv, 0, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
+  if (nv > 0) issue_rows<DR, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
+  keys = tile_keys(rt, nv, kTile, lane);
   for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
     tile(c0, buf0, buf1);
     if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+  }
+  if (nv > 0) {
+    __syncthreads();
+    copy_out((nv - 1) / kTile * kTile);
   }
 }
 
@@ -260,6 +296,7 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
 
   // dS rows of the tile (64 heads = 128 bytes each), 8 rows per instruction;
   // rows past nv are zero-filled instead.
+  int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
   auto issue_tile = [&](int c0, unsigned char* base) {
     unsigned char* dsb = base + KM_BYTES + KR_BYTES;
     const int r = wave * 8 + (lane >> 3);
@@ -268,7 +305,8 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
     // Zero fill before any asynchronous copy is issued, so that no plain LDS
     // store follows an asynchronous one into the same buffer.
     if (!live) *(uint4*)(dsb + r * 128 + (lane & 7) * 16) = make_uint4(0, 0, 0, 0);
-    issue_rows<DR, false>(a.k, a.kr, nullptr, rt, nv, c0, base, KM_BYTES, KR_BYTES, wave, 4, lane);
+    issue_rows<DR, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, 4, lane);
+    keys = tile_keys(rt, nv, c0 + kTile, lane);
     if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * 64 + (lane & 7) * 8, dsb + wave * 8 * 128);
   };
 

@@ -44,6 +44,7 @@ constexpr int kStageB = 256 * 64;          // up to 256 columns x 32 heads
 constexpr int kStageBytes = kStageA + 64 + kStageB;
 constexpr int kWin = 256;                  // visits whose metadata sit in LDS at a time
 constexpr int kEnt = 256;                  // pairs of a visit copied into LDS
+constexpr int kXcds = 8;                   // XCDs of the chip (workgroup b runs on XCD b % 8)
 
 // Asynchronous global -> LDS copies (lane l of the wave writes 16 or 4 bytes
 // at the wave-uniform LDS address l_base + l * size).  Written as inline asm
@@ -353,10 +354,19 @@ __global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
   __shared__ int32_t e_pair[kEnt];   // pairs of the visit whose map is built next
   __shared__ int32_t e_row[kEnt];
 
-  // unit order: token range major, then key block, then column block
-  const int cb = blockIdx.x % a.nCB;
-  const int kb = (blockIdx.x / a.nCB) % a.nKB;
-  const int tr = blockIdx.x / (a.nCB * a.nKB);
+  // XCD-aware unit order.  Workgroup b runs on XCD b % 8.  XCD x takes the
+  // token ranges 16p + x and 16p + 15 - x (p = 0, 1, ...; a snake, so that
+  // causal workloads, whose later ranges hold more pairs, stay balanced) and
+  // runs each as (key block, column block) units in that order: the column
+  // blocks of one key block read the same dS/P rows and the key blocks of one
+  // range the same Q/dO rows, now through the same L2.
+  const int xcd = blockIdx.x % kXcds, u = blockIdx.x / kXcds;
+  const int per_tr = a.nKB * a.nCB;
+  const int jt = u / per_tr, rem = u - jt * per_tr;
+  const int tr = 16 * (jt >> 1) + ((jt & 1) ? 15 - xcd : xcd);
+  if (tr >= a.nTR) return;
+  const int kb = rem / a.nCB;
+  const int cb = rem - kb * a.nCB;
   const ColBlock c = a.cbs[cb];
   const int64_t t_lo = (int64_t)tr * a.TR, t_hi = min<int64_t>(t_lo + a.TR, a.ntok);
   const int64_t nvis = *a.n_vis;
@@ -482,7 +492,9 @@ void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO,
 }
 
 void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.nTR * a.nKB * a.nCB)), block(kThreads);
+  // token ranges per XCD: two per group of 16 (see the unit order above)
+  const int64_t per_xcd = 2 * (((int64_t)a.nTR + 15) / 16);
+  const dim3 grid((unsigned)(kXcds * per_xcd * a.nKB * a.nCB)), block(kThreads);
   if (dtype == SFAG_BF16) hipLaunchKernelGGL(k_keyblock<BF16>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(k_keyblock<FP16>, grid, block, 0, s, a);
 }

@@ -9,8 +9,8 @@
 //          Q and dO fragments in registers; the 32 gathered K|Krope|V rows of
 //          a tile arrive in LDS through global_load_lds_dwordx4, double
 //          buffered, 16-byte chunks XOR-swizzled by row.
-//   k_dq   (token x 64 heads): dQ = scale·dS·K_sel.  Each wave owns every
-//          fourth 16-column block of dQ|dQrope for all 64 heads, so a tile's K rows
+//   k_dq   (token x 128 heads): dQ = scale·dS·K_sel.  Each wave owns every
+//          fourth 16-column block of dQ|dQrope for 64 heads, so a tile's K rows
 //          and dS rows are both read once per wave: K columns and dS head
 //          groups come out of LDS transposed with ds_read_b64_tr_b16.
 #include <algorithm>
@@ -263,16 +263,17 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_dq: 256 threads; head block of 64 heads; wave w owns the 16-column blocks
-// w, w+4, w+8, ... of dQ|dQrope (blocks 32..35 are the rope columns).
+// k_dq: 512 threads; head block of 128 heads; wave w takes heads
+// 64 (w / 4) .. +64 of the block and the 16-column blocks w % 4, w % 4 + 4,
+// ... of dQ|dQrope (blocks 32..35 are the rope columns).
 // ---------------------------------------------------------------------------
 template <typename TT, int DR>
-__global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
+__global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int NB = DQK / 64;             // column blocks per wave
   constexpr int KM_BYTES = kTile * 1024;
   constexpr int KR_BYTES = kTile * DR * 2;
-  constexpr int DS_BYTES = kTile * 128;     // 32 positions x 64 heads, 16-bit
+  constexpr int DS_BYTES = kTile * 256;     // 32 positions x 128 heads, 16-bit
   constexpr int BUF = KM_BYTES + KR_BYTES + DS_BYTES;
   typedef typename TT::vec8 V8;
 
@@ -284,7 +285,8 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
-  const int hmax = (int)(a.Gp - hb * 64);   // heads of this block present in the dS rows
+  const int hw = wave >> 2, wq = wave & 3;    // head half, column group
+  const int hmax = (int)(a.Gp - hb * 128);    // heads of this block present in the dS rows
   const int nv = a.nvalid[tl];
   const int32_t* rt = a.rows + tl * a.E;
 
@@ -294,33 +296,39 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // dS rows of the tile (64 heads = 128 bytes each), 8 rows per instruction;
-  // rows past nv are zero-filled instead.
+  // dS rows of the tile (128 heads = 256 bytes each), 4 rows per
+  // instruction: the lane writing position p of row r fetches chunk
+  // p ^ (r & 15); chunks of rows past nv or of heads past the block are
+  // zero-filled instead.
   int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
   auto issue_tile = [&](int c0, unsigned char* base) {
     unsigned char* dsb = base + KM_BYTES + KR_BYTES;
-    const int r = wave * 8 + (lane >> 3);
+    const int r = wave * 4 + (lane >> 4);
     const int c = c0 + r;
-    const bool live = c < nv && (lane & 7) * 8 < hmax;
+    const int q = n ^ (r & 15);
+    const bool live = c < nv && q * 8 < hmax;
     // Zero fill before any asynchronous copy is issued, so that no plain LDS
     // store follows an asynchronous one into the same buffer.
-    if (!live) *(uint4*)(dsb + r * 128 + (lane & 7) * 16) = make_uint4(0, 0, 0, 0);
-    issue_rows<DR, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, 4, lane);
+    if (!live) *(uint4*)(dsb + r * 256 + n * 16) = make_uint4(0, 0, 0, 0);
+    issue_rows<DR, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, 8, lane);
     keys = tile_keys(rt, nv, c0 + kTile, lane);
-    if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * 64 + (lane & 7) * 8, dsb + wave * 8 * 128);
+    if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * 128 + q * 8, dsb + wave * 1024);
   };
 
   // Transposed-read offsets (see lds_read_tr): K rows 4g+(n>>2) and +16, dS
-  // rows likewise.  Wave w owns the 16-column blocks w, w+4, w+8, ..., so
-  // block j of the wave starts at 16-byte chunk 2w + 8j of a K row and the
-  // XOR swizzle touches only the low three chunk bits: every read is one
-  // per-lane base plus a compile-time offset.
+  // rows likewise.  Wave w owns the 16-column blocks wq, wq+4, wq+8, ...
+  // (wq = w % 4), so block j of the wave starts at 16-byte chunk 2wq + 8j of
+  // a K row and the XOR swizzle touches only the low three chunk bits: every
+  // K read is one per-lane base plus a compile-time offset.
   const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;
   const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
-  const int sw = ((2 * wave + half) ^ x1) << 4;
+  const int sw = ((2 * wq + half) ^ x1) << 4;
   const int offM = r1 * 1024 + sw + hoff;
   const int offR = r1 * (DR * 2) + sw + hoff;
-  const int offD = r1 * 128 + 8 * (n & 3);
+  // dS: heads 64hw + 16s + 4(n & 3) .. +4 sit in chunk 8hw + 2s + half
+  int offD[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) offD[s] = r1 * 256 + (((8 * hw + 2 * s + half) ^ (r1 & 15)) << 4) + hoff;
 
   auto tile = [&](int c0, int cend, const unsigned char* Km, unsigned char* nxt) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -328,12 +336,12 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
     if (c0 + kTile < cend) issue_tile(c0 + kTile, nxt);
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Ds = Kr + KR_BYTES;
-    // A operands: dS of heads 16s + n at positions 4g+i and 16+4g+i
+    // A operands: dS of heads 64hw + 16s + n at positions 4g+i and 16+4g+i
     V8 A[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const unsigned char* p1 = Ds + offD + s * 32;
-      A[s] = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 128)));
+      const unsigned char* p1 = Ds + offD[s];
+      A[s] = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 256)));
     }
 #pragma unroll
     for (int nb0 = 0; nb0 < NB; nb0 += 3) {
@@ -344,10 +352,10 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
         if (nb < NB) {
           const unsigned char* p1;
           int rs;
-          if (nb < 8) {           // K columns 16(w + 4nb) ..
+          if (nb < 8) {           // K columns 16(wq + 4nb) ..
             p1 = Km + offM + nb * 128;
             rs = 16 * 1024;
-          } else {                // rope columns 16w ..
+          } else {                // rope columns 16wq ..
             p1 = Kr + offR;
             rs = 16 * (DR * 2);
           }
@@ -375,15 +383,16 @@ __global__ void __launch_bounds__(256, 1) k_dq(RowArgs a) {
     tile(c0, nv2, buf0, buf1);
     tile(c0 + kTile, nv2, buf1, buf0);
   }
-  // dQ[t][h][col] = scale * acc / ds_scale; lane holds heads 16s + 4g + i, column n
+  // dQ[t][h][col] = scale * acc / ds_scale; lane holds heads 16s + 4g + i of
+  // its half, column n
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = 16 * (wave + 4 * nb) + n;
+      const int col = 16 * (wq + 4 * nb) + n;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int hh = hb * 64 + 16 * s + 4 * g + i;
+        const int hh = hb * 128 + hw * 64 + 16 * s + 4 * g + i;
         if (hh < a.G) {
           const uint16_t v = TT::from_f(acc[s][nb][i] * a.dq_mul);
           if (col < 512) a.dq[(t * a.G + hh) * 512 + col] = v;
@@ -417,9 +426,9 @@ void launch_dq(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a_in.ntok + per - 1) / per * per;
   RowArgs a = a_in;
-  // k_dq: 64 heads per block
-  a.n_hb = (int32_t)((a.Gp + 63) / 64);
-  const dim3 g2((unsigned)(padded * a.n_hb)), b2(256);
+  // k_dq: 128 heads per block
+  a.n_hb = (int32_t)((a.Gp + 127) / 128);
+  const dim3 g2((unsigned)(padded * a.n_hb)), b2(512);
   if (dtype == SFAG_BF16) {
     if (rope) hipLaunchKernelGGL((k_dq<BF16, 64>), g2, b2, 0, s, a);
     else hipLaunchKernelGGL((k_dq<BF16, 0>), g2, b2, 0, s, a);

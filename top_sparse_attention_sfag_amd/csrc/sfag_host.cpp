@@ -8,6 +8,7 @@
 // (B in 1..256, S1/S2 up to 128K).
 #include <cmath>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <sstream>
@@ -345,8 +346,14 @@ extern "C" int sfag_workspace_size(
   d.chunk = chunk;
   d.nKB = (d.T2 + kKeyBlockRows - 1) / kKeyBlockRows;
   if (keyblock) {
-    // up to 16 token ranges per chunk; the key-block sort key must fit in 31 bits
-    d.TR = (chunk + 15) / 16;
+    // 16 token ranges per chunk (the XCD snake pairs ranges x and 15 - x),
+    // fewer when that would leave under 32 tokens per range or need more
+    // than 4 GiB of fp32 partials.  The key-block sort key must fit in 31 bits.
+    int64_t ntr = 16;
+    const int64_t part_bytes = d.T2 * (2 * d.D + d.Dr) * 4;
+    if (part_bytes > 0) ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, (4LL << 30) / part_bytes));
+    ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, chunk / 32));
+    d.TR = (chunk + ntr - 1) / ntr;
     d.nTR = (chunk + d.TR - 1) / d.TR;
     const int64_t sentinel = d.nKB * chunk;
     if (sentinel >= 0x7fffffffLL) {

@@ -2,13 +2,15 @@
 // "aclnnSparseFlashAttentionGrad", 功能说明 stages 1-3), split so that neither
 // holds more registers than the matrix cores can be fed from:
 //
-//   k_sdp  (token x up to 128 heads): Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ with
-//          v_mfma_f32_32x32x16 (32 positions x 32 heads per wave), then
+//   k_sdp  (token x up to 128 heads): S = Q·Kᵀ and dP = dO·Vᵀ with
+//          v_mfma_f32_32x32x16 (32 heads x 32 positions per wave), then
 //          P = exp(scale·S − max)/sum and dS = P ∘ (dP − Delta), stored as
-//          16-bit (token, position, head) rows.  Each wave keeps its 32 heads'
-//          Q and dO fragments in registers; the 32 gathered K|Krope|V rows of
-//          a tile arrive in LDS through global_load_lds_dwordx4, double
-//          buffered, 16-byte chunks XOR-swizzled by row.
+//          16-bit (token, position, head) rows straight from registers (each
+//          lane holds 4 consecutive heads of one position per group).  Each
+//          wave keeps its 32 heads' Q and dO fragments in registers; the 32
+//          gathered K|Krope|V rows of a tile arrive in LDS through
+//          global_load_lds_dwordx4, double buffered, 16-byte chunks
+//          XOR-swizzled by row.
 //   k_dq   (token x 128 heads): dQ = scale·dS·K_sel.  Each wave owns every
 //          fourth 16-column block of dQ|dQrope for 64 heads, so a tile's K rows
 //          and dS rows are both read once per wave: K columns and dS head
@@ -82,14 +84,17 @@ __device__ __forceinline__ int32_t tile_keys(const int32_t* rt, int nv, int c0, 
 // Issue the async gather of one tile (rows of keyv, see tile_keys).  K main
 // rows (1024 B) and, when WITH_V, V rows go one row per instruction; rope
 // rows (DR*2 bytes) go 8 per instruction.  Every wave of the block takes a
-// share.
-template <int DR, bool WITH_V>
+// share.  The lane writing 16-byte position p of row r fetches chunk
+// p ^ swz(r): with WIDE, swz = r & 15 for the 1024-byte rows and
+// (r >> 1) & 7 for the rope rows (16 consecutive rows then fill all 64 LDS
+// banks when read one chunk per row); otherwise r & 7 for both.
+template <int DR, bool WITH_V, bool WIDE>
 __device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr, const uint16_t* v, int32_t keyv,
                                            unsigned char* base, int km_bytes, int kr_bytes, int wave, int nw,
                                            int lane) {
   for (int r = wave; r < kTile; r += nw) {
     const int64_t key = __builtin_amdgcn_readlane(keyv, r);
-    const int gc = lane ^ (r & 7);
+    const int gc = lane ^ (r & (WIDE ? 15 : 7));
     lds_load16(k + key * 512 + gc * 8, base + r * 1024);
     if (WITH_V) lds_load16(v + key * 512 + gc * 8, base + km_bytes + kr_bytes + r * 1024);
   }
@@ -97,7 +102,7 @@ __device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr
     for (int gi = wave; gi < kTile / 8; gi += nw) {
       const int r = gi * 8 + (lane >> 3);
       const int64_t key = __shfl(keyv, r);
-      const int gc = (lane & 7) ^ (r & 7);
+      const int gc = (lane & 7) ^ (WIDE ? ((r >> 1) & 7) : (r & 7));
       lds_load16(kr + key * DR + gc * 8, base + km_bytes + gi * 8 * (DR * 2));
     }
   }
@@ -108,6 +113,11 @@ __device__ __forceinline__ void issue_rows(const uint16_t* k, const uint16_t* kr
 // ---------------------------------------------------------------------------
 // k_sdp: blockDim = 64 * nw, nw = min(4, Gp / 32); head block = 32 * nw heads.
 // ---------------------------------------------------------------------------
+template <typename TT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)TT::from_f(lo) | ((uint32_t)TT::from_f(hi) << 16);
+}
+
 template <typename TT, int DR>
 __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   constexpr int DQK = 512 + DR;
@@ -116,15 +126,11 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   constexpr int KM_BYTES = kTile * 1024;
   constexpr int KR_BYTES = kTile * DR * 2;
   constexpr int BUF = KM_BYTES + KR_BYTES + kTile * 1024;
-  constexpr int STAGE = kTile * 128 * 2;  // 32 positions x up to 128 heads, 16-bit
   typedef typename TT::vec8 V8;
 
-  // Two tile buffers as separate LDS objects: the compiler then knows that
-  // the asynchronous fills of one do not alias reads of the other.
+  // Two tile buffers as separate LDS objects.
   __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
-  __shared__ __attribute__((aligned(16))) unsigned char stage_ds[STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char stage_p[STAGE];
 
   const int nw = blockDim.x >> 6;
   const int HB = 32 * nw;
@@ -133,12 +139,12 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hi = lane & 31, kg = lane >> 5;   // head within the wave, k-group
+  const int hi = lane & 31, kg = lane >> 5;   // row of the A operand, k-group
   const int h0 = hb * HB + wave * 32;
   const int h = h0 + hi;
   const bool hv = h < a.G;
 
-  // B operands: Q and dO rows of head h, 8 consecutive columns per k-step.
+  // A operands: Q and dO rows of head h, 8 consecutive columns per k-step.
   V8 Qf[KS_QK], dOf[KS_V];
 #pragma unroll
   for (int ks = 0; ks < KS_QK; ++ks) {
@@ -156,110 +162,121 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     if (hv) v = *(const uint4*)(a.dO + (t * a.G + h) * 512 + 16 * ks + 8 * kg);
     dOf[ks] = as_vec8<V8>(v);
   }
-  float mlog = 0.f, inv_l = 0.f, dl = 0.f;
-  bool live = false;
-  if (hv) {
-    const float m = a.smax[t * a.G + h], l = a.ssum[t * a.G + h];
-    live = l > 0.f;
-    inv_l = live ? 1.f / l : 0.f;
-    mlog = m * kLog2e;
-    dl = a.delta[t * a.G + h];
+  // S = Q·Kᵀ and dP = dO·Vᵀ come out as (32 heads x 32 positions): lane l
+  // holds position l % 32 and heads h0 + 8(i/4) + 4kg + i%4, i = 0..15.
+  // Per head: P = exp2(scale·log2e·S − mb), mb = log2e·max + log2(sum)
+  // (+inf for heads past G or with an empty row, which gives P = 0).
+  float mb[16], dl[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int hh = h0 + 8 * (i >> 2) + 4 * kg + (i & 3);
+    mb[i] = __builtin_inff();
+    dl[i] = 0.f;
+    if (hh < a.G) {
+      const float m = a.smax[t * a.G + hh], l = a.ssum[t * a.G + hh];
+      if (l > 0.f) mb[i] = m * kLog2e + __log2f(l);
+      dl[i] = a.delta[t * a.G + hh];
+    }
   }
   const int nv = a.nvalid[tl];
   const int32_t* rt = a.rows + tl * a.E;
-  // A operand rows: position m = lane & 31 of the tile, chunk 2ks + kg.
+  // B operand rows: position m = lane & 31 of the tile, chunk 2ks + kg.
   const int m = hi;
-  const int x = m & 7;
+  const int x = m & 15, xr = (m >> 1) & 7;   // swizzles of the K|V and rope rows
   const int oK = m * 1024;
   const int oR = m * (DR * 2);
 
   int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
-  // 32 positions x HB heads of each staged array to dS / P, 16-byte chunks
-  const int cpr = HB / 8;  // chunks per row
-  auto copy_out = [&](int c0) {
-    for (int q = tid; q < kTile * cpr; q += blockDim.x) {
-      const int j = q / cpr, ch = q - j * cpr;
-      const int hh = hb * HB + ch * 8;
-      if (c0 + j < nv && hh < a.Gp) {
-        const int64_t o = (tl * a.E + c0 + j) * a.Gp + hh;
-        *(uint4*)(a.ds_out + o) = *(const uint4*)(stage_ds + (j * 128 + ch * 8) * 2);
-        *(uint4*)(a.p_out + o) = *(const uint4*)(stage_p + (j * 128 + ch * 8) * 2);
+  // P and dS of the previous tile, packed, stored at the start of the next
+  // tile (before its gather is issued, so that waiting for that gather also
+  // covers these stores, issued a whole tile earlier)
+  uint2 pend_p[4], pend_ds[4];
+  int pend_pos = -1;
+  auto store_pending = [&]() {
+    if (pend_pos >= 0 && pend_pos < nv) {
+      const int64_t orow = (tl * a.E + pend_pos) * a.Gp;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int hh0 = h0 + 8 * q4 + 4 * kg;
+        if (hh0 < a.Gp) {
+          *(uint2*)(a.p_out + orow + hh0) = pend_p[q4];
+          *(uint2*)(a.ds_out + orow + hh0) = pend_ds[q4];
+        }
       }
     }
   };
 
-  // One tile: the stores of the previous tile's dS/P go out first, then the
-  // gather of the next tile, so that waiting for that gather at the next tile
-  // also covers those stores, issued a whole tile earlier.
   auto tile = [&](int c0, const unsigned char* Km, unsigned char* nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (c0 + kTile < nv) issue_rows<DR, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    store_pending();
+    if (c0 + kTile < nv)
+      issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
     keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
-    if (c0 > 0) copy_out(c0 - kTile);
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = Kr + KR_BYTES;
     f32x16 S, P;
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = P[i] = 0.f;
-    // Sᵀ over D (then Dr): batches of 4 operand reads ahead of their MFMAs
+    // S over D (then Dr): batches of 4 operand reads ahead of their MFMAs
 #pragma unroll
     for (int k0 = 0; k0 < 32; k0 += 4) {
-      uint4 av[4];
+      uint4 bv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ch = 2 * (k0 + j) + kg;
-        av[j] = *(const uint4*)(Km + oK + (((ch & ~7) | ((ch & 7) ^ x)) << 4));
+        bv[j] = *(const uint4*)(Km + oK + ((ch ^ x) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S = mfma32<TT>(as_vec8<V8>(av[j]), Qf[k0 + j], S);
+      for (int j = 0; j < 4; ++j) S = mfma32<TT>(Qf[k0 + j], as_vec8<V8>(bv[j]), S);
     }
     if (DR > 0) {
-      uint4 av[4];
+      uint4 bv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ch = 2 * j + kg;
-        av[j] = *(const uint4*)(Kr + oR + ((ch ^ x) << 4));
+        bv[j] = *(const uint4*)(Kr + oR + ((ch ^ xr) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S = mfma32<TT>(as_vec8<V8>(av[j]), Qf[32 + j], S);
+      for (int j = 0; j < 4; ++j) S = mfma32<TT>(Qf[32 + j], as_vec8<V8>(bv[j]), S);
     }
 #pragma unroll
     for (int k0 = 0; k0 < KS_V; k0 += 4) {
-      uint4 av[4];
+      uint4 bv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ch = 2 * (k0 + j) + kg;
-        av[j] = *(const uint4*)(Vm + oK + (((ch & ~7) | ((ch & 7) ^ x)) << 4));
+        bv[j] = *(const uint4*)(Vm + oK + ((ch ^ x) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) P = mfma32<TT>(as_vec8<V8>(av[j]), dOf[k0 + j], P);
+      for (int j = 0; j < 4; ++j) P = mfma32<TT>(dOf[k0 + j], as_vec8<V8>(bv[j]), P);
     }
-    // every wave is done reading the staged previous tile
-    bar();
-    // P, dS for head h and positions 8(i/4) + 4kg + (i%4)
+    // P and dS of position c0 + m for the lane's 16 heads
+    const bool valid = c0 + m < nv;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = 8 * (i >> 2) + 4 * kg + (i & 3);
-      const bool ok = live && (c0 + j < nv);
-      const float p = ok ? exp2f(S[i] * a.scale_log2 - mlog) * inv_l : 0.f;
-      const float ds = p * (P[i] - dl);
-      const int so = (j * 128 + wave * 32 + hi) * 2;
-      *(uint16_t*)(stage_ds + so) = TT::from_f(ds * a.ds_scale);
-      *(uint16_t*)(stage_p + so) = TT::from_f(p);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float pv[4], dv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = 4 * q4 + jj;
+        float p = __builtin_amdgcn_exp2f(S[i] * a.scale_log2 - mb[i]);
+        p = valid ? p : 0.f;
+        pv[jj] = p;
+        dv[jj] = p * (P[i] - dl[i]) * a.ds_scale;
+      }
+      pend_p[q4] = make_uint2(pack2<TT>(pv[0], pv[1]), pack2<TT>(pv[2], pv[3]));
+      pend_ds[q4] = make_uint2(pack2<TT>(dv[0], dv[1]), pack2<TT>(dv[2], dv[3]));
     }
+    pend_pos = c0 + m;
   };
 
-  if (nv > 0) issue_rows<DR, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
+  if (nv > 0) issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
   keys = tile_keys(rt, nv, kTile, lane);
   for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
     tile(c0, buf0, buf1);
     if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
   }
-  if (nv > 0) {
-    __syncthreads();
-    copy_out((nv - 1) / kTile * kTile);
-  }
+  store_pending();
 }
 
 // ---------------------------------------------------------------------------
@@ -310,7 +327,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
     // Zero fill before any asynchronous copy is issued, so that no plain LDS
     // store follows an asynchronous one into the same buffer.
     if (!live) *(uint4*)(dsb + r * 256 + n * 16) = make_uint4(0, 0, 0, 0);
-    issue_rows<DR, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, 8, lane);
+    issue_rows<DR, false, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, 8, lane);
     keys = tile_keys(rt, nv, c0 + kTile, lane);
     if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * 128 + q * 8, dsb + wave * 1024);
   };

@@ -207,6 +207,8 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   };
 
   auto tile = [&](int c0, const unsigned char* Km, unsigned char* nxt) {
+    // (the previous tile's MFMAs stay above this wait: the wait stalls issue)
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     store_pending();
@@ -218,17 +220,22 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     f32x16 S, P;
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = P[i] = 0.f;
-    // S over D (then Dr): batches of 4 operand reads ahead of their MFMAs
+    // S over D and dP over D as two interleaved chains (independent MFMAs
+    // back to back), operand reads issued two k-steps ahead, then S over Dr
+    uint4 kv[3], vv[3];
+    auto rd = [&](int ks, int slot) {
+      const int ch = 2 * ks + kg;
+      kv[slot] = *(const uint4*)(Km + oK + ((ch ^ x) << 4));
+      vv[slot] = *(const uint4*)(Vm + oK + ((ch ^ x) << 4));
+    };
+    rd(0, 0);
+    rd(1, 1);
 #pragma unroll
-    for (int k0 = 0; k0 < 32; k0 += 4) {
-      uint4 bv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = 2 * (k0 + j) + kg;
-        bv[j] = *(const uint4*)(Km + oK + ((ch ^ x) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S = mfma32<TT>(Qf[k0 + j], as_vec8<V8>(bv[j]), S);
+    for (int ks = 0; ks < 32; ++ks) {
+      if (ks + 2 < 32) rd(ks + 2, (ks + 2) % 3);
+      S = mfma32<TT>(Qf[ks], as_vec8<V8>(kv[ks % 3]), S);
+      P = mfma32<TT>(dOf[ks], as_vec8<V8>(vv[ks % 3]), P);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (DR > 0) {
       uint4 bv[4];
@@ -239,17 +246,6 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) S = mfma32<TT>(Qf[32 + j], as_vec8<V8>(bv[j]), S);
-    }
-#pragma unroll
-    for (int k0 = 0; k0 < KS_V; k0 += 4) {
-      uint4 bv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = 2 * (k0 + j) + kg;
-        bv[j] = *(const uint4*)(Vm + oK + ((ch ^ x) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) P = mfma32<TT>(dOf[k0 + j], as_vec8<V8>(bv[j]), P);
     }
     // P and dS of position c0 + m for the lane's 16 heads
     const bool valid = c0 + m < nv;
@@ -348,6 +344,8 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
   for (int s = 0; s < 4; ++s) offD[s] = r1 * 256 + (((8 * hw + 2 * s + half) ^ (r1 & 15)) << 4) + hoff;
 
   auto tile = [&](int c0, int cend, const unsigned char* Km, unsigned char* nxt) {
+    // (the previous tile's MFMAs stay above this wait: the wait stalls issue)
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (c0 + kTile < cend) issue_tile(c0 + kTile, nxt);

@@ -314,6 +314,10 @@ extern "C" int sfag_workspace_size(
     if (env && std::strcmp(env, "keyblock") == 0) sc = kScatterKeyBlock;
     if (env && std::strcmp(env, "partials") == 0) sc = kScatterPartials;
     if (env && std::strcmp(env, "atomic") == 0) sc = deterministic ? kScatterPartials : kScatterAtomic;
+    // the key-block kernel addresses one token's dS/P rows (E x Gp halves)
+    // through a buffer resource with a 31-bit size
+    if (sc == kScatterKeyBlock && (uint64_t)d.E * (uint64_t)d.Gp * 2 > 0x7fffffffULL)
+      sc = deterministic ? kScatterPartials : kScatterAtomic;
     p->scatter = sc;
   }
   const bool partials = p->scatter == kScatterPartials;

@@ -58,6 +58,22 @@ __device__ __forceinline__ void dma16(const void* g, const void* l) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
                : "memory");
 }
+// Same copy through a buffer resource: a lane whose offset lies past the
+// resource's size fetches nothing (bounds-checked buffer access), so rows that
+// are never read cost no memory traffic.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* l) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
+               : "memory");
+}
+constexpr uint32_t kOutside = 0x80000000u;   // offset past any resource size used here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, bytes,
+                                           0x00020000);
+}
 __device__ __forceinline__ void dma4(const void* g, const void* l) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
                : "memory");
@@ -181,10 +197,13 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // A of stage (visit, ks): 256 rows x 4 chunks (heads 32ks + 8q .. +8), 16
   // instructions, wave w issuing w, w+4, w+8, w+12; the lane writing position
   // p of row r fetches chunk p ^ ((r >> 2) & 3).  Rows not selected (and
-  // chunks past the heads) re-read the token's first row into slots that are
-  // never read.  B: the block's columns x 4 chunks likewise, NB per wave.
+  // chunks past the heads) take an offset outside the resource: they fetch
+  // nothing, and their slots are never read.  B: the block's columns x 4
+  // chunks likewise, NB per wave.
   auto issue_stage = [&](int b, int64_t tl, int ks, unsigned char* st) {
-    const uint16_t* arow0 = Asrc + tl * a.E * Gp;
+    // A rows of token tl: pairs tl*E .. tl*E + E - 1, one buffer resource
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
+    const int32_t p0 = (int32_t)(tl * a.E);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = wave + 4 * k;
@@ -192,8 +211,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       const int q = (lane & 3) ^ ((row >> 2) & 3);
       const int hq = 32 * ks + 8 * q;
       const int32_t pr = sh.prim[b][row];
-      const uint16_t* src = (pr >= 0 && hq < Gp) ? Asrc + (int64_t)pr * Gp + hq : arow0;
-      dma16(src, st + i * 1024);
+      const uint32_t off = (pr >= 0 && hq < Gp) ? (uint32_t)(((pr - p0) * Gp + hq) * 2) : kOutside;
+      bdma16(ars, off, st + i * 1024);
     }
     const uint16_t* bcol0 = Bsrc + (tl * Bcols + c.tcol0) * Gp;
 #pragma unroll

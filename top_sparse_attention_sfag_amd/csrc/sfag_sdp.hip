@@ -16,6 +16,7 @@
 //          and dS rows are both read once per wave: K columns and dS head
 //          groups come out of LDS transposed with ds_read_b64_tr_b16.
 #include <algorithm>
+#include <type_traits>
 
 #include "sfag_device.h"
 #include "sfag_kernels.h"
@@ -41,6 +42,14 @@ constexpr int kRun = 16;
 __device__ __forceinline__ void lds_load16(const void* g, const void* l) {
   const uint32_t la = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+}
+
+// Same, with the LDS address given as a 32-bit offset.
+__device__ __forceinline__ void lds_load16_at(const void* g, uint32_t la) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_off(const void* l) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
 }
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations,
@@ -118,7 +127,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)TT::from_f(lo) | ((uint32_t)TT::from_f(hi) << 16);
 }
 
-template <typename TT, int DR>
+template <typename TT, int DR, int NW>
 __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int KS_QK = DQK / 16;   // k-steps of 16 along D+Dr
@@ -132,7 +141,7 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
 
-  const int nw = blockDim.x >> 6;
+  constexpr int nw = NW;
   const int HB = 32 * nw;
   int hb;
   const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb);
@@ -192,16 +201,41 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   // covers these stores, issued a whole tile earlier)
   uint2 pend_p[4], pend_ds[4];
   int pend_pos = -1;
+  // store j of 8: P (j even) or dS (j odd) of head group j / 2
+  auto store_one = [&](int j) {
+    const int q4 = j >> 1;
+    const int hh0 = h0 + 8 * q4 + 4 * kg;
+    if (pend_pos >= 0 && pend_pos < nv && hh0 < a.Gp) {
+      const int64_t o = (tl * a.E + pend_pos) * a.Gp + hh0;
+      if (j & 1) *(uint2*)(a.ds_out + o) = pend_ds[q4];
+      else *(uint2*)(a.p_out + o) = pend_p[q4];
+    }
+  };
   auto store_pending = [&]() {
-    if (pend_pos >= 0 && pend_pos < nv) {
-      const int64_t orow = (tl * a.E + pend_pos) * a.Gp;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int hh0 = h0 + 8 * q4 + 4 * kg;
-        if (hh0 < a.Gp) {
-          *(uint2*)(a.p_out + orow + hh0) = pend_p[q4];
-          *(uint2*)(a.ds_out + orow + hh0) = pend_ds[q4];
-        }
+    for (int j = 0; j < 8; ++j) store_one(j);
+  };
+  // The gather of a tile as a fixed list of copy instructions per wave: K
+  // and V rows wave + nw*j (two each), then rope groups wave + nw*j (8 rows
+  // each); entries past the tile's rows (nw = 3) are skipped.
+  constexpr int kRowOps = 2 * ((kTile + nw - 1) / nw);
+  constexpr int kOps = kRowOps + (DR > 0 ? (kTile / 8 + nw - 1) / nw : 0);
+  auto issue_op = [&](int i, int32_t keyv, uint32_t base) {
+    if (i < kRowOps) {
+      const int r = wave + nw * (i >> 1);
+      if (r < kTile) {
+        const int64_t key = __builtin_amdgcn_readlane(keyv, r);
+        const int gc = lane ^ (r & 15);
+        if (i & 1) lds_load16_at(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+        else lds_load16_at(a.k + key * 512 + gc * 8, base + r * 1024);
+      }
+    } else {
+      const int gi = wave + nw * (i - kRowOps);
+      if (gi < kTile / 8) {
+        const int r = gi * 8 + (lane >> 3);
+        const int64_t key = __shfl(keyv, r);
+        const int gc = (lane & 7) ^ ((r >> 1) & 7);
+        lds_load16_at(a.kr + key * DR + gc * 8, base + KM_BYTES + gi * 8 * (DR * 2));
       }
     }
   };
@@ -211,10 +245,12 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    store_pending();
-    if (c0 + kTile < nv)
-      issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
-    keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
+    const bool more = c0 + kTile < nv;
+    const uint32_t nxt_l = lds_off(nxt);
+    // With fewer than four waves (more copies per wave) the copies go out
+    // here at once; spreading them would cost registers.
+    constexpr bool kSpread = NW == 4;
+    if (!kSpread && more) issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = Kr + KR_BYTES;
     f32x16 S, P;
@@ -233,10 +269,17 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
       if (ks + 2 < 32) rd(ks + 2, (ks + 2) % 3);
+      // the next tile's copies over the first 24 k-steps and the previous
+      // tile's stores over the last 8, between the MFMAs
+      if (kSpread && more && ks < 24)
+        #pragma unroll
+        for (int i = ks * kOps / 24; i < (ks + 1) * kOps / 24; ++i) issue_op(i, keys, nxt_l);
+      if (ks >= 24) store_one(ks - 24);
       S = mfma32<TT>(Qf[ks], as_vec8<V8>(kv[ks % 3]), S);
       P = mfma32<TT>(dOf[ks], as_vec8<V8>(vv[ks % 3]), P);
       __builtin_amdgcn_sched_barrier(0);
     }
+    keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
     if (DR > 0) {
       uint4 bv[4];
 #pragma unroll
@@ -427,12 +470,22 @@ void launch_sdp(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
   const int nw = (int)std::min<int64_t>(4, a.Gp / 32);
   a.n_hb = (int32_t)((a.Gp + 32 * nw - 1) / (32 * nw));
   const dim3 g1((unsigned)(padded * a.n_hb)), b1(64 * nw);
+  auto go = [&](auto tt, auto dr) {
+    typedef decltype(tt) T;
+    constexpr int D = decltype(dr)::value;
+    switch (nw) {
+      case 1: hipLaunchKernelGGL((k_sdp<T, D, 1>), g1, b1, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((k_sdp<T, D, 2>), g1, b1, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((k_sdp<T, D, 3>), g1, b1, 0, s, a); break;
+      default: hipLaunchKernelGGL((k_sdp<T, D, 4>), g1, b1, 0, s, a); break;
+    }
+  };
   if (dtype == SFAG_BF16) {
-    if (rope) hipLaunchKernelGGL((k_sdp<BF16, 64>), g1, b1, 0, s, a);
-    else hipLaunchKernelGGL((k_sdp<BF16, 0>), g1, b1, 0, s, a);
+    if (rope) go(BF16(), std::integral_constant<int, 64>());
+    else go(BF16(), std::integral_constant<int, 0>());
   } else {
-    if (rope) hipLaunchKernelGGL((k_sdp<FP16, 64>), g1, b1, 0, s, a);
-    else hipLaunchKernelGGL((k_sdp<FP16, 0>), g1, b1, 0, s, a);
+    if (rope) go(FP16(), std::integral_constant<int, 64>());
+    else go(FP16(), std::integral_constant<int, 0>());
   }
 }
 

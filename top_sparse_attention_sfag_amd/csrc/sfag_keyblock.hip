@@ -39,9 +39,8 @@ namespace {
 constexpr int kKB = kKeyBlock;             // key rows per block (256)
 constexpr int kThreads = 256;              // 4 waves, one per SIMD
 constexpr int kStageA = kKB * 64;          // 256 rows x 32 heads, 16-bit
-constexpr int kZeroA = kStageA;            // a zero row after the rows
 constexpr int kStageB = 256 * 64;          // up to 256 columns x 32 heads
-constexpr int kStageBytes = kStageA + 64 + kStageB;
+constexpr int kStageBytes = kStageA + kStageB;
 constexpr int kWin = 256;                  // visits whose metadata sit in LDS at a time
 constexpr int kEnt = 256;                  // pairs of a visit copied into LDS
 constexpr int kXcds = 8;                   // XCDs of the chip (workgroup b runs on XCD b % 8)
@@ -54,17 +53,12 @@ constexpr int kXcds = 8;                   // XCDs of the chip (workgroup b runs
 __device__ __forceinline__ uint32_t lds_addr(const void* l) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
 }
-__device__ __forceinline__ void dma16(const void* g, const void* l) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
-               : "memory");
-}
-// Same copy through a buffer resource: a lane whose offset lies past the
-// resource's size fetches nothing (bounds-checked buffer access), so rows that
-// are never read cost no memory traffic.
-__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* l) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-               "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
-               : "memory");
+// (LDS destinations are 32-bit LDS addresses, wave-uniform.)
+// Copy through a buffer resource: a lane whose offset lies past the
+// resource's size fetches nothing (bounds-checked buffer access) and lands
+// zeros, so rows that are never used cost no memory traffic.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t l) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(l) : "memory");
 }
 constexpr uint32_t kOutside = 0x80000000u;   // offset past any resource size used here
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -74,9 +68,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, const void* l) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(l)))
-               : "memory");
+__device__ __forceinline__ void dma4(const void* g, uint32_t l) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(l) : "memory");
 }
 
 __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int64_t v) {
@@ -176,6 +169,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     const int64_t s0 = v_start(v);
     for (int j = tid + kEnt; j < cnt; j += kThreads) add_entry(b, a.svals[s0 + j], a.er[s0 + j]);
   };
+  const uint32_t l_pair = lds_addr(e_pair), l_row = lds_addr(e_row);
   // copy of visit v's first kEnt pairs (ids and key rows) into LDS: 8
   // dword-copy instructions, two per wave; lanes past the visit re-read
   // its first pair
@@ -188,8 +182,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       const int part = ins & 3;
       const int e = part * 64 + lane;
       const int64_t src = s0 + (e < cnt ? e : 0);
-      if (ins < 4) dma4(a.svals + src, &e_pair[part * 64]);
-      else dma4(a.er + src, &e_row[part * 64]);
+      if (ins < 4) dma4(a.svals + src, l_pair + part * 256);
+      else dma4(a.er + src, l_row + part * 256);
     }
   };
 
@@ -200,56 +194,67 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // chunks past the heads) take an offset outside the resource: they fetch
   // nothing, and their slots are never read.  B: the block's columns x 4
   // chunks likewise, NB per wave.
-  auto issue_stage = [&](int b, int64_t tl, int ks, unsigned char* st) {
-    // A rows of token tl: pairs tl*E .. tl*E + E - 1, one buffer resource
+  auto issue_stage = [&](int b, int64_t tl, int ks, uint32_t st) {
+    // A rows of token tl: pairs tl*E .. tl*E + E - 1, one buffer resource.
+    // The slot map entries are read before the first copy is issued (a copy
+    // is a memory clobber: reads after it would wait one by one).
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
     const int32_t p0 = (int32_t)(tl * a.E);
+    int32_t pr[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pr[k] = sh.prim[b][16 * (wave + 4 * k) + (lane >> 2)];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = wave + 4 * k;
       const int row = 16 * i + (lane >> 2);
       const int q = (lane & 3) ^ ((row >> 2) & 3);
       const int hq = 32 * ks + 8 * q;
-      const int32_t pr = sh.prim[b][row];
-      const uint32_t off = (pr >= 0 && hq < Gp) ? (uint32_t)(((pr - p0) * Gp + hq) * 2) : kOutside;
+      const uint32_t off = (pr[k] >= 0 && hq < Gp) ? (uint32_t)(((pr[k] - p0) * Gp + hq) * 2) : kOutside;
       bdma16(ars, off, st + i * 1024);
     }
-    const uint16_t* bcol0 = Bsrc + (tl * Bcols + c.tcol0) * Gp;
+    // B columns of token tl, one buffer resource over the block's columns
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bsrc + (tl * Bcols + c.tcol0) * Gp, (int)(NB * 64 * Gp * 2));
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int i = wave + 4 * k;
       const int col = 16 * i + (lane >> 2);
       const int q = (lane & 3) ^ ((col >> 2) & 3);
       const int hq = 32 * ks + 8 * q;
-      const uint16_t* src = hq < Gp ? bcol0 + (int64_t)col * Gp + hq : bcol0;
-      dma16(src, st + kStageA + 64 + i * 1024);
+      const uint32_t off = hq < Gp ? (uint32_t)((col * Gp + hq) * 2) : kOutside;
+      bdma16(brs, off, st + kStageA + i * 1024);
     }
   };
-  // bit mb: this lane's row of MFMA block mb is listed more than r times
-  auto selmask = [&](int b, int r) -> unsigned {
-    unsigned m = 0;
+  // Round r of a stage (r >= 1, keys listed more than once by the token):
+  // the rows listed exactly r times leave the sum, so their stage rows are
+  // cleared (between barriers: other waves may still read the previous
+  // round).
+  auto drop_rows = [&](unsigned char* st, int b, int r) {
+    bar();
+    if (sh.cnt[b][tid] == r) {
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) m |= (sh.cnt[b][mb * 16 + n] > r ? 1u : 0u) << mb;
-    return m;
+      for (int j = 0; j < 4; ++j) *(uint4*)(st + tid * 64 + j * 16) = make_uint4(0, 0, 0, 0);
+    }
+    bar();
   };
   // C += A · B over the 32 heads of one stage
   const int bcol = wave * 16 * NB + n;
-  auto compute = [&](const unsigned char* st, unsigned sel, int ks) {
-    const bool qok = 32 * ks + 8 * g < Gp;
+  // Rows the token does not select, and head chunks past Gp, hold zeros in
+  // the stage (their copies fetch nothing and land zeros), so every row is
+  // read as it is.
+  auto compute = [&](const unsigned char* st) {
     const int po = (g ^ (n >> 2)) << 4;          // rows mb*16 + n: (r >> 2) & 3 = n >> 2
     V8 Bf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = bcol + 16 * nb;
-      Bf[nb] = as_vec8<V8>(*(const uint4*)(st + kStageA + 64 + col * 64 + ((g ^ ((col >> 2) & 3)) << 4)));
+      Bf[nb] = as_vec8<V8>(*(const uint4*)(st + kStageA + col * 64 + ((g ^ ((col >> 2) & 3)) << 4)));
     }
     uint4 av[2][4];
     auto rd = [&](int h, uint4 (&dst)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int mb = 4 * h + j;
-        const int ro = (qok && ((sel >> mb) & 1)) ? (mb * 16 + n) * 64 : kZeroA;
-        dst[j] = *(const uint4*)(st + ro + po);
+        dst[j] = *(const uint4*)(st + (mb * 16 + n) * 64 + po);
       }
     };
     rd(0, av[0]);
@@ -274,6 +279,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     else wait_vm<K>();
   };
   auto stage_buf = [&](int ks) -> unsigned char* { return ks == 0 ? st0 : ks == 1 ? st1 : ks == 2 ? st2 : st3; };
+  const uint32_t L0 = lds_addr(st0), L1 = lds_addr(st1), L2 = lds_addr(st2), L3 = lds_addr(st3);
+  auto stage_lds = [&](int ks) -> uint32_t { return ks == 0 ? L0 : ks == 1 ? L1 : ks == 2 ? L2 : L3; };
 
   // ---- prologue ------------------------------------------------------------
   for (int b = 0; b < 3; ++b) reset(b);
@@ -287,16 +294,12 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       for (int j = tid; j < cnt; j += kThreads) add_entry(x, a.svals[s0 + j], a.er[s0 + j]);
     }
   }
-  if (tid < 4) *(uint4*)(st0 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
-  if (tid < 4) *(uint4*)(st1 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
-  if (tid < 4) *(uint4*)(st2 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
-  if (tid < 4) *(uint4*)(st3 + kZeroA + tid * 16) = make_uint4(0, 0, 0, 0);
   __syncthreads();
   {
     const int64_t tl = v_token(vlo);
-    issue_stage(0, tl, 0, st0);
-    if (nks > 1) issue_stage(0, tl, 1, st1);
-    if (nks > 2) issue_stage(0, tl, 2, st2);
+    issue_stage(0, tl, 0, L0);
+    if (nks > 1) issue_stage(0, tl, 1, L1);
+    if (nks > 2) issue_stage(0, tl, 2, L2);
   }
 
   // ---- one visit per iteration, four stages ---------------------------------
@@ -316,14 +319,13 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     // stage 0
     wait_stage(s);
     bar();
-    unsigned sel = selmask(u, 0);
     const int R = sh.rounds[u];
     reset(u2);
     if (v + 2 < vhi) issue_entries(v + 2);
-    if (nks > 3) issue_stage(u, tl, 3, st3);
+    if (nks > 3) issue_stage(u, tl, 3, L3);
     for (int r = 0; r < R; ++r) {
-      if (r) sel = selmask(u, r);
-      compute(st0, sel, 0);
+      if (r) drop_rows(st0, u, r);
+      compute(st0);
     }
     // stages 1 .. 3: each issues the copy of the next visit's stage ks - 1
 #pragma unroll
@@ -334,11 +336,11 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
         // map of visit v + 2: its pairs were copied during stage 0, before
         // the copies waited for above
         if (ks == 3 && v + 2 < vhi) build(u2, v + 2);
-        if (more) issue_stage(u1, tl1, ks - 1, stage_buf(ks - 1));
+        if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
         if (ks < nks) {
           for (int r = 0; r < R; ++r) {
-            if (r) sel = selmask(u, r);
-            compute(stage_buf(ks), sel, ks);
+            if (r) drop_rows(stage_buf(ks), u, r);
+            compute(stage_buf(ks));
           }
         }
       }

@@ -215,6 +215,40 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) store_one(j);
   };
+  // Four waves (128 heads, whole rows): P and dS of a tile are staged in LDS
+  // as (tensor, position) rows of 256 bytes and leave as 1 KB coalesced
+  // stores of 4 rows.  Chunk j of row r sits at chunk j ^ (r & 15), and the
+  // two 8-byte halves of a chunk are swapped in rows 16..31, so that the
+  // 8-byte writes of 32 lanes (32 rows, one head group) hit distinct banks.
+  constexpr bool kStage = NW == 4;
+  __shared__ __attribute__((aligned(16))) unsigned char stg[kStage ? 2 * kTile * 256 : 16];
+  uint4 pst[4];          // staged rows read back by this wave: tensor wave / 2, rows 16 (wave & 1) + 4 i + lane / 16
+  int stg_c0 = -1;       // first position of the staged tile, -1 if none
+  const int srow0 = 16 * (wave & 1) + (lane >> 4), sj = lane & 15;
+  auto stage_read = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = srow0 + 4 * i;
+      uint4 v = *(const uint4*)(stg + ((wave >> 1) * kTile + r) * 256 + ((sj ^ (r & 15)) << 4));
+      pst[i] = (wave & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
+    }
+  };
+  auto stage_store = [&](int i) {
+    const int pos = stg_c0 + srow0 + 4 * i;
+    if (stg_c0 >= 0 && pos < nv) {
+      uint16_t* out = (wave >> 1) ? a.ds_out : a.p_out;
+      *(uint4*)(out + (tl * a.E + pos) * a.Gp + sj * 8) = pst[i];
+    }
+  };
+  auto stage_write = [&]() {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int j = 4 * wave + q4;
+      const int o = m * 256 + ((j ^ (m & 15)) << 4) + ((kg ^ (m >> 4)) << 3);
+      *(uint2*)(stg + o) = pend_p[q4];
+      *(uint2*)(stg + kTile * 256 + o) = pend_ds[q4];
+    }
+  };
   // The gather of a tile as a fixed list of copy instructions per wave: K
   // and V rows wave + nw*j (two each), then rope groups wave + nw*j (8 rows
   // each); entries past the tile's rows (nw = 3) are skipped.
@@ -245,6 +279,7 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (kStage && stg_c0 >= 0) stage_read();
     const bool more = c0 + kTile < nv;
     const uint32_t nxt_l = lds_off(nxt);
     // With fewer than four waves (more copies per wave) the copies go out
@@ -274,7 +309,11 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
       if (kSpread && more && ks < 24)
         #pragma unroll
         for (int i = ks * kOps / 24; i < (ks + 1) * kOps / 24; ++i) issue_op(i, keys, nxt_l);
-      if (ks >= 24) store_one(ks - 24);
+      if (kStage) {
+        if (ks >= 24 && ks < 28) stage_store(ks - 24);
+      } else if (ks >= 24) {
+        store_one(ks - 24);
+      }
       S = mfma32<TT>(Qf[ks], as_vec8<V8>(kv[ks % 3]), S);
       P = mfma32<TT>(dOf[ks], as_vec8<V8>(vv[ks % 3]), P);
       __builtin_amdgcn_sched_barrier(0);
@@ -306,7 +345,13 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
       pend_p[q4] = make_uint2(pack2<TT>(pv[0], pv[1]), pack2<TT>(pv[2], pv[3]));
       pend_ds[q4] = make_uint2(pack2<TT>(dv[0], dv[1]), pack2<TT>(dv[2], dv[3]));
     }
-    pend_pos = c0 + m;
+    if (kStage) {
+      bar();   // every wave has read the previous staged tile back
+      stage_write();
+      stg_c0 = c0;
+    } else {
+      pend_pos = c0 + m;
+    }
   };
 
   if (nv > 0) issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
@@ -315,7 +360,16 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     tile(c0, buf0, buf1);
     if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
   }
-  store_pending();
+  if (kStage) {
+    __syncthreads();
+    if (stg_c0 >= 0) {
+      stage_read();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stage_store(i);
+    }
+  } else {
+    store_pending();
+  }
 }
 
 // ---------------------------------------------------------------------------

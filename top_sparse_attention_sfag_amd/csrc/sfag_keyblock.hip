@@ -194,10 +194,65 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // chunks past the heads) take an offset outside the resource: they fetch
   // nothing, and their slots are never read.  B: the block's columns x 4
   // chunks likewise, NB per wave.
+  // The copies of one stage, prepared once (slot-map entries read, buffer
+  // resources made) and then issued one A and one B instruction at a time
+  // between the MFMAs of the stage being computed: a burst of copies at the
+  // top of a stage stalls the issuing wave until the address unit takes them.
+  struct StageCopy {
+    __amdgpu_buffer_rsrc_t ars, brs;
+    int32_t pr[4];
+    int32_t p0;
+    int ks;
+    uint32_t st;
+    bool on;
+  };
+  auto prep_stage = [&](StageCopy& sc, bool on, int b, int64_t tl, int ks, uint32_t st) {
+    sc.on = on;
+    if (!on) return;
+    // A rows of token tl: pairs tl*E .. tl*E + E - 1; B: the block's
+    // columns of the token's transposed copy
+    sc.ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
+    sc.brs = make_rsrc(Bsrc + (tl * Bcols + c.tcol0) * Gp, (int)(NB * 64 * Gp * 2));
+    sc.p0 = (int32_t)(tl * a.E);
+    sc.ks = ks;
+    sc.st = st;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sc.pr[k] = sh.prim[b][16 * (wave + 4 * k) + (lane >> 2)];
+  };
+  auto issue_a = [&](const StageCopy& sc, int k) {
+    const int i = wave + 4 * k;
+    const int row = 16 * i + (lane >> 2);
+    const int q = (lane & 3) ^ ((row >> 2) & 3);
+    const int hq = 32 * sc.ks + 8 * q;
+    const uint32_t off = (sc.pr[k] >= 0 && hq < Gp) ? (uint32_t)(((sc.pr[k] - sc.p0) * Gp + hq) * 2) : kOutside;
+    bdma16(sc.ars, off, sc.st + i * 1024);
+  };
+  auto issue_b = [&](const StageCopy& sc, int k) {
+    const int i = wave + 4 * k;
+    const int col = 16 * i + (lane >> 2);
+    const int q = (lane & 3) ^ ((col >> 2) & 3);
+    const int hq = 32 * sc.ks + 8 * q;
+    const uint32_t off = hq < Gp ? (uint32_t)((col * Gp + hq) * 2) : kOutside;
+    bdma16(sc.brs, off, sc.st + kStageA + i * 1024);
+  };
+  auto issue_part = [&](const StageCopy& sc, int k) {
+    if (!sc.on) return;
+    issue_a(sc, k);
+    if (k < NB) issue_b(sc, k);
+  };
+  auto issue_all = [&](StageCopy& sc) {
+    if (sc.on) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) issue_a(sc, k);
+#pragma unroll
+      for (int k = 0; k < NB; ++k) issue_b(sc, k);
+    }
+    sc.on = false;
+  };
+  // All copies of a stage at once, at the top of the stage: the generic path
+  // (Gp != 128) waits for every copy at each stage, so spreading its copies
+  // over the MFMAs would leave the last ones no time before that wait.
   auto issue_stage = [&](int b, int64_t tl, int ks, uint32_t st) {
-    // A rows of token tl: pairs tl*E .. tl*E + E - 1, one buffer resource.
-    // The slot map entries are read before the first copy is issued (a copy
-    // is a memory clobber: reads after it would wait one by one).
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
     const int32_t p0 = (int32_t)(tl * a.E);
     int32_t pr[4];
@@ -212,7 +267,6 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       const uint32_t off = (pr[k] >= 0 && hq < Gp) ? (uint32_t)(((pr[k] - p0) * Gp + hq) * 2) : kOutside;
       bdma16(ars, off, st + i * 1024);
     }
-    // B columns of token tl, one buffer resource over the block's columns
     const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bsrc + (tl * Bcols + c.tcol0) * Gp, (int)(NB * 64 * Gp * 2));
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -241,7 +295,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // Rows the token does not select, and head chunks past Gp, hold zeros in
   // the stage (their copies fetch nothing and land zeros), so every row is
   // read as it is.
-  auto compute = [&](const unsigned char* st) {
+  auto compute = [&](const unsigned char* st, const StageCopy& sc) {
     const int po = (g ^ (n >> 2)) << 4;          // rows mb*16 + n: (r >> 2) & 3 = n >> 2
     V8 Bf[NB];
 #pragma unroll
@@ -261,6 +315,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       if (h + 1 < 4) rd(h + 1, av[(h + 1) & 1]);
+      if (GP != 0) issue_part(sc, h);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -297,9 +352,13 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   __syncthreads();
   {
     const int64_t tl = v_token(vlo);
-    issue_stage(0, tl, 0, L0);
-    if (nks > 1) issue_stage(0, tl, 1, L1);
-    if (nks > 2) issue_stage(0, tl, 2, L2);
+    StageCopy sc;
+    prep_stage(sc, true, 0, tl, 0, L0);
+    issue_all(sc);
+    prep_stage(sc, nks > 1, 0, tl, 1, L1);
+    issue_all(sc);
+    prep_stage(sc, nks > 2, 0, tl, 2, L2);
+    issue_all(sc);
   }
 
   // ---- one visit per iteration, four stages ---------------------------------
@@ -322,10 +381,17 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     const int R = sh.rounds[u];
     reset(u2);
     if (v + 2 < vhi) issue_entries(v + 2);
-    if (nks > 3) issue_stage(u, tl, 3, L3);
+    StageCopy sc;
+    if (GP == 0) {
+      sc.on = false;
+      if (nks > 3) issue_stage(u, tl, 3, L3);
+    } else {
+      prep_stage(sc, nks > 3, u, tl, 3, L3);
+    }
     for (int r = 0; r < R; ++r) {
       if (r) drop_rows(st0, u, r);
-      compute(st0);
+      compute(st0, sc);
+      sc.on = false;   // the copies go out during the first round
     }
     // stages 1 .. 3: each issues the copy of the next visit's stage ks - 1
 #pragma unroll
@@ -336,11 +402,16 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
         // map of visit v + 2: its pairs were copied during stage 0, before
         // the copies waited for above
         if (ks == 3 && v + 2 < vhi) build(u2, v + 2);
-        if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
+        if (GP == 0) {
+          if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
+        } else {
+          prep_stage(sc, more, u1, tl1, ks - 1, stage_lds(ks - 1));
+        }
         if (ks < nks) {
           for (int r = 0; r < R; ++r) {
             if (r) drop_rows(stage_buf(ks), u, r);
-            compute(stage_buf(ks));
+            compute(stage_buf(ks), sc);
+            sc.on = false;
           }
         }
       }

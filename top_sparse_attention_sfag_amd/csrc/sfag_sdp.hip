@@ -304,11 +304,13 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
       if (ks + 2 < 32) rd(ks + 2, (ks + 2) % 3);
-      // the next tile's copies over the first 24 k-steps and the previous
-      // tile's stores over the last 8, between the MFMAs
-      if (kSpread && more && ks < 24)
+      // the next tile's copies over the first 8 k-steps (two or three per
+      // k-step: early enough to land before the next tile, spread enough not
+      // to stall the wave) and the previous tile's stores over the last 8,
+      // between the MFMAs
+      if (kSpread && more && ks < 8)
         #pragma unroll
-        for (int i = ks * kOps / 24; i < (ks + 1) * kOps / 24; ++i) issue_op(i, keys, nxt_l);
+        for (int i = ks * kOps / 8; i < (ks + 1) * kOps / 8; ++i) issue_op(i, keys, nxt_l);
       if (kStage) {
         if (ks >= 24 && ks < 28) stage_store(ks - 24);
       } else if (ks >= 24) {

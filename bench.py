@@ -45,12 +45,13 @@ def _count_valid(case, inp, sfag):
     return n, nv
 
 
-def _alg_bytes(case, n_pairs):
-    """No-reuse algorithmic bytes of one backward call."""
+def _alg_bytes(case, n_pairs, value_is_key=False):
+    """No-reuse algorithmic bytes of one backward call (with value passed as
+    the key tensor, the V row of a pair is the K row already gathered)."""
     e = 2
     G, D, Dr, T1, T2 = case.G, case.D, case.Dr, case.T1, case.T2
     per_token = G * (D + Dr) * e * 2 + G * D * e * 2 + G * 4 * 2 + G * 4 * 2 + case.Kent * 4
-    per_pair = (2 * D + Dr) * e + (2 * D + Dr) * 4
+    per_pair = ((D + Dr) if value_is_key else (2 * D + Dr)) * e + (2 * D + Dr) * 4
     per_key = (2 * D + Dr) * 4 * 2 + (2 * D + Dr) * e
     return T1 * per_token + n_pairs * per_pair + T2 * per_key
 
@@ -264,6 +265,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
     ap.add_argument("--deterministic", choices=("config", "true", "false"), default="config")
+    ap.add_argument("--value-is-key", action="store_true",
+                    help="pass the key tensor as value too (the operator page's supported case)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -290,6 +293,8 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     print(f"[bench] generating {case.name} on {dev}", file=sys.stderr, flush=True)
     inp = si.make_inputs(case, seed, device=dev)
+    if args.value_is_key:
+        inp["value"] = inp["key"]
     inp.update(si.standin_stats(case, inp, seed, device=dev))
     torch.cuda.synchronize()
     n_pairs, _ = _count_valid(case, inp, sfag)
@@ -340,7 +345,7 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     tflops = flops / (ms * 1e-3) / 1e12
-    alg_bytes = _alg_bytes(case, n_pairs)
+    alg_bytes = _alg_bytes(case, n_pairs, args.value_is_key)
     # Dominant kernel and its algorithmic work per launch.
     dom = max(prof, key=lambda k: prof[k][0])
     dom_ms = prof[dom][0] / prof[dom][1]
@@ -365,7 +370,8 @@ def main(argv=None):
         "data": "synthetic (seeded generator; stand-in softmax statistics)",
         "config": {"workload": case.name, "layout": case.layout, "B": case.B, "T1": case.T1, "T2": case.T2,
                    "N1": case.G, "D": case.D, "Dr": case.Dr, "K": case.K, "sparse_block": case.block,
-                   "sparse_mode": case.mode, "deterministic": det, "valid_pairs": n_pairs},
+                   "sparse_mode": case.mode, "deterministic": det, "valid_pairs": n_pairs,
+                   "value_is_key": bool(args.value_is_key)},
         "mfma_frac": tflops / MFMA_PEAK_TFLOPS,
         "alg_GBs": alg_bytes / (ms * 1e-3) / 1e9,
         "hbm_frac_alg": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

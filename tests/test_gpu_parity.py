@@ -91,6 +91,33 @@ def test_small_against_oracle(case):
     _run(case, seed=7)
 
 
+# Value passed as the key tensor itself (the operator page supports only
+# value identical to key): the library gathers each row once and reads it for
+# both S and dP.  dK and dV stay separate outputs.
+VALUE_IS_KEY = [
+    si.Case("vk_g128_rope", S1=6, S2=300, G=128, K=100),
+    si.Case("vk_g64_causal", S1=70, S2=70, G=64, K=40, mode=3, index_rule="causal_mix"),
+    si.Case("vk_g96_norope_fp16", S1=5, S2=150, G=96, Dr=0, K=77, dtype="fp16"),
+    si.Case("vk_g16_blocks", S1=6, S2=512, G=16, Dr=0, K=9, block=16, dtype="fp16", std=0.5,
+            index_rule="blocks", scale=1 / 512 ** 0.5),
+    si.Case("vk_g4_rope", S1=8, S2=256, G=4, K=100),
+]
+
+
+@pytest.mark.parametrize("case", VALUE_IS_KEY, ids=[c.name for c in VALUE_IS_KEY])
+def test_value_is_key(case):
+    inp = si.make_inputs(case, 11)
+    inp["value"] = inp["key"]
+    inp = add_oracle_stats(case, inp)
+    ref = oracle_backward(case, inp)
+    dev = to_device(inp)
+    dev["value"] = dev["key"]          # one device tensor passed twice
+    print(f"case {case.name} value is key", flush=True)
+    outs = call_backward(case, dev)
+    torch.cuda.synchronize()
+    _check(case, _outs_np(case, outs), ref, label=case.name)
+
+
 def test_duplicated_indices():
     case = si.Case("dup", S1=4, S2=64, G=16, K=40)
     inp = si.make_inputs(case, 3)

@@ -40,7 +40,9 @@ __device__ __forceinline__ void lds_load16(const void* g, void* l) {
 
 }  // namespace
 
-template <typename TT, int DR>
+// VK: value is the key tensor itself; the first 512 columns of each gathered
+// K row serve as its V row (one gather per position).
+template <typename TT, int DR, bool VK>
 __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int KS_QK = DQK / 32;
@@ -48,7 +50,7 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
   constexpr int NB_Q = DQK / 16;
   constexpr int KM_BYTES = kTile * 1024;        // K main part of a tile
   constexpr int KR_BYTES = kTile * DR * 2;      // K rope part
-  constexpr int V_BYTES = kTile * 1024;
+  constexpr int V_BYTES = VK ? 0 : kTile * 1024;
   constexpr int BUF = KM_BYTES + KR_BYTES + V_BYTES;
   constexpr int STAGE = kTile * 64 * 2;         // one 32 x 64 16-bit staging tile
   typedef typename TT::vec8 V8;
@@ -118,7 +120,7 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
       const int64_t key = __builtin_amdgcn_readfirstlane(__shfl(key_l, j * 8, 64));
       const int gc = lane ^ (r & 7);
       lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
-      lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+      if (!VK) lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
     }
     if (DR > 0) {
       const int pc = lane & 7;
@@ -152,7 +154,7 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
     if (c0 + kTile < nv) issue_tile(c0 + kTile, cur ^ 1);
     const unsigned char* Km = smem + cur * BUF;
     const unsigned char* Kr = Km + KM_BYTES;
-    const unsigned char* Vm = Km + KM_BYTES + KR_BYTES;
+    const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
     if (wave_on) {
       f32x4 s[2], dp[2];
 #pragma unroll
@@ -246,12 +248,24 @@ void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s) {
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a.ntok + per - 1) / per * per;
   const dim3 grid((unsigned)(padded * a.n_hb)), block(256);
+  // value passed as the key tensor itself: gather each row once
+  const bool vk = a.v == a.k;
   if (dtype == SFAG_BF16) {
-    if (rope) hipLaunchKernelGGL((k_row<BF16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_row<BF16, 0>), grid, block, 0, s, a);
+    if (rope) {
+      if (vk) hipLaunchKernelGGL((k_row<BF16, 64, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_row<BF16, 64, false>), grid, block, 0, s, a);
+    } else {
+      if (vk) hipLaunchKernelGGL((k_row<BF16, 0, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_row<BF16, 0, false>), grid, block, 0, s, a);
+    }
   } else {
-    if (rope) hipLaunchKernelGGL((k_row<FP16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_row<FP16, 0>), grid, block, 0, s, a);
+    if (rope) {
+      if (vk) hipLaunchKernelGGL((k_row<FP16, 64, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_row<FP16, 64, false>), grid, block, 0, s, a);
+    } else {
+      if (vk) hipLaunchKernelGGL((k_row<FP16, 0, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_row<FP16, 0, false>), grid, block, 0, s, a);
+    }
   }
 }
 

@@ -127,14 +127,17 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)TT::from_f(lo) | ((uint32_t)TT::from_f(hi) << 16);
 }
 
-template <typename TT, int DR, int NW>
+// VK: value is the key tensor itself (the operator page's supported case):
+// one K|Krope row per position is gathered and its first 512 columns serve as
+// the V row, read once for both the S and the dP chains.
+template <typename TT, int DR, int NW, bool VK>
 __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int KS_QK = DQK / 16;   // k-steps of 16 along D+Dr
   constexpr int KS_V = 512 / 16;
   constexpr int KM_BYTES = kTile * 1024;
   constexpr int KR_BYTES = kTile * DR * 2;
-  constexpr int BUF = KM_BYTES + KR_BYTES + kTile * 1024;
+  constexpr int BUF = KM_BYTES + KR_BYTES + (VK ? 0 : kTile * 1024);
   typedef typename TT::vec8 V8;
 
   // Two tile buffers as separate LDS objects.
@@ -252,15 +255,16 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   // The gather of a tile as a fixed list of copy instructions per wave: K
   // and V rows wave + nw*j (two each), then rope groups wave + nw*j (8 rows
   // each); entries past the tile's rows (nw = 3) are skipped.
-  constexpr int kRowOps = 2 * ((kTile + nw - 1) / nw);
+  constexpr int kPerRow = VK ? 1 : 2;   // copies per K(|V) row
+  constexpr int kRowOps = kPerRow * ((kTile + nw - 1) / nw);
   constexpr int kOps = kRowOps + (DR > 0 ? (kTile / 8 + nw - 1) / nw : 0);
   auto issue_op = [&](int i, int32_t keyv, uint32_t base) {
     if (i < kRowOps) {
-      const int r = wave + nw * (i >> 1);
+      const int r = wave + nw * (i / kPerRow);
       if (r < kTile) {
         const int64_t key = __builtin_amdgcn_readlane(keyv, r);
         const int gc = lane ^ (r & 15);
-        if (i & 1) lds_load16_at(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+        if (!VK && (i & 1)) lds_load16_at(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
         else lds_load16_at(a.k + key * 512 + gc * 8, base + r * 1024);
       }
     } else {
@@ -285,9 +289,9 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     // With fewer than four waves (more copies per wave) the copies go out
     // here at once; spreading them would cost registers.
     constexpr bool kSpread = NW == 4;
-    if (!kSpread && more) issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    if (!kSpread && more) issue_rows<DR, !VK, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
     const unsigned char* Kr = Km + KM_BYTES;
-    const unsigned char* Vm = Kr + KR_BYTES;
+    const unsigned char* Vm = VK ? Km : Kr + KR_BYTES;
     f32x16 S, P;
 #pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = P[i] = 0.f;
@@ -297,7 +301,7 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     auto rd = [&](int ks, int slot) {
       const int ch = 2 * ks + kg;
       kv[slot] = *(const uint4*)(Km + oK + ((ch ^ x) << 4));
-      vv[slot] = *(const uint4*)(Vm + oK + ((ch ^ x) << 4));
+      vv[slot] = VK ? kv[slot] : *(const uint4*)(Vm + oK + ((ch ^ x) << 4));
     };
     rd(0, 0);
     rd(1, 1);
@@ -356,7 +360,7 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     }
   };
 
-  if (nv > 0) issue_rows<DR, true, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
+  if (nv > 0) issue_rows<DR, !VK, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
   keys = tile_keys(rt, nv, kTile, lane);
   for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
     tile(c0, buf0, buf1);
@@ -526,14 +530,25 @@ void launch_sdp(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
   const int nw = (int)std::min<int64_t>(4, a.Gp / 32);
   a.n_hb = (int32_t)((a.Gp + 32 * nw - 1) / (32 * nw));
   const dim3 g1((unsigned)(padded * a.n_hb)), b1(64 * nw);
+  // value passed as the key tensor itself (same rows): gather each row once
+  const bool vk = a.v == a.k;
   auto go = [&](auto tt, auto dr) {
     typedef decltype(tt) T;
     constexpr int D = decltype(dr)::value;
-    switch (nw) {
-      case 1: hipLaunchKernelGGL((k_sdp<T, D, 1>), g1, b1, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((k_sdp<T, D, 2>), g1, b1, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((k_sdp<T, D, 3>), g1, b1, 0, s, a); break;
-      default: hipLaunchKernelGGL((k_sdp<T, D, 4>), g1, b1, 0, s, a); break;
+    if (vk) {
+      switch (nw) {
+        case 1: hipLaunchKernelGGL((k_sdp<T, D, 1, true>), g1, b1, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_sdp<T, D, 2, true>), g1, b1, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_sdp<T, D, 3, true>), g1, b1, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_sdp<T, D, 4, true>), g1, b1, 0, s, a); break;
+      }
+    } else {
+      switch (nw) {
+        case 1: hipLaunchKernelGGL((k_sdp<T, D, 1, false>), g1, b1, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_sdp<T, D, 2, false>), g1, b1, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_sdp<T, D, 3, false>), g1, b1, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_sdp<T, D, 4, false>), g1, b1, 0, s, a); break;
+      }
     }
   };
   if (dtype == SFAG_BF16) {

@@ -10,6 +10,7 @@ namespace sfag {
 
 struct RowArgs {
   const uint16_t *q, *qr, *dO, *k, *kr, *v;
+  const uint16_t* o;   // forward output (k_sdp computes Delta from it)
   const float *smax, *ssum, *delta;
   const int32_t *rows, *nvalid;
   uint16_t *ds_out, *p_out, *dq, *dqr;

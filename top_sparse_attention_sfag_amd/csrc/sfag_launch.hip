@@ -136,7 +136,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   int32_t* rows = at<int32_t>(workspace, w.rows);
   uint16_t* ds = at<uint16_t>(workspace, w.ds);
   uint16_t* pb = at<uint16_t>(workspace, w.p);
-  {
+  if (d.Gp < 32) {   // k_row reads Delta; k_sdp forms it from dO and O itself
     TimedScope ts("delta", s);
     launch_delta(plan->dtype, plan->dout, plan->out, delta, d.T1 * d.G, s);
   }
@@ -155,6 +155,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   ra.q = (const uint16_t*)plan->q;
   ra.qr = (const uint16_t*)plan->qr;
   ra.dO = (const uint16_t*)plan->dout;
+  ra.o = (const uint16_t*)plan->out;
   ra.k = (const uint16_t*)plan->k;
   ra.kr = (const uint16_t*)plan->kr;
   ra.v = (const uint16_t*)plan->v;

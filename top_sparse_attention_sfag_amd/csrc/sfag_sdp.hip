@@ -156,6 +156,26 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   const int h = h0 + hi;
   const bool hv = h < a.G;
 
+  // Delta = rowsum(dO ∘ O) of head h (功能说明 stage 2): this lane's 256
+  // columns (chunks 2ks + kg) against O, fp32, then the other half from lane
+  // ^ 32; lanes 0..31 then hold heads h0 .. h0 + 31.
+  // (dO is read again here, from L2, a few chunks at a time, so that O and
+  // dO are not all held in registers next to the operands)
+  float dsum = 0.f;
+  if (hv) {
+    const uint16_t* orow = a.o + (t * a.G + h) * 512 + 8 * kg;
+    const uint16_t* drow = a.dO + (t * a.G + h) * 512 + 8 * kg;
+#pragma unroll 2
+    for (int ks = 0; ks < KS_V; ++ks) {
+      const uint4 ov = *(const uint4*)(orow + 16 * ks);
+      const uint4 dv = *(const uint4*)(drow + 16 * ks);
+      const uint16_t* po = (const uint16_t*)&ov;
+      const uint16_t* pd = (const uint16_t*)&dv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsum = fmaf(TT::to_f(pd[j]), TT::to_f(po[j]), dsum);
+    }
+  }
+  dsum += __shfl_xor(dsum, 32);
   // A operands: Q and dO rows of head h, 8 consecutive columns per k-step.
   V8 Qf[KS_QK], dOf[KS_V];
 #pragma unroll
@@ -183,11 +203,12 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   for (int i = 0; i < 16; ++i) {
     const int hh = h0 + 8 * (i >> 2) + 4 * kg + (i & 3);
     mb[i] = __builtin_inff();
-    dl[i] = 0.f;
+    dl[i] = __shfl(dsum, hh - h0);
     if (hh < a.G) {
       const float m = a.smax[t * a.G + hh], l = a.ssum[t * a.G + hh];
       if (l > 0.f) mb[i] = m * kLog2e + __log2f(l);
-      dl[i] = a.delta[t * a.G + hh];
+    } else {
+      dl[i] = 0.f;
     }
   }
   const int nv = a.nvalid[tl];

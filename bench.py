@@ -61,7 +61,7 @@ def _alg_bytes(case, n_pairs, value_is_key=False):
 # dK over D+Dr and dV over D (keyblock, col).
 def _unit_flops(case, kernel):
     D, Dr = case.D, case.Dr
-    return {"sdp": 2 * (2 * D + Dr), "dq": 2 * (D + Dr), "row": 2 * (3 * D + 2 * Dr),
+    return {"sdp": 2 * (2 * D + Dr), "dq": 2 * (D + Dr), "row": 2 * (3 * D + 2 * Dr), "fwd": 2 * (2 * D + Dr),
             "keyblock": 2 * (2 * D + Dr), "col": 2 * (2 * D + Dr)}.get(kernel)
 
 
@@ -75,6 +75,10 @@ def _kernel_bytes(case, kernel, n_pairs):
         # gathered K|Krope|V row in and the 16-bit dS and P out.
         return (T1 * (G * (2 * (D + Dr) + D) * e + G * 12 + case.Kent * 4)
                 + n_pairs * ((2 * D + Dr) * e + 2 * G * e))
+    if kernel == "fwd":
+        # Q, Qrope, indices in; out and the two statistics out; per pair the
+        # gathered K|Krope|V row in.
+        return T1 * (G * (2 * D + Dr) * e + G * 8 + case.Kent * 4) + n_pairs * (2 * D + Dr) * e
     if kernel == "keyblock":
         # per pair dS and P in; per token Q|Qrope and dO in; per key the fp32
         # dK|dKrope|dV partial out.
@@ -129,6 +133,7 @@ _GROUPS = {
     "keyblock": (r"k_keyblock<", [_CSRC + "sfag_keyblock.hip"]),
     "transpose": (r"k_transpose", [_CSRC + "sfag_keyblock.hip"]),
     "col": (r"k_col<", [_CSRC + "sfag_mfma.hip"]),
+    "fwd": (r"k_fwd<", [_CSRC + "sfag_fwd.hip"]),
 }
 
 
@@ -215,10 +220,11 @@ def _summarize_profiles(d, config, calib_mb):
     return 0
 
 
-def _cpu_baseline(case, inp, seed, target_s=15.0):
+def _cpu_baseline(case, inp, seed, target_s=15.0, forward=False):
     """The oracle as it stands, on one host thread, over a seeded sample of
     tokens: each sampled token's full backward (its dQ row and its dK/dV
-    scatter).  Batches double in size until about ``target_s`` seconds."""
+    scatter), or its forward with ``forward``.  Batches double in size until
+    about ``target_s`` seconds."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -247,15 +253,20 @@ def _cpu_baseline(case, inp, seed, target_s=15.0):
             g = {n: (a[sel] if isinstance(a, np.ndarray) else a) for n, a in geom.items()}
             g["T1"] = len(sel)
             t0 = time.perf_counter()
-            orc.backward(sub["q"], k, v, sub["qr"], kr, sub["idx"], sub["dO"], sub["O"], sub["m"], sub["l"], g,
-                         case.block, case.mode, case.scale_value)
+            if forward:
+                orc.forward(sub["q"], k, v, sub["qr"], kr, sub["idx"], g, case.block, case.mode, case.scale_value)
+            else:
+                orc.backward(sub["q"], k, v, sub["qr"], kr, sub["idx"], sub["dO"], sub["O"], sub["m"], sub["l"], g,
+                             case.block, case.mode, case.scale_value)
             used += time.perf_counter() - t0
-            flops += orc.flops(orc.decode(sub["idx"], case.block, case.mode, g), G, D, Dr)
+            rows = orc.decode(sub["idx"], case.block, case.mode, g)
+            flops += (int((rows >= 0).sum()) * G * 2 * (2 * D + Dr) if forward else orc.flops(rows, G, D, Dr))
             done += len(sel)
             batch *= 2
     return dict(value=flops / used / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
-                sample=f"{done} seeded tokens of the same workload, each token's full backward (dQ row and dK/dV "
-                       f"scatter), float64 NumPy on one thread, {used:.1f} s")
+                sample=(f"{done} seeded tokens of the same workload, each token's full "
+                        + ("forward" if forward else "backward (dQ row and dK/dV scatter)")
+                        + f", float64 NumPy on one thread, {used:.1f} s"))
 
 
 def main(argv=None):
@@ -265,6 +276,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
     ap.add_argument("--deterministic", choices=("config", "true", "false"), default="config")
+    ap.add_argument("--pass", dest="which", choices=("backward", "forward"), default="backward",
+                    help="time the backward pass (the headline) or the forward pass that feeds it")
     ap.add_argument("--value-is-key", action="store_true",
                     help="pass the key tensor as value too (the operator page's supported case)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -316,6 +329,20 @@ def main(argv=None):
     def step():
         sfag.backward(*args_pos, outputs=outs, workspace=ws, stream=stream, **kw)
 
+    if args.which == "forward":
+        # out / softmaxMax / softmaxSum written into the input tensors' copies
+        fouts = (torch.empty_like(inp["out"]), torch.empty_like(inp["softmax_max"]),
+                 torch.empty_like(inp["softmax_sum"]))
+        fws = torch.empty(case.T1 * (case.Kent * case.block + 1) * 4 + 4096, dtype=torch.uint8, device=dev)
+        fkw = dict(seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"),
+                   query_rope=inp.get("query_rope"), key_rope=inp.get("key_rope"), scale=case.scale_value,
+                   block_size=case.block, layout=case.layout, sparse_mode=case.mode)
+        flops = n_pairs * case.G * 2 * (2 * case.D + case.Dr)
+
+        def step():  # noqa: F811
+            sfag.forward(inp["query"], inp["key"], inp["value"], inp["sparse_indices"], outputs=fouts,
+                         workspace=fws, stream=stream, **fkw)
+
     if args.calib_copy_mb:
         # one elementwise kernel that reads and writes calib_copy_mb MiB each
         src = torch.ones((args.calib_copy_mb << 20) // 4, dtype=torch.int32, device=dev)
@@ -345,7 +372,8 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     tflops = flops / (ms * 1e-3) / 1e12
-    alg_bytes = _alg_bytes(case, n_pairs, args.value_is_key)
+    alg_bytes = (_alg_bytes(case, n_pairs, args.value_is_key) if args.which == "backward"
+                 else _kernel_bytes(case, "fwd", n_pairs))
     # Dominant kernel and its algorithmic work per launch.
     dom = max(prof, key=lambda k: prof[k][0])
     dom_ms = prof[dom][0] / prof[dom][1]
@@ -356,7 +384,8 @@ def main(argv=None):
     roof["kernel_ms"] = dom_ms
 
     line = {
-        "metric": "sparse-attn bwd TFLOP/s + % bf16 MFMA peak (G=128) / % HBM peak (G<=16), 1 GPU",
+        "metric": ("sparse-attn bwd TFLOP/s + % bf16 MFMA peak (G=128) / % HBM peak (G<=16), 1 GPU"
+                   if args.which == "backward" else "sparse-attn fwd TFLOP/s (forward pass), 1 GPU"),
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -380,7 +409,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = _cpu_baseline(case, inp, seed, args.cpu_seconds)
+        line["cpu_baseline"] = _cpu_baseline(case, inp, seed, args.cpu_seconds, forward=args.which == "forward")
     print(json.dumps(line), flush=True)
     return 0
 

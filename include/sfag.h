@@ -115,6 +115,31 @@ int sfag_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const 
  */
 int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
 
+/*
+ * Forward pass of the same attention (the producer of the backward's out,
+ * softmaxMax and softmaxSum inputs, whose meaning the operator page's
+ * parameter table gives): for each query token t and head h, over the valid
+ * positions p of t (the decode and mask rules above),
+ *   z = scale·(Q[t,h]·K[p] + Qrope[t,h]·Krope[p]),
+ *   softmaxMax[t,h] = max_p z,  softmaxSum[t,h] = Σ_p exp(z − softmaxMax),
+ *   out[t,h] = Σ_p exp(z − softmaxMax)/softmaxSum · V[p]
+ * (fp32 accumulation; out rounded to the input dtype).  A token with no valid
+ * position gets softmaxMax = −inf, softmaxSum = 0 and out = 0.
+ * Inputs as for sfag_workspace_size; out has query's shape and dtype,
+ * softmaxMax/softmaxSum the statistics' shapes, float32.  All three are
+ * written in full by sfag_forward.  The two-phase protocol, the plan's
+ * ownership and the error behaviour are those of the backward call; a plan
+ * from one call cannot be executed by the other (SFAG_ERR_PARAM_INVALID).
+ */
+int sfag_forward_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const sfag_tensor* value,
+                                const sfag_tensor* sparseIndices, const sfag_tensor* actualSeqLengthsQueryOptional,
+                                const sfag_tensor* actualSeqLengthsKvOptional, const sfag_tensor* queryRopeOptional,
+                                const sfag_tensor* keyRopeOptional, double scaleValue, int64_t sparseBlockSize,
+                                const char* layoutOptional, int64_t sparseMode, const sfag_tensor* out,
+                                const sfag_tensor* softmaxMax, const sfag_tensor* softmaxSum,
+                                uint64_t* workspaceSize, sfag_plan** plan);
+int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
+
 /* Frees a plan that will not be executed.  NULL is accepted. */
 void sfag_plan_destroy(sfag_plan* plan);
 

@@ -143,3 +143,45 @@ def test_backward_rejects_small_workspace_before_launch():
 
 def test_null_plan():
     assert sfag.lib().sfag_backward(None, ctypes.c_uint64(0), None, None) == 161001
+
+
+def _fwd_plan(t, drop=None):
+    """Phase 1 of the forward call through the C ABI; returns (rc, ws, plan)."""
+    from top_sparse_attention_sfag_amd._binding import _desc
+    t = dict(t)
+    if drop:
+        t[drop] = None
+    ws = ctypes.c_uint64(0)
+    p = ctypes.c_void_p(None)
+    rc = sfag.lib().sfag_forward_workspace_size(
+        _desc(t["query"]), _desc(t["key"]), _desc(t["value"]), _desc(t["sparse_indices"]), _desc(t["seqlens_q"]),
+        _desc(t["seqlens_kv"]), _desc(t["query_rope"]), _desc(t["key_rope"]), 0.04, 1, t["layout"].encode(), 0,
+        _desc(t["out"]), _desc(t["softmax_max"]), _desc(t["softmax_sum"]), ctypes.byref(ws), ctypes.byref(p))
+    return rc, int(ws.value), p
+
+
+def test_forward_plans():
+    for layout in ("BSND", "TND"):
+        for Dr in (0, 64):
+            rc, ws, p = _fwd_plan(_tensors(layout, Dr=Dr))
+            assert rc == 0 and ws > 0
+            sfag.destroy(p)
+    rc, ws, p = _fwd_plan(_tensors(S1=0))
+    assert rc == 0 and ws == 0
+    sfag.destroy(p)
+    for missing, code in (("out", 161001), ("softmax_sum", 161001), ("query", 161001), ("key_rope", 161002)):
+        rc, _, p = _fwd_plan(_tensors(), drop=missing)
+        assert rc == code, (missing, rc)
+        assert not p.value
+
+
+def test_plans_are_not_interchangeable():
+    # a forward plan given to the backward call and the other way round: both
+    # fail before anything is enqueued, and consume the plan
+    rc, ws, p = _fwd_plan(_tensors())
+    assert rc == 0
+    assert sfag.lib().sfag_backward(None, ctypes.c_uint64(ws), p, None) == 161002
+    assert b"forward" in sfag.lib().sfag_last_error()
+    ws, p = _plan(_tensors())
+    assert sfag.lib().sfag_forward(None, ctypes.c_uint64(ws), p, None) == 161002
+    assert b"backward" in sfag.lib().sfag_last_error()

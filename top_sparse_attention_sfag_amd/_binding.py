@@ -61,6 +61,12 @@ def lib():
             ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p)]
         L.sfag_backward.restype = ctypes.c_int
         L.sfag_backward.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        L.sfag_forward_workspace_size.restype = ctypes.c_int
+        L.sfag_forward_workspace_size.argtypes = [T] * 8 + [ctypes.c_double, ctypes.c_int64, ctypes.c_char_p,
+                                                           ctypes.c_int64] + [T] * 3 + [
+            ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p)]
+        L.sfag_forward.restype = ctypes.c_int
+        L.sfag_forward.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
         L.sfag_plan_destroy.restype = None
         L.sfag_plan_destroy.argtypes = [ctypes.c_void_p]
         L.sfag_last_error.restype = ctypes.c_char_p
@@ -82,7 +88,7 @@ def lib():
 
 
 KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "sdp", "dq", "col", "csr", "key_reduce", "transpose", "kb_sort",
-                 "keyblock", "kb_reduce", "cast")
+                 "keyblock", "kb_reduce", "cast", "fwd")
 
 
 def profile_enable(on: bool = True):
@@ -185,6 +191,41 @@ def backward(query, key, value, sparse_indices, dout, out, softmax_max, softmax_
     if rc != OK:
         _raise(rc)
     return dq, dk, dv, dqr, dkr
+
+
+def forward(query, key, value, sparse_indices, *, seqlens_q=None, seqlens_kv=None, query_rope=None, key_rope=None,
+            scale=None, block_size=1, layout="BSND", sparse_mode=0, outputs=None, workspace=None, stream=None):
+    """Forward pass on the GPU: returns (out, softmax_max, softmax_sum), the
+    inputs the backward pass takes from the forward.  ``outputs`` may supply
+    preallocated tensors of those shapes."""
+    if not query.is_cuda:
+        raise SfagValueError(ERR_PARAM_INVALID, "tensors must be on the GPU")
+    if scale is None:
+        scale = 1.0 / (query.shape[-1] + (query_rope.shape[-1] if query_rope is not None else 0)) ** 0.5
+    if outputs is None:
+        G = query.shape[-2]
+        stats = (1, query.shape[0], G) if layout == "TND" else (query.shape[0], 1, query.shape[1], G)
+        out = torch.empty_like(query)
+        smax = torch.empty(stats, dtype=torch.float32, device=query.device)
+        ssum = torch.empty(stats, dtype=torch.float32, device=query.device)
+    else:
+        out, smax, ssum = outputs
+    ws = ctypes.c_uint64(0)
+    p = ctypes.c_void_p(None)
+    rc = lib().sfag_forward_workspace_size(
+        _desc(query), _desc(key), _desc(value), _desc(sparse_indices), _desc(seqlens_q), _desc(seqlens_kv),
+        _desc(query_rope), _desc(key_rope), float(scale), int(block_size), None if layout is None else layout.encode(),
+        int(sparse_mode), _desc(out), _desc(smax), _desc(ssum), ctypes.byref(ws), ctypes.byref(p))
+    if rc != OK:
+        _raise(rc)
+    ws = int(ws.value)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
+    rc = lib().sfag_forward(ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()), p,
+                            _stream_ptr(query.device, stream))
+    if rc != OK:
+        _raise(rc)
+    return out, smax, ssum
 
 
 def workspace_size(*args, **kw) -> int:

@@ -31,7 +31,7 @@ FILE_FLAGS = {
     "sfag_sdp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 HIP_SOURCES = ["sfag_prep.hip", "sfag_row.hip", "sfag_sdp.hip", "sfag_mfma.hip", "sfag_keyblock.hip",
-               "sfag_launch.hip"]
+               "sfag_fwd.hip", "sfag_launch.hip"]
 HOST_SOURCES = ["sfag_host.cpp"]
 
 

@@ -1,0 +1,244 @@
+// Forward pass of the top-k sparse attention whose backward the rest of the
+// library computes.  It produces the three tensors the backward takes from
+// the forward (operator page "aclnnSparseFlashAttentionGrad", 功能说明 and the
+// parameter table: out, softmaxMax, softmaxSum):
+//     z[h][p] = scale · (Q[h]·K[p] + Qrope[h]·Krope[p])   over valid positions p
+//     softmaxMax[h] = max_p z,  softmaxSum[h] = Σ_p exp(z − max)
+//     out[h] = Σ_p exp(z − max) / softmaxSum · V[p]
+// A token without a valid position gets max = −inf, sum = 0 and out = 0.
+//
+// gfx950 mapping (the same tiles as the N1 <= 16 backward kernel): one
+// workgroup per (token, 64-head block), 4 waves of 16 heads.  Per tile of 32
+// gathered positions, Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32 (positions as M, the
+// wave's Q rows resident in registers), an online softmax per head (running
+// max and sum; the fp32 output accumulators are rescaled when the max
+// grows), and out += P·V with P taken straight from the Sᵀ accumulator
+// layout as the A operand and V read transposed from LDS
+// (ds_read_b64_tr_b16).  K|Krope|V rows arrive through global_load_lds into
+// a double buffer, 16-byte chunks XOR-swizzled by (row & 7).
+#include "sfag_device.h"
+#include "sfag_kernels.h"
+#include "sfag_plan.h"
+
+namespace sfag {
+
+namespace {
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+constexpr int kTile = 32;   // positions per tile
+constexpr int kXcds = 8;    // blockIdx % 8 picks the XCD
+constexpr int kRun = 16;    // consecutive tokens per XCD run
+
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 16, 0, 0);
+}
+
+}  // namespace
+
+template <typename TT, int DR, bool VK>
+__global__ void __launch_bounds__(256, 1) k_fwd(FwdArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int KS_QK = DQK / 32;
+  constexpr int NB_V = 512 / 16;                // 16-column blocks of out
+  constexpr int KM_BYTES = kTile * 1024;
+  constexpr int KR_BYTES = kTile * DR * 2;
+  constexpr int V_BYTES = VK ? 0 : kTile * 1024;
+  constexpr int BUF = KM_BYTES + KR_BYTES + V_BYTES;
+  typedef typename TT::vec8 V8;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+
+  // ---- work unit: (token, head block), XCD-aware order ---------------------
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, u = b / kXcds;
+  const int hb = u % a.n_hb;
+  const int tq = u / a.n_hb;
+  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int h0 = hb * 64 + wave * 16;
+  const bool wave_on = h0 < a.Gp;
+  const int h = h0 + n;
+  const bool hv = h < a.G;
+
+  // B operand of Sᵀ = K·Qᵀ: lane (head n, k-group g) holds dims 32ks + 8g ..
+  V8 Qf[KS_QK];
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (wave_on && hv) {
+      if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
+      else v = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
+    }
+    Qf[ks] = as_vec8<V8>(v);
+  }
+  f32x4 acc[NB_V];
+#pragma unroll
+  for (int i = 0; i < NB_V; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max (natural units) of head n, and this lane's share of the sum
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+
+  // Gather the 32 rows of tile c0 into buffer `buf`; rows past nv repeat a
+  // valid row (masked out of the softmax).  Wave w loads rows 8w..8w+7.
+  auto issue_tile = [&](int c0, int buf) {
+    unsigned char* base = smem + buf * BUF;
+    const int r_l = wave * 8 + (lane >> 3);  // rope row handled by this lane
+    const int c_l = c0 + r_l;
+    const int key_l = rt[c_l < nv ? c_l : 0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = wave * 8 + j;
+      const int64_t key = __builtin_amdgcn_readfirstlane(__shfl(key_l, j * 8, 64));
+      const int gc = lane ^ (r & 7);
+      lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
+      if (!VK) lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+    }
+    if (DR > 0) {
+      const int pc = lane & 7;
+      const int gc = pc ^ (r_l & 7);
+      lds_load16(a.kr + (int64_t)key_l * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
+    }
+  };
+
+  // Per-lane LDS byte offsets (chunk c of row r sits at (c & ~7) | ((c & 7) ^ (r & 7))).
+  const int x = n & 7;
+  const int oA_even = n * 1024 + 16 * (g ^ x);
+  const int oA_odd = n * 1024 + 16 * ((4 + g) ^ x);
+  const int oR_even = n * (DR * 2) + 16 * (g ^ x);
+  const int oR_odd = n * (DR * 2) + 16 * ((4 + g) ^ x);
+  const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;       // V rows r1 and r1 + 16 for the out MFMA
+  const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
+  int oT[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) oT[w] = r1 * 1024 + 16 * ((2 * w + half) ^ x1) + hoff;
+
+  if (nv > 0) issue_tile(0, 0);
+  int cur = 0;
+  for (int c0 = 0; c0 < nv; c0 += kTile) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c0 + kTile < nv) issue_tile(c0 + kTile, cur ^ 1);
+    const unsigned char* Km = smem + cur * BUF;
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
+    if (wave_on) {
+      // Sᵀ: rows = positions mb*16 + 4g + i, column = head n
+      f32x4 s[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* ke = Km + oA_even + mb * 16384;
+        const unsigned char* ko = Km + oA_odd + mb * 16384;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const unsigned char* p = ((ks & 1) ? ko : ke) + 128 * (ks >> 1);
+          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), Qf[ks], s[mb]);
+        }
+        if (DR > 0) {
+          const unsigned char* re = Kr + oR_even + mb * 16 * (DR * 2);
+          const unsigned char* ro = Kr + oR_odd + mb * 16 * (DR * 2);
+          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)re), Qf[KS_QK - 2], s[mb]);
+          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)ro), Qf[KS_QK - 1], s[mb]);
+        }
+      }
+      // online softmax of head n over the tile's valid positions
+      float z[8];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = mb * 16 + 4 * g + i;
+          z[mb * 4 + i] = c0 + j < nv ? s[mb][i] * a.scale : -__builtin_inff();
+          tmax = fmaxf(tmax, z[mb * 4 + i]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);   // finite: the tile has a valid position
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+      uint16_t pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f((z[j] - m_new) * kLog2e);
+        psum += p;
+        pv[j] = TT::from_f(p);
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // rescale the accumulator rows (heads 4g + i) by their heads' alpha
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int nb = 0; nb < NB_V; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nb][i] *= ar[i];
+      // out += P·V: A = P (head n, positions 4g+i and 16+4g+i), B = V rows
+      // 4g..4g+3 and 16+4g..16+4g+3 of one column, read transposed
+      const uint4 pu = make_uint4(pv[0] | ((uint32_t)pv[1] << 16), pv[2] | ((uint32_t)pv[3] << 16),
+                                  pv[4] | ((uint32_t)pv[5] << 16), pv[6] | ((uint32_t)pv[7] << 16));
+      const V8 A8 = as_vec8<V8>(pu);
+#pragma unroll
+      for (int nb = 0; nb < NB_V; ++nb) {
+        const unsigned char* p1 = Vm + oT[nb & 3] + 128 * (nb >> 2);
+        const V8 B8 = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 1024)));
+        acc[nb] = TT::mfma(A8, B8, acc[nb]);
+      }
+    }
+    cur ^= 1;
+  }
+  if (!wave_on) return;
+  // the sum of head n over the four lanes that share it
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (g == 0 && hv) {
+    a.smax[t * a.G + h] = m_run;
+    a.ssum[t * a.G + h] = l_tot;
+  }
+  float inv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float li = __shfl(l_tot, 4 * g + i);
+    inv[i] = li > 0.f ? 1.f / li : 0.f;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB_V; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = h0 + 4 * g + i;
+      if (hh < a.G) a.out[(t * a.G + hh) * 512 + 16 * nb + n] = TT::from_f(acc[nb][i] * inv[i]);
+    }
+  }
+}
+
+void launch_fwd(int32_t dtype, bool rope, const FwdArgs& a, hipStream_t s) {
+  if (a.ntok == 0) return;
+  const int64_t per = (int64_t)kXcds * kRun;
+  const int64_t padded = (a.ntok + per - 1) / per * per;
+  const dim3 grid((unsigned)(padded * a.n_hb)), block(256);
+  const bool vk = a.v == a.k;   // value passed as the key tensor: gather each row once
+  auto go = [&](auto tt, auto dr) {
+    typedef decltype(tt) T;
+    constexpr int D = decltype(dr)::value;
+    if (vk) hipLaunchKernelGGL((k_fwd<T, D, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_fwd<T, D, false>), grid, block, 0, s, a);
+  };
+  if (dtype == SFAG_BF16) {
+    if (rope) go(BF16(), std::integral_constant<int, 64>());
+    else go(BF16(), std::integral_constant<int, 0>());
+  } else {
+    if (rope) go(FP16(), std::integral_constant<int, 64>());
+    else go(FP16(), std::integral_constant<int, 0>());
+  }
+}
+
+}  // namespace sfag

@@ -374,3 +374,56 @@ extern "C" int sfag_workspace_size(
   *plan = p;
   return SFAG_OK;
 }
+
+// Forward pass (produces out, softmaxMax, softmaxSum).  The shared inputs and
+// the three outputs obey the same rules as in the backward call, so the
+// backward validation runs on them, with the outputs standing in for dOut and
+// the statistics and the inputs for the gradient outputs (same shapes and
+// dtypes by construction).  The workspace holds the TND offsets and the
+// decoded key rows of one chunk of tokens.
+extern "C" int sfag_forward_workspace_size(
+    const sfag_tensor* query, const sfag_tensor* key, const sfag_tensor* value, const sfag_tensor* sparseIndices,
+    const sfag_tensor* lensQ, const sfag_tensor* lensKv, const sfag_tensor* queryRope, const sfag_tensor* keyRope,
+    double scaleValue, int64_t sparseBlockSize, const char* layoutOptional, int64_t sparseMode,
+    const sfag_tensor* out, const sfag_tensor* softmaxMax, const sfag_tensor* softmaxSum, uint64_t* workspaceSize,
+    sfag_plan** plan) {
+  if (plan) *plan = nullptr;
+  if (!out || !softmaxMax || !softmaxSum) return fail(SFAG_ERR_NULLPTR, "out, softmaxMax and softmaxSum are required");
+  if (!workspaceSize || !plan) return fail(SFAG_ERR_NULLPTR, "workspaceSize or plan output pointer is NULL");
+  sfag_plan* p = nullptr;
+  uint64_t ws = 0;
+  const int rc = sfag_workspace_size(query, key, value, sparseIndices, out, out, softmaxMax, softmaxSum, lensQ,
+                                     lensKv, queryRope, keyRope, scaleValue, sparseBlockSize, layoutOptional,
+                                     sparseMode, kWindow, kWindow, false, query, key, value, queryRope, keyRope,
+                                     &ws, &p);
+  if (rc != SFAG_OK) return rc;
+  Dims d = p->d;
+  p->forward = true;
+  p->out_w = out->data;
+  p->smax_w = softmaxMax->data;
+  p->ssum_w = softmaxSum->data;
+  if (d.T1 == 0) {
+    p->d = d;
+    p->ws = WorkspaceLayout();
+    *workspaceSize = 0;
+    *plan = p;
+    return SFAG_OK;
+  }
+  const uint64_t per_tok = 4 + (uint64_t)d.E * 4;
+  const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 16384);
+  int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
+  if (chunk < 1) chunk = 1;
+  if (chunk > d.T1) chunk = d.T1;
+  d.chunk = chunk;
+  WorkspaceLayout w;
+  uint64_t c = 0;
+  carve(c, w.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
+  carve(c, w.nvalid, (uint64_t)chunk * 4);
+  carve(c, w.rows, (uint64_t)chunk * d.E * 4);
+  w.total = c;
+  p->d = d;
+  p->ws = w;
+  *workspaceSize = w.total;
+  *plan = p;
+  return SFAG_OK;
+}

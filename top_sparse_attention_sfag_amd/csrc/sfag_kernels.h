@@ -44,6 +44,18 @@ struct KbArgs {
   ColBlock cbs[kMaxColBlocks];
 };
 
+// Forward pass (out, softmaxMax, softmaxSum) over one chunk of tokens.
+struct FwdArgs {
+  const uint16_t *q, *qr, *k, *kr, *v;
+  const int32_t *rows, *nvalid;
+  uint16_t* out;
+  float *smax, *ssum;
+  int64_t t0, ntok, G, Gp, E;
+  int32_t n_hb;   // 64-head blocks per token
+  float scale;
+};
+void launch_fwd(int32_t dtype, bool rope, const FwdArgs& a, hipStream_t s);
+
 struct ColArgs {
   const uint16_t *q, *qr, *dO, *ds, *p;
   const int32_t *rows, *nvalid;

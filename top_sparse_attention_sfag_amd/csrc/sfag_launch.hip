@@ -103,10 +103,62 @@ extern "C" int sfag_profile_read(const char* name, double* total_ms, int64_t* la
   return SFAG_OK;
 }
 
+extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream) {
+  set_error("");
+  std::unique_ptr<sfag_plan> own(plan);
+  if (!plan) return fail(SFAG_ERR_NULLPTR, "plan is NULL");
+  if (!plan->forward) return fail(SFAG_ERR_PARAM_INVALID, "plan was made for the backward pass");
+  const Dims& d = plan->d;
+  const WorkspaceLayout& w = plan->ws;
+  if (workspaceSize < w.total) return fail(SFAG_ERR_PARAM_INVALID, "workspace smaller than the phase-1 size");
+  if (w.total > 0 && !workspace) return fail(SFAG_ERR_NULLPTR, "workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d.T1 == 0) return SFAG_OK;
+  int32_t* q_off = nullptr;
+  int32_t* kv_off = nullptr;
+  if (d.layout == 1) {
+    q_off = at<int32_t>(workspace, w.seq_off);
+    kv_off = q_off + (d.B + 1);
+    launch_seq_offsets((const int32_t*)plan->lq, (const int32_t*)plan->lk, (int32_t)d.B, q_off, kv_off, s);
+  }
+  FwdArgs fa;
+  fa.q = (const uint16_t*)plan->q;
+  fa.qr = (const uint16_t*)plan->qr;
+  fa.k = (const uint16_t*)plan->k;
+  fa.kr = (const uint16_t*)plan->kr;
+  fa.v = (const uint16_t*)plan->v;
+  int32_t* rows = at<int32_t>(workspace, w.rows);
+  int32_t* nvalid = at<int32_t>(workspace, w.nvalid);
+  fa.rows = rows;
+  fa.nvalid = nvalid;
+  fa.out = (uint16_t*)plan->out_w;
+  fa.smax = (float*)plan->smax_w;
+  fa.ssum = (float*)plan->ssum_w;
+  fa.G = d.G;
+  fa.Gp = d.Gp;
+  fa.E = d.E;
+  fa.n_hb = (int32_t)((d.Gp + 63) / 64);
+  fa.scale = plan->scale;
+  for (int64_t t0 = 0; t0 < d.T1; t0 += d.chunk) {
+    const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
+    {
+      TimedScope ts("decode", s);
+      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s);
+    }
+    fa.t0 = t0;
+    fa.ntok = ntok;
+    TimedScope ts("fwd", s);
+    launch_fwd(plan->dtype, d.Dr > 0, fa, s);
+  }
+  return check_launch("forward kernels");
+}
+
 extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream) {
   set_error("");
   std::unique_ptr<sfag_plan> own(plan);
   if (!plan) return fail(SFAG_ERR_NULLPTR, "plan is NULL");
+  if (plan->forward) return fail(SFAG_ERR_PARAM_INVALID, "plan was made for the forward pass");
   const Dims& d = plan->d;
   const WorkspaceLayout& w = plan->ws;
   if (workspaceSize < w.total) return fail(SFAG_ERR_PARAM_INVALID, "workspace smaller than the phase-1 size");

@@ -84,6 +84,9 @@ struct sfag_plan {
   bool deterministic = false;
   float scale = 0.f;
   int32_t scatter = 0;
+  // forward plans: the outputs out / softmaxMax / softmaxSum
+  bool forward = false;
+  void *out_w = nullptr, *smax_w = nullptr, *ssum_w = nullptr;
   sfag::Dims d;
   sfag::WorkspaceLayout ws;
 };

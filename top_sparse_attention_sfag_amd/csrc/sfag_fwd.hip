@@ -31,8 +31,16 @@ constexpr int kTile = 32;   // positions per tile
 constexpr int kXcds = 8;    // blockIdx % 8 picks the XCD
 constexpr int kRun = 16;    // consecutive tokens per XCD run
 
+// Asynchronous global -> LDS copy of 16 bytes per lane (lane l writes at the
+// wave-uniform LDS address l_base + 16 l).  Inline asm on purpose: the
+// compiler's own form of this copy is tracked as a pending LDS write, and
+// without alias information it then waits for every outstanding copy before
+// the next LDS read, so the next tile's gather would not overlap the current
+// tile's MFMAs.  Reads of copied data follow the explicit s_waitcnt and the
+// barrier at the top of each tile.
 __device__ __forceinline__ void lds_load16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((gvoid*)g, (lvoid*)l, 16, 0, 0);
+  const uint32_t la = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
 }
 
 }  // namespace

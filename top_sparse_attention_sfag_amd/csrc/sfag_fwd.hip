@@ -139,23 +139,22 @@ __global__ void __launch_bounds__(256, 1) k_fwd(FwdArgs a) {
     const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
     if (wave_on) {
       // Sᵀ: rows = positions mb*16 + 4g + i, column = head n
-      f32x4 s[2];
+      // (operand reads issued three MFMAs ahead; each step pinned in order)
+      constexpr int NS = 2 * KS_QK;                 // MFMAs of the two row blocks
+      auto kaddr = [&](int i) -> const unsigned char* {
+        const int mb = i / KS_QK, ks = i % KS_QK;
+        if (ks < 16) return Km + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1) + mb * 16384;
+        return Kr + ((ks & 1) ? oR_odd : oR_even) + mb * 16 * (DR * 2);
+      };
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      uint4 kb4[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* ke = Km + oA_even + mb * 16384;
-        const unsigned char* ko = Km + oA_odd + mb * 16384;
+      for (int i = 0; i < 3; ++i) kb4[i] = *(const uint4*)kaddr(i);
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          const unsigned char* p = ((ks & 1) ? ko : ke) + 128 * (ks >> 1);
-          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), Qf[ks], s[mb]);
-        }
-        if (DR > 0) {
-          const unsigned char* re = Kr + oR_even + mb * 16 * (DR * 2);
-          const unsigned char* ro = Kr + oR_odd + mb * 16 * (DR * 2);
-          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)re), Qf[KS_QK - 2], s[mb]);
-          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)ro), Qf[KS_QK - 1], s[mb]);
-        }
+      for (int i = 0; i < NS; ++i) {
+        if (i + 3 < NS) kb4[(i + 3) & 3] = *(const uint4*)kaddr(i + 3);
+        s[i / KS_QK] = TT::mfma(as_vec8<V8>(kb4[i & 3]), Qf[i % KS_QK], s[i / KS_QK]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // online softmax of head n over the tile's valid positions
       float z[8];
@@ -195,11 +194,18 @@ __global__ void __launch_bounds__(256, 1) k_fwd(FwdArgs a) {
       const uint4 pu = make_uint4(pv[0] | ((uint32_t)pv[1] << 16), pv[2] | ((uint32_t)pv[3] << 16),
                                   pv[4] | ((uint32_t)pv[5] << 16), pv[6] | ((uint32_t)pv[7] << 16));
       const V8 A8 = as_vec8<V8>(pu);
+      auto vread = [&](int nb) -> V8 {
+        const unsigned char* p1 = Vm + oT[nb & 3] + 128 * (nb >> 2);
+        return join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 1024)));
+      };
+      V8 vb[4];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) vb[i] = vread(i);
 #pragma unroll
       for (int nb = 0; nb < NB_V; ++nb) {
-        const unsigned char* p1 = Vm + oT[nb & 3] + 128 * (nb >> 2);
-        const V8 B8 = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 1024)));
-        acc[nb] = TT::mfma(A8, B8, acc[nb]);
+        if (nb + 3 < NB_V) vb[(nb + 3) & 3] = vread(nb + 3);
+        acc[nb] = TT::mfma(A8, vb[nb & 3], acc[nb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     cur ^= 1;

@@ -164,30 +164,60 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
     if (wave_on) {
-      f32x4 s[2], dp[2];
+      // Sᵀ and dPᵀ.  With operand room (no rope, or value passed as the key)
+      // the reads run three MFMAs ahead, each step pinned in order; with the
+      // rope operands and a separate V that form spills, so the plain loops
+      // stay there.
+      constexpr bool kAhead = !(DR > 0 && !VK);
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 dp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (kAhead) {
+        constexpr int NS = 2 * KS_QK, NP = 2 * KS_V;
+        auto addr = [&](int i) -> const unsigned char* {
+          if (i < NS) {
+            const int mb = i / KS_QK, ks = i % KS_QK;
+            if (ks < 16) return Km + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1) + mb * 16384;
+            return Kr + ((ks & 1) ? oR_odd : oR_even) + mb * 16 * (DR * 2);
+          }
+          const int j = i - NS, mb = j / KS_V, ks = j % KS_V;
+          return Vm + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1) + mb * 16384;
+        };
+        constexpr int RA = 3;
+        uint4 ob[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* ke = Km + oA_even + mb * 16384;
-        const unsigned char* ko = Km + oA_odd + mb * 16384;
-        const unsigned char* ve = Vm + oA_even + mb * 16384;
-        const unsigned char* vo = Vm + oA_odd + mb * 16384;
+        for (int i = 0; i < RA; ++i) ob[i] = *(const uint4*)addr(i);
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          const unsigned char* p = ((ks & 1) ? ko : ke) + 128 * (ks >> 1);
-          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), Qf[ks], s[mb]);
+        for (int i = 0; i < NS + NP; ++i) {
+          if (i + RA < NS + NP) ob[(i + RA) & 3] = *(const uint4*)addr(i + RA);
+          if (i < NS) s[i / KS_QK] = TT::mfma(as_vec8<V8>(ob[i & 3]), Qf[i % KS_QK], s[i / KS_QK]);
+          else dp[(i - NS) / KS_V] = TT::mfma(as_vec8<V8>(ob[i & 3]), dOf[(i - NS) % KS_V], dp[(i - NS) / KS_V]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (DR > 0) {
-          const unsigned char* re = Kr + oR_even + mb * 16 * (DR * 2);
-          const unsigned char* ro = Kr + oR_odd + mb * 16 * (DR * 2);
-          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)re), Qf[KS_QK - 2], s[mb]);
-          s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)ro), Qf[KS_QK - 1], s[mb]);
-        }
+      } else {
 #pragma unroll
-        for (int ks = 0; ks < KS_V; ++ks) {
-          const unsigned char* p = ((ks & 1) ? vo : ve) + 128 * (ks >> 1);
-          dp[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), dOf[ks], dp[mb]);
+        for (int mb = 0; mb < 2; ++mb) {
+          s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const unsigned char* ke = Km + oA_even + mb * 16384;
+          const unsigned char* ko = Km + oA_odd + mb * 16384;
+          const unsigned char* ve = Vm + oA_even + mb * 16384;
+          const unsigned char* vo = Vm + oA_odd + mb * 16384;
+#pragma unroll
+          for (int ks = 0; ks < 16; ++ks) {
+            const unsigned char* p = ((ks & 1) ? ko : ke) + 128 * (ks >> 1);
+            s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), Qf[ks], s[mb]);
+          }
+          if (DR > 0) {
+            const unsigned char* re = Kr + oR_even + mb * 16 * (DR * 2);
+            const unsigned char* ro = Kr + oR_odd + mb * 16 * (DR * 2);
+            s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)re), Qf[KS_QK - 2], s[mb]);
+            s[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)ro), Qf[KS_QK - 1], s[mb]);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS_V; ++ks) {
+            const unsigned char* p = ((ks & 1) ? vo : ve) + 128 * (ks >> 1);
+            dp[mb] = TT::mfma(as_vec8<V8>(*(const uint4*)p), dOf[ks], dp[mb]);
+          }
         }
       }
       // P = exp(scale·S − max)/sum and dS = P ∘ (dP − Delta) for head h and
@@ -213,12 +243,24 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
       const V8 A8 = as_vec8<V8>(dsu);
       // dQ += dS·K over the tile's 32 positions: B operand = K rows
       // 4g..4g+3 and 16+4g..16+4g+3 of one column, read transposed.
-#pragma unroll
-      for (int nb = 0; nb < NB_Q; ++nb) {
+      auto kread = [&](int nb) -> V8 {
         const unsigned char* p1 = nb < 32 ? Km + oT[nb & 3] + 128 * (nb >> 2) : Kr + oTr[nb & 3];
         const unsigned char* p2 = p1 + (nb < 32 ? 16 * 1024 : 16 * (DR * 2));
-        const V8 B8 = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)p2));
-        acc[nb] = TT::mfma(A8, B8, acc[nb]);
+        return join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)p2));
+      };
+      if constexpr (kAhead) {
+        V8 kb[4];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) kb[i] = kread(i);
+#pragma unroll
+        for (int nb = 0; nb < NB_Q; ++nb) {
+          if (nb + 3 < NB_Q) kb[(nb + 3) & 3] = kread(nb + 3);
+          acc[nb] = TT::mfma(A8, kb[nb & 3], acc[nb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB_Q; ++nb) acc[nb] = TT::mfma(A8, kread(nb), acc[nb]);
       }
     }
     __syncthreads();

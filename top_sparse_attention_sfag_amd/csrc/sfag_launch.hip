@@ -1,6 +1,7 @@
 // Phase 2 of the two-phase call (the operator page's aclnnSparseFlashAttentionGrad
 // execute step): carve the caller's workspace and enqueue the kernels on the
 // caller's stream.  Also the stand-alone index inversion entry point.
+#include <cstdlib>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -188,7 +189,14 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   int32_t* rows = at<int32_t>(workspace, w.rows);
   uint16_t* ds = at<uint16_t>(workspace, w.ds);
   uint16_t* pb = at<uint16_t>(workspace, w.p);
-  if (d.Gp < 32) {   // k_row reads Delta; k_sdp forms it from dO and O itself
+  // Token side: k_row (fused, 64 heads per workgroup) or k_sdp + k_dq (up to
+  // 128 heads per workgroup).  SFAG_TOKEN_PATH=row|sdp overrides.
+  bool use_row = d.Gp < 32;
+  if (const char* tp = std::getenv("SFAG_TOKEN_PATH")) {
+    if (std::string(tp) == "row") use_row = true;
+    if (std::string(tp) == "sdp" && d.Gp >= 32) use_row = false;
+  }
+  if (use_row) {   // k_row reads Delta; k_sdp forms it from dO and O itself
     TimedScope ts("delta", s);
     launch_delta(plan->dtype, plan->dout, plan->out, delta, d.T1 * d.G, s);
   }
@@ -260,7 +268,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
     }
     ra.t0 = ca.t0 = t0;
     ra.ntok = ca.ntok = ntok;
-    if (d.Gp >= 32) {
+    if (!use_row) {
       {
         TimedScope ts("sdp", s);
         launch_sdp(plan->dtype, rope, ra, s);

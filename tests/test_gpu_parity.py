@@ -118,6 +118,17 @@ def test_value_is_key(case):
     _check(case, _outs_np(case, outs), ref, label=case.name)
 
 
+@pytest.mark.parametrize("name", ["g64_tnd_causal", "g128_zipf"])
+def test_token_paths_agree(monkeypatch, name):
+    """The fused token kernel (k_row, 64 heads per workgroup) and the split
+    one (k_sdp + k_dq) both match the oracle on the same N1 >= 32 inputs."""
+    case = next(c for c in SMALL if c.name == name)
+    inp = add_oracle_stats(case, si.make_inputs(case, 21))
+    for path in ("row", "sdp"):
+        monkeypatch.setenv("SFAG_TOKEN_PATH", path)
+        _run(case, seed=21, inp=inp)
+
+
 def test_duplicated_indices():
     case = si.Case("dup", S1=4, S2=64, G=16, K=40)
     inp = si.make_inputs(case, 3)

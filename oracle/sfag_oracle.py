@@ -320,3 +320,41 @@ def flops(rows: np.ndarray, G: int, D: int, Dr: int) -> int:
     (S, dQ, dK over D+Dr; dP, dV over D)."""
     n = int((rows >= 0).sum())
     return n * G * 2 * (3 * (D + Dr) + 2 * D)
+
+
+# ---------------------------------------------------------------------------
+# Band (sliding-window or dense) selection expressed as sparse indices.  The
+# MindSpore FlashAttention backward page ("flash_attention_bwd.py",
+# compute_in_each_kv_block) computes a query block q against a key block k only
+# when k - next_block_num <= q <= k + prev_block_num; here the same test is
+# taken per query token and aligned, as sparseMode 3 is, on the diagonal
+# through the bottom-right corner, so that dense and banded attention run
+# through the sparse backward unchanged.
+# ---------------------------------------------------------------------------
+
+def band_entries(max_key_len: int, pre: int, nxt: int, block: int) -> int:
+    """Index entries per row that hold every block a band can touch."""
+    if max_key_len <= 0:
+        return 0
+    width = min(max_key_len, pre + nxt + 1)
+    return min(-(-max_key_len // block), -(-(width - 1) // block) + 1)
+
+
+def band_indices(geom, K: int, pre: int, nxt: int, block: int) -> np.ndarray:
+    """(T1, K) int64 index rows of the band.
+
+    Query position t of a sequence (Lq queries, Lk keys) covers key positions
+    d - pre .. d + nxt, d = t + Lk - Lq, clipped to [0, Lk).  Its row lists, in
+    ascending order, the start of every block of ``block`` positions (block
+    starts are multiples of ``block``) that holds at least one covered
+    position, then -1; rows are cut at K entries.
+    """
+    T1 = geom["T1"]
+    out = np.full((T1, K), -1, np.int64)
+    for t in range(T1):
+        Lk = int(geom["Lk"][t])
+        d = int(geom["t_loc"][t]) + Lk - int(geom["Lq"][t])
+        covered = [p for p in range(max(0, d - pre), min(Lk - 1, d + nxt) + 1)]
+        starts = sorted({(p // block) * block for p in covered})[:K]
+        out[t, :len(starts)] = starts
+    return out

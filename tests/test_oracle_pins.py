@@ -370,3 +370,62 @@ def test_sampled_rows_equal_full_backward():
                         tokens=[0, 2, 3, 5])
     for n in ("dk", "dv", "dkr"):
         np.testing.assert_allclose(sub[n] + rest[n], g[n], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("S1,S2,pre,nxt,block", [(6, 6, 2, 1, 1), (5, 9, 3, 0, 1), (9, 5, 10**9, 0, 1),
+                                                  (7, 7, 10**9, 10**9, 1), (6, 20, 4, 2, 4), (8, 8, 0, 0, 1)])
+def test_band_equals_dense_band_mask(S1, S2, pre, nxt, block):
+    """band_indices (sliding window from the FlashAttention backward page's
+    block-band test, bottom-right aligned) through the sparse backward equals
+    dense attention under the band mask written as a 2-D comparison: key p is
+    live for query t iff its block holds a position within [d - pre, d + nxt]
+    (d = t + S2 - S1) inside [0, S2)."""
+    rng = np.random.default_rng(S1 * 31 + S2 + block)
+    G, D, Dr = 2, 6, 2
+    geom = orc.geometry("BSND", 1, S1, S2)
+    K = orc.band_entries(S2, pre, nxt, block)
+    idx = orc.band_indices(geom, K, pre, nxt, block)
+    q, qr = rng.standard_normal((S1, G, D)), rng.standard_normal((S1, G, Dr))
+    k, kr, v = rng.standard_normal((S2, D)), rng.standard_normal((S2, Dr)), rng.standard_normal((S2, D))
+    dO = rng.standard_normal((S1, G, D))
+    t = np.arange(S1)[:, None]
+    p = np.arange(S2)[None, :]
+    d = t + S2 - S1
+    lo, hi = np.maximum(d - pre, 0), np.minimum(d + nxt, S2 - 1)
+    mask = (lo <= hi) & (p // block >= lo // block) & (p // block <= hi // block)
+    # every selected block lies inside the key range here, so positions are never cut
+    ref = _dense_reference(q, k, v, qr, kr, dO, 0.31, mask)
+    O, M, L = orc.forward(q, k, v, qr, kr, idx, geom, block, 0, 0.31)
+    live = mask.any(1)
+    np.testing.assert_allclose(O[live], ref["O"][live], rtol=1e-12, atol=1e-12)
+    g = orc.backward(q, k, v, qr, kr, idx, dO, O, M, L, geom, block, 0, 0.31)
+    for name in ("dq", "dk", "dv", "dqr", "dkr"):
+        np.testing.assert_allclose(g[name], ref[name], rtol=1e-10, atol=1e-11, err_msg=name)
+
+
+def test_band_special_cases_and_entry_count():
+    """Unbounded band = every key in order; pre unbounded, next 0 = the
+    sparseMode 3 causal set; band_entries is the largest row any alignment
+    of the window needs (brute force over key lengths and offsets)."""
+    geom = orc.geometry("TND", 3, seqlens_q=(4, 0, 6), seqlens_kv=(9, 3, 6))
+    big = 10**9
+    rows = orc.band_indices(geom, 9, big, big, 1)
+    for t in range(geom["T1"]):
+        Lk = int(geom["Lk"][t])
+        np.testing.assert_array_equal(rows[t, :Lk], np.arange(Lk))
+        assert np.all(rows[t, Lk:] == -1)
+    causal = orc.band_indices(geom, 9, big, 0, 1)
+    dec_band = orc.decode(causal, 1, 0, geom)
+    dec_mode3 = orc.decode(np.tile(np.arange(9), (geom["T1"], 1)), 1, 3, geom)
+    np.testing.assert_array_equal(dec_band, dec_mode3)
+    for Lk in (1, 5, 16, 33):
+        for pre in (0, 1, 3, 7, 20):
+            for nxt in (0, 2, 5):
+                for block in (1, 2, 4, 8):
+                    g = orc.geometry("BSND", 1, Lk, Lk)
+                    full = orc.band_indices(g, Lk, pre, nxt, block)
+                    need = int((full >= 0).sum(1).max())
+                    got = orc.band_entries(Lk, pre, nxt, block)
+                    # the formula bounds every alignment; equality holds whenever the
+                    # worst alignment occurs among the Lk diagonals
+                    assert need <= got <= need + 1, (Lk, pre, nxt, block, need, got)

@@ -280,6 +280,11 @@ def main(argv=None):
                     help="time the backward pass (the headline) or the forward pass that feeds it")
     ap.add_argument("--value-is-key", action="store_true",
                     help="pass the key tensor as value too (the operator page's supported case)")
+    ap.add_argument("--dtype", choices=("config", "bf16", "fp16"), default="config",
+                    help="input/output dtype (default: the workload's own)")
+    ap.add_argument("--band", metavar="PRE,NEXT",
+                    help="replace the workload's indices with a band (sliding-window / dense) selection made by "
+                         "sfag_band_indices: key positions d-PRE..d+NEXT of the bottom-right diagonal d")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -300,12 +305,28 @@ def main(argv=None):
     import top_sparse_attention_sfag_amd as sfag
 
     case = si.CONFIGS[args.config]
+    if args.dtype != "config" and args.dtype != case.dtype:
+        case = case.replace(name=f"{case.name}_as_{args.dtype}", dtype=args.dtype)
+    band = None
+    if args.band:
+        band = tuple(int(x) for x in args.band.split(","))
+        max_lk = case.S2 if case.layout == "BSND" else max(case.seqlens_kv)
+        kb = sfag.band_entries(max_lk, band[0], band[1], case.block)
+        case = case.replace(name=f"{case.name}_band_pre{band[0]}_next{band[1]}", K=kb, index_rule="uniform")
     det = case.deterministic if args.deterministic == "config" else args.deterministic == "true"
     seed = si.seed_for(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {case.name} on {dev}", file=sys.stderr, flush=True)
     inp = si.make_inputs(case, seed, device=dev)
+    if band is not None:
+        shape = tuple(inp["sparse_indices"].shape)
+        kw_b = dict(pre_tokens=band[0], next_tokens=band[1], block_size=case.block, layout=case.layout, K=case.K)
+        if case.layout == "BSND":
+            kw_b.update(B=case.B, S1=case.S1, S2=case.S2, device=dev)
+        else:
+            kw_b.update(seqlens_q=inp["seqlens_q"], seqlens_kv=inp["seqlens_kv"])
+        inp["sparse_indices"] = sfag.band_indices(**kw_b).reshape(shape)
     if args.value_is_key:
         inp["value"] = inp["key"]
     inp.update(si.standin_stats(case, inp, seed, device=dev))

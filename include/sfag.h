@@ -169,6 +169,36 @@ int sfag_build_index(const void* sparseIndices, const void* seqLensQ, const void
                      void* csrOffsets, void* csrPairs, void* stream);
 
 /*
+ * Band (sliding-window or dense) selection written as sparse indices, so that
+ * dense and banded attention run through sfag_forward / sfag_backward on the
+ * same kernels.  The band is the block-band test of the MindSpore
+ * FlashAttention backward page ("flash_attention_bwd.py",
+ * compute_in_each_kv_block: query block q meets key block k iff
+ * k − next ≤ q ≤ k + prev), taken per query token and aligned, as sparseMode 3
+ * is, on the diagonal through the bottom-right corner: query position t of a
+ * sequence with Lq query and Lk key tokens covers key positions
+ * d − preTokens .. d + nextTokens, d = t + Lk − Lq, clipped to [0, Lk).
+ *
+ * sfag_band_indices writes sparseIndices (T1, K) int32 (device, row-major):
+ * row t holds, ascending, the start (a multiple of sparseBlockSize, local to
+ * the sequence) of every block of sparseBlockSize positions that contains a
+ * covered position, then −1 up to K entries; rows are cut after K entries.
+ * Tokens past the declared TND lengths get rows of −1.  seqLensQ / seqLensKv:
+ * device int32 (B,) per-sequence counts for layout 1 (TND, 1 ≤ B ≤ 256),
+ * ignored for layout 0 (BSND: T1 = B·S1, keys S2).  preTokens, nextTokens ≥ 0
+ * (2147483647 = unbounded); block ≥ 1.  Enqueued on `stream`; writes nothing
+ * else.  Errors: SFAG_ERR_TILING for bad layout or sizes, SFAG_ERR_NULLPTR for
+ * a missing pointer, SFAG_ERR_RUNTIME for a failed launch.
+ *
+ * sfag_band_entries(maxKeyLen, ...) is the K that loses no block for any
+ * sequence with at most maxKeyLen keys (0 for bad arguments).
+ */
+int64_t sfag_band_entries(int64_t maxKeyLen, int64_t preTokens, int64_t nextTokens, int64_t block);
+int sfag_band_indices(void* sparseIndices, const void* seqLensQ, const void* seqLensKv, int64_t B, int64_t S1,
+                      int64_t S2, int64_t T1, int64_t K, int64_t block, int32_t layout, int64_t preTokens,
+                      int64_t nextTokens, void* stream);
+
+/*
  * Optional per-kernel timing for measurement.  While enabled, sfag_backward
  * records a pair of HIP events on its stream around each kernel group
  * ("seq_offsets", "delta", "fill", "decode", "row", "col", "csr", "key_reduce",

@@ -185,3 +185,24 @@ def test_plans_are_not_interchangeable():
     ws, p = _plan(_tensors())
     assert sfag.lib().sfag_forward(None, ctypes.c_uint64(ws), p, None) == 161002
     assert b"backward" in sfag.lib().sfag_last_error()
+
+
+def test_band_entries_and_argument_errors():
+    """Band selection: the entry count and every host-side rejection (these
+    return before anything is launched, so no GPU is needed)."""
+    L = sfag.lib()
+    assert L.sfag_band_entries(4096, 2147483647, 0, 1) == 4096
+    assert L.sfag_band_entries(4096, 127, 0, 1) == 128
+    assert L.sfag_band_entries(4096, 127, 0, 16) == 9      # 128 positions can straddle 9 blocks of 16
+    assert L.sfag_band_entries(100, 2147483647, 2147483647, 64) == 2
+    assert L.sfag_band_entries(0, 5, 5, 1) == 0 and L.sfag_band_entries(10, -1, 0, 1) == 0
+    null = ctypes.c_void_p(None)
+    dummy = ctypes.c_void_p(16)
+    call = lambda *a: L.sfag_band_indices(*a)
+    assert call(dummy, null, null, 1, 8, 8, 8, 8, 1, 2, 0, 0, null) == sfag.ERR_TILING        # layout
+    assert call(dummy, null, null, 1, 8, 8, 8, 8, 0, 0, 0, 0, null) == sfag.ERR_TILING        # block
+    assert call(dummy, null, null, 1, 8, 8, 8, 8, 1, 0, -1, 0, null) == sfag.ERR_TILING       # preTokens
+    assert call(dummy, null, null, 1, 8, 8, 9, 8, 1, 0, 0, 0, null) == sfag.ERR_TILING        # T1 != B*S1
+    assert call(dummy, null, null, 0, 0, 0, 4, 8, 1, 1, 0, 0, null) == sfag.ERR_TILING        # TND B = 0
+    assert call(dummy, null, null, 2, 0, 0, 4, 8, 1, 1, 0, 0, null) == sfag.ERR_NULLPTR       # TND lengths
+    assert call(null, null, null, 1, 8, 8, 8, 8, 1, 0, 0, 0, null) == sfag.ERR_NULLPTR        # output

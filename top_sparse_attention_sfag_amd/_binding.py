@@ -76,6 +76,11 @@ def lib():
         L.sfag_build_index.restype = ctypes.c_int
         L.sfag_build_index.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 7 + [ctypes.c_int32, ctypes.c_int64]
                                        + [ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_void_p] * 5)
+        L.sfag_band_entries.restype = ctypes.c_int64
+        L.sfag_band_entries.argtypes = [ctypes.c_int64] * 4
+        L.sfag_band_indices.restype = ctypes.c_int
+        L.sfag_band_indices.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int64] * 6 + [ctypes.c_int32]
+                                        + [ctypes.c_int64] * 2 + [ctypes.c_void_p])
         L.sfag_profile_enable.restype = None
         L.sfag_profile_enable.argtypes = [ctypes.c_int]
         L.sfag_profile_reset.restype = None
@@ -266,3 +271,35 @@ def build_index(sparse_indices, *, T2, block_size=1, layout="BSND", sparse_mode=
     if rc != OK:
         _raise(rc)
     return n_valid, rows, off, pairs[: T1 * E]
+
+
+def band_entries(max_key_len, pre_tokens, next_tokens, block_size=1):
+    """Index entries per row that keep every block of a band (sfag_band_entries)."""
+    return int(lib().sfag_band_entries(max_key_len, pre_tokens, next_tokens, block_size))
+
+
+def band_indices(*, pre_tokens, next_tokens, block_size=1, layout="BSND", B=1, S1=None, S2=None, seqlens_q=None,
+                 seqlens_kv=None, K=None, device="cuda", stream=None):
+    """Sparse index rows of a band (sliding-window or dense) selection, made on
+    the GPU by sfag_band_indices.  Returns int32 (B, S1, 1, K) for BSND or
+    (T1, 1, K) for TND; K defaults to band_entries over the longest key
+    sequence."""
+    lay = 0 if layout == "BSND" else 1
+    if lay == 0:
+        T1, max_lk = B * S1, S2
+    else:
+        B = seqlens_q.numel()
+        T1 = int(seqlens_q.clamp(min=0).sum().item())
+        max_lk = int(seqlens_kv.max().item()) if seqlens_kv.numel() else 0
+        S1 = S2 = 0
+    if K is None:
+        K = band_entries(max_lk, pre_tokens, next_tokens, block_size)
+    dev = torch.device(device) if seqlens_q is None else seqlens_q.device
+    shape = (B, S1, 1, K) if lay == 0 else (T1, 1, K)
+    idx = torch.empty(shape, dtype=torch.int32, device=dev)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+    rc = lib().sfag_band_indices(ptr(idx), ptr(seqlens_q), ptr(seqlens_kv), B, S1 or 0, S2 or 0, T1, K, block_size,
+                                 lay, pre_tokens, next_tokens, _stream_ptr(dev, stream))
+    if rc != OK:
+        _raise(rc)
+    return idx

@@ -63,6 +63,8 @@ struct ColArgs {
   int64_t t0, ntok, G, Gp, E, AW;
 };
 
+void launch_band_indices(int32_t* idx, int64_t T1, int64_t K, int32_t block, int32_t layout, int64_t S1, int64_t S2,
+                         const int32_t* lq, const int32_t* lk, int32_t B, int64_t pre, int64_t nxt, hipStream_t s);
 void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int32_t* q_off, int32_t* kv_off,
                         hipStream_t s);
 void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, int64_t nrows, hipStream_t s);

@@ -1,6 +1,7 @@
 // Phase 2 of the two-phase call (the operator page's aclnnSparseFlashAttentionGrad
 // execute step): carve the caller's workspace and enqueue the kernels on the
 // caller's stream.  Also the stand-alone index inversion entry point.
+#include <algorithm>
 #include <cstdlib>
 #include <map>
 #include <memory>
@@ -390,6 +391,34 @@ IndexLayout index_layout(int64_t T1, int64_t E) {
 }
 
 }  // namespace
+
+extern "C" int64_t sfag_band_entries(int64_t maxKeyLen, int64_t preTokens, int64_t nextTokens, int64_t block) {
+  if (maxKeyLen <= 0 || preTokens < 0 || nextTokens < 0 || block < 1) return 0;
+  const int64_t width = std::min<int64_t>(maxKeyLen, std::min<int64_t>(preTokens, maxKeyLen) +
+                                                         std::min<int64_t>(nextTokens, maxKeyLen) + 1);
+  return std::min<int64_t>((maxKeyLen + block - 1) / block, (width - 1 + block - 1) / block + 1);
+}
+
+extern "C" int sfag_band_indices(void* sparseIndices, const void* seqLensQ, const void* seqLensKv, int64_t B,
+                                 int64_t S1, int64_t S2, int64_t T1, int64_t K, int64_t block, int32_t layout,
+                                 int64_t preTokens, int64_t nextTokens, void* stream) {
+  set_error("");
+  if (layout != 0 && layout != 1) return fail(SFAG_ERR_TILING, "layout must be 0 (BSND) or 1 (TND)");
+  if (block < 1 || block > (1 << 20) || K < 0 || T1 < 0 || B < 0)
+    return fail(SFAG_ERR_TILING, "bad sizes (block >= 1, K, T1, B >= 0)");
+  if (preTokens < 0 || nextTokens < 0) return fail(SFAG_ERR_TILING, "preTokens and nextTokens must be >= 0");
+  if (layout == 0 && (S1 < 0 || S2 < 0 || S2 > 0x7fffffffLL || B * S1 != T1))
+    return fail(SFAG_ERR_TILING, "BSND needs T1 = B*S1 and 0 <= S2 < 2^31");
+  if (layout == 1 && (B < 1 || B > 256)) return fail(SFAG_ERR_TILING, "TND needs 1 <= B <= 256");
+  if (T1 > 0 && K > 0 && !sparseIndices) return fail(SFAG_ERR_NULLPTR, "sparseIndices is NULL");
+  if (layout == 1 && (!seqLensQ || !seqLensKv)) return fail(SFAG_ERR_NULLPTR, "TND needs both length arrays");
+  if (T1 > 0x7fffffffLL) return fail(SFAG_ERR_TILING, "T1 must be below 2^31");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_band_indices((int32_t*)sparseIndices, T1, K, (int32_t)block, layout, S1, S2, (const int32_t*)seqLensQ,
+                      (const int32_t*)seqLensKv, (int32_t)B, preTokens, nextTokens, s);
+  return check_launch("band indices");
+}
 
 extern "C" uint64_t sfag_index_workspace_size(int64_t T1, int64_t T2, int64_t K, int64_t block) {
   (void)T2;

@@ -347,6 +347,50 @@ static inline unsigned grid_for(uint64_t n, unsigned per_block, unsigned cap = 6
 }
 
 // In-place exclusive scan of n counts; tmp holds ceil(n / kScanSeg) ints.
+// ---------------------------------------------------------------------------
+// Band selection written as index rows (the block-band test of the MindSpore
+// FlashAttention backward page, "flash_attention_bwd.py",
+// compute_in_each_kv_block, taken per query token and aligned like
+// sparseMode 3 on the bottom-right diagonal): query position t of a sequence
+// covers key positions d - pre .. d + nxt (d = t + Lk - Lq) inside [0, Lk);
+// its row holds the ascending starts of the blocks that overlap them, then -1.
+// One block per token; with TND the per-sequence offsets are formed in LDS
+// (B <= 256, negative lengths count as 0).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_band_indices(int32_t* __restrict__ idx, int64_t K, int32_t block,
+                                                      int32_t layout, int64_t S1, int64_t S2,
+                                                      const int32_t* __restrict__ lq,
+                                                      const int32_t* __restrict__ lk, int32_t B, int64_t pre,
+                                                      int64_t nxt) {
+  __shared__ int32_t sq[257], sk[257];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (layout == 1) {
+    if (tid < B) {
+      sq[tid + 1] = max(lq[tid], 0);
+      sk[tid + 1] = max(lk[tid], 0);
+    }
+    if (tid == 0) {
+      sq[0] = sk[0] = 0;
+      for (int b = 1; b <= B; ++b) {
+        sq[b] += sq[b - 1];
+        sk[b] += sk[b - 1];
+      }
+    }
+    __syncthreads();
+  }
+  const TokenGeo g = token_geo(t, layout, S1, S2, sq, sk, B);
+  const int64_t lo = max<int64_t>(0, (int64_t)g.bound - pre);
+  const int64_t hi = min<int64_t>((int64_t)g.Lk - 1, (int64_t)g.bound + nxt);
+  int64_t first = 0, nblk = 0;
+  if (g.ok && lo <= hi) {
+    first = lo / block;
+    nblk = hi / block - first + 1;
+  }
+  int32_t* row = idx + t * K;
+  for (int64_t j = tid; j < K; j += 256) row[j] = j < nblk ? (int32_t)((first + j) * block) : -1;
+}
+
 void launch_scan_i32(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s) {
   const int64_t nseg = (n + kScanSeg - 1) / kScanSeg;
   if (nseg <= 1) {
@@ -437,6 +481,13 @@ void launch_cast(int32_t dtype, const float* acc, int64_t T2, int32_t D, int32_t
   else
     hipLaunchKernelGGL(k_cast<FP16>, grid, dim3(256), 0, s, acc, T2, D, Dr, kscale, (uint16_t*)dk, (uint16_t*)dkr,
                        (uint16_t*)dv);
+}
+
+void launch_band_indices(int32_t* idx, int64_t T1, int64_t K, int32_t block, int32_t layout, int64_t S1, int64_t S2,
+                         const int32_t* lq, const int32_t* lk, int32_t B, int64_t pre, int64_t nxt, hipStream_t s) {
+  if (T1 == 0 || K == 0) return;
+  hipLaunchKernelGGL(k_band_indices, dim3((unsigned)T1), dim3(256), 0, s, idx, K, block, layout, S1, S2, lq, lk, B,
+                     pre, nxt);
 }
 
 }  // namespace sfag

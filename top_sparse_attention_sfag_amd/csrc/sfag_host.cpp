@@ -350,10 +350,11 @@ extern "C" int sfag_workspace_size(
   d.chunk = chunk;
   d.nKB = (d.T2 + kKeyBlockRows - 1) / kKeyBlockRows;
   if (keyblock) {
-    // 16 token ranges per chunk (the XCD snake pairs ranges x and 15 - x),
-    // fewer when that would leave under 32 tokens per range or need more
-    // than 4 GiB of fp32 partials.  The key-block sort key must fit in 31 bits.
-    int64_t ntr = 16;
+    // 16 token ranges per chunk (the XCD snake pairs ranges x and 15 - x;
+    // SFAG_KB_RANGES overrides the count), fewer when that would leave under
+    // 32 tokens per range or need more than 4 GiB of fp32 partials.  The
+    // key-block sort key must fit in 31 bits.
+    int64_t ntr = std::max<int64_t>(1, env_i64("SFAG_KB_RANGES", 16));
     const int64_t part_bytes = d.T2 * (2 * d.D + d.Dr) * 4;
     if (part_bytes > 0) ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, (4LL << 30) / part_bytes));
     ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, chunk / 32));

@@ -140,9 +140,13 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   constexpr int BUF = KM_BYTES + KR_BYTES + (VK ? 0 : kTile * 1024);
   typedef typename TT::vec8 V8;
 
-  // Two tile buffers as separate LDS objects.
+  // Two tile buffers as separate LDS objects.  With fewer than four waves and
+  // a separate V (68 KB per tile) one buffer is used, so that two workgroups
+  // share a CU and each hides the other's gathers: a tile's copies are issued
+  // once every wave has read the buffer, and land during its P/dS work.
+  constexpr bool kSingle = NW < 4 && !VK;
   __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
-  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[kSingle ? 16 : BUF];
 
   constexpr int nw = NW;
   const int HB = 32 * nw;
@@ -310,7 +314,17 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
     // With fewer than four waves (more copies per wave) the copies go out
     // here at once; spreading them would cost registers.
     constexpr bool kSpread = NW == 4;
-    if (!kSpread && more) issue_rows<DR, !VK, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    if (!kSpread && !kSingle && more)
+      issue_rows<DR, !VK, true>(a.k, a.kr, a.v, keys, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+    // single buffer: the next tile's copies once every wave has read this one
+    // (with the row indices of the next tile, taken before `keys` advances)
+    const int32_t keys_next = keys;
+    auto issue_single = [&]() {
+      if (kSingle && more) {
+        bar();
+        issue_rows<DR, !VK, true>(a.k, a.kr, a.v, keys_next, nxt, KM_BYTES, KR_BYTES, wave, nw, lane);
+      }
+    };
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = VK ? Km : Kr + KR_BYTES;
     f32x16 S, P;
@@ -353,8 +367,11 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
         const int ch = 2 * j + kg;
         bv[j] = *(const uint4*)(Kr + oR + ((ch ^ xr) << 4));
       }
+      issue_single();
 #pragma unroll
       for (int j = 0; j < 4; ++j) S = mfma32<TT>(Qf[32 + j], as_vec8<V8>(bv[j]), S);
+    } else {
+      issue_single();
     }
     // P and dS of position c0 + m for the lane's 16 heads
     const bool valid = c0 + m < nv;
@@ -384,8 +401,13 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   if (nv > 0) issue_rows<DR, !VK, true>(a.k, a.kr, a.v, keys, buf0, KM_BYTES, KR_BYTES, wave, nw, lane);
   keys = tile_keys(rt, nv, kTile, lane);
   for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
-    tile(c0, buf0, buf1);
-    if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+    if (kSingle) {
+      tile(c0, buf0, buf0);
+      if (c0 + kTile < nv) tile(c0 + kTile, buf0, buf0);
+    } else {
+      tile(c0, buf0, buf1);
+      if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+    }
   }
   if (kStage) {
     __syncthreads();

@@ -163,9 +163,10 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   };
   // map of visit v from its pairs: the first kEnt from the LDS copy, the
   // rest (only with duplicated keys) straight from memory
-  auto build = [&](int b, int64_t v) {
+  // (eh: which of the two entry buffers holds the visit's pairs)
+  auto build = [&](int b, int64_t v, int eh) {
     const int cnt = v_count(v);
-    if (tid < cnt && tid < kEnt) add_entry(b, e_pair[tid], e_row[tid]);
+    if (tid < cnt && tid < kEnt) add_entry(b, e_pair[eh * kEnt + tid], e_row[eh * kEnt + tid]);
     const int64_t s0 = v_start(v);
     for (int j = tid + kEnt; j < cnt; j += kThreads) add_entry(b, a.svals[s0 + j], a.er[s0 + j]);
   };
@@ -173,7 +174,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // copy of visit v's first kEnt pairs (ids and key rows) into LDS: 8
   // dword-copy instructions, two per wave; lanes past the visit re-read
   // its first pair
-  auto issue_entries = [&](int64_t v) {
+  auto issue_entries = [&](int64_t v, int eh) {
     const int64_t s0 = v_start(v);
     const int cnt = v_count(v);
 #pragma unroll
@@ -182,8 +183,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       const int part = ins & 3;
       const int e = part * 64 + lane;
       const int64_t src = s0 + (e < cnt ? e : 0);
-      if (ins < 4) dma4(a.svals + src, l_pair + part * 256);
-      else dma4(a.er + src, l_row + part * 256);
+      if (ins < 4) dma4(a.svals + src, l_pair + eh * kEnt * 4 + part * 256);
+      else dma4(a.er + src, l_row + eh * kEnt * 4 + part * 256);
     }
   };
 
@@ -350,6 +351,54 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     }
   }
   __syncthreads();
+
+  if (GP == 0 && nks <= 2) {
+    // Up to 64 heads (one or two 32-head stages per visit): visits alternate
+    // between the buffer pairs st0|st1 and st2|st3; the stages of visit v + 1
+    // are copied while visit v is computed (its slot map was built a visit
+    // earlier), so each visit waits once, for copies issued a visit ago.
+    auto vbuf = [&](int64_t v, int ks) -> unsigned char* { return stage_buf((int)(((v - vlo) & 1) << 1) + ks); };
+    auto vlds = [&](int64_t v, int ks) -> uint32_t { return stage_lds((int)(((v - vlo) & 1) << 1) + ks); };
+    auto issue_visit = [&](int b, int64_t v) {
+      const int64_t tl = v_token(v);
+      for (int ks = 0; ks < nks; ++ks) issue_stage(b, tl, ks, vlds(v, ks));
+    };
+    // The pairs of visit v + 3 are copied at the top of visit v (the two
+    // entry buffers alternate) and its slot map is built at the end of visit
+    // v + 1: the top-of-visit wait covers both kinds of copies, each issued a
+    // whole visit earlier.
+    auto ehalf = [&](int64_t v) -> int { return (int)((v - vlo) & 1); };
+    StageCopy none;
+    none.on = false;
+    if (vlo + 2 < vhi) issue_entries(vlo + 2, ehalf(vlo + 2));
+    issue_visit(0, vlo);
+    for (int64_t v = vlo; v < vhi; ++v) {
+      const int u = (int)((v - vlo) % 3);
+      const int u1 = u == 2 ? 0 : u + 1, u2 = u == 0 ? 2 : u - 1;
+      if (v - wb + 3 > kWin) {   // visits v .. v + 3 leave the window
+        __syncthreads();
+        wb = v;
+        load_window();
+        __syncthreads();
+      }
+      wait_vm<0>();   // the stages of visit v and the pairs of visit v + 2
+      bar();
+      const int R = sh.rounds[u];
+      reset(u2);
+      if (v + 3 < vhi) issue_entries(v + 3, ehalf(v + 3));
+      if (v + 1 < vhi) issue_visit(u1, v + 1);
+      for (int ks = 0; ks < nks; ++ks) {
+        for (int r = 0; r < R; ++r) {
+          if (r) drop_rows(vbuf(v, ks), u, r);
+          compute(vbuf(v, ks), none);
+        }
+      }
+      if (v + 2 < vhi) {
+        bar();   // every thread's reset of map u2 precedes the build
+        build(u2, v + 2, ehalf(v + 2));
+      }
+    }
+  } else {
   {
     const int64_t tl = v_token(vlo);
     StageCopy sc;
@@ -380,7 +429,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     bar();
     const int R = sh.rounds[u];
     reset(u2);
-    if (v + 2 < vhi) issue_entries(v + 2);
+    if (v + 2 < vhi) issue_entries(v + 2, 0);
     StageCopy sc;
     if (GP == 0) {
       sc.on = false;
@@ -401,7 +450,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
         bar();
         // map of visit v + 2: its pairs were copied during stage 0, before
         // the copies waited for above
-        if (ks == 3 && v + 2 < vhi) build(u2, v + 2);
+        if (ks == 3 && v + 2 < vhi) build(u2, v + 2, 0);
         if (GP == 0) {
           if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
         } else {
@@ -416,6 +465,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
         }
       }
     }
+  }
+
   }
 
   // ---- partial of this token range ----------------------------------------
@@ -443,8 +494,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char st2[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char st3[kStageBytes];
   __shared__ KbShared sh;
-  __shared__ int32_t e_pair[kEnt];   // pairs of the visit whose map is built next
-  __shared__ int32_t e_row[kEnt];
+  __shared__ int32_t e_pair[2 * kEnt];   // pairs of the visits whose maps are built next
+  __shared__ int32_t e_row[2 * kEnt];
 
   // XCD-aware unit order.  Workgroup b runs on XCD b % 8.  XCD x takes the
   // token ranges 16p + x and 16p + 15 - x (p = 0, 1, ...; a snake, so that

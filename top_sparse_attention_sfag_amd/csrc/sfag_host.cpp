@@ -332,11 +332,15 @@ extern "C" int sfag_workspace_size(
     return SFAG_OK;
   }
   // Tokens per chunk: the chunk's buffers (index rows, dS/P, and for the
-  // partials scatter the partial rows and the sort buffers) within a budget.
+  // partials scatter the partial rows and the sort buffers) within a budget
+  // (48 GiB by default: a sixth of one MI355X's 288 GB of HBM; fewer, larger
+  // chunks amortise each launch's tail — config 5 runs in 4 chunks instead
+  // of 10 at 16 GiB, 346 vs 355 ms, config 4 in one instead of two, 157 vs
+  // 171 ms).
   uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
   if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
   if (keyblock) per_tok += 8 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
-  const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 16384);
+  const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 49152);
   int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
   const int64_t forced = env_i64("SFAG_CHUNK_TOKENS", 0);
   if (forced > 0) chunk = forced;

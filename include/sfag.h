@@ -23,8 +23,9 @@
  *
  * Memory: every tensor and the workspace belong to the caller and live in
  * device memory (HBM) of the current HIP device; the library allocates and
- * frees no device memory and keeps no device state between calls.  Work is
- * enqueued asynchronously on the caller's stream.
+ * frees no device memory and keeps no device state between calls (apart from
+ * one auxiliary stream and two events per device, see sfag_backward).  Work
+ * is enqueued asynchronously on the caller's stream.
  */
 #ifndef SFAG_H
 #define SFAG_H
@@ -112,6 +113,11 @@ int sfag_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const 
  * consumed and freed, also on error.  Returns SFAG_OK once the work is
  * enqueued; errors found by the kernels are not reported (indices are bounds
  * checked on the device, so bad indices are masked, never dereferenced).
+ * With 32 <= N1 < 128 the dQ kernel runs on a second stream of the library's
+ * (one per device, default priority, made on first use) between an event
+ * recorded on `stream` and an event `stream` waits for, so every output is
+ * complete once `stream` reaches that point: the caller synchronizes `stream`
+ * only.  SFAG_CONCURRENT=0 keeps everything on `stream`.
  */
 int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
 

@@ -53,6 +53,7 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter) {
     carve(c, w.sort_hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
     carve(c, w.csr_off, (uint64_t)(d.T2 + 1) * 4);
   }
+  if (d.row_split > 1) carve(c, w.dq_acc, ch * (uint64_t)d.G * (d.D + d.Dr) * 4);
   if (keyblock) {
     const uint64_t n = ch * E;
     const uint64_t nblk = (n + kSortBlock - 1) / kSortBlock;
@@ -352,16 +353,26 @@ extern "C" int sfag_workspace_size(
     return fail(SFAG_ERR_TILING, "K * sparseBlockSize too large for 32-bit pair indices");
   }
   d.chunk = chunk;
+  // With few tokens (the fused token kernel, N1 <= 16, gives one workgroup
+  // per token) a token's positions are split over up to 4 workgroups, each
+  // at least 64 positions, which add their dQ|dQrope sums into an fp32
+  // buffer (config 1, 128 tokens: token kernel 0.200 ms unsplit, 0.126 ms in
+  // 4 shares, 0.140 ms in 8); SFAG_ROW_SPLIT overrides (at most 8).
+  if (d.Gp < 32) {
+    int64_t sp = std::min<int64_t>(4, std::min<int64_t>((1024 + chunk - 1) / chunk, d.E / 64));
+    sp = env_i64("SFAG_ROW_SPLIT", sp);
+    d.row_split = (int32_t)std::max<int64_t>(1, std::min<int64_t>(8, sp));
+  }
   d.nKB = (d.T2 + kKeyBlockRows - 1) / kKeyBlockRows;
   if (keyblock) {
     // 16 token ranges per chunk (the XCD snake pairs ranges x and 15 - x;
     // SFAG_KB_RANGES overrides the count), fewer when that would leave under
-    // 32 tokens per range or need more than 4 GiB of fp32 partials.  The
+    // 8 tokens per range or need more than 4 GiB of fp32 partials.  The
     // key-block sort key must fit in 31 bits.
     int64_t ntr = std::max<int64_t>(1, env_i64("SFAG_KB_RANGES", 16));
     const int64_t part_bytes = d.T2 * (2 * d.D + d.Dr) * 4;
     if (part_bytes > 0) ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, (4LL << 30) / part_bytes));
-    ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, chunk / 32));
+    ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, chunk / 8));
     d.TR = (chunk + ntr - 1) / ntr;
     d.nTR = (chunk + d.TR - 1) / d.TR;
     const int64_t sentinel = d.nKB * chunk;

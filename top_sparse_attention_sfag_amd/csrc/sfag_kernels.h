@@ -19,6 +19,8 @@ struct RowArgs {
   float scale_log2;  // scale·log2(e)
   float ds_scale;    // power of two applied to dS before its 16-bit rounding
   float dq_mul;      // scale / ds_scale
+  int32_t n_split;   // k_row: workgroups per token (>1: dQ sums go to dq_acc)
+  float* dq_acc;     // (ntok, G, 512 + Dr) fp32, zeroed, when n_split > 1
 };
 
 constexpr int kKeyBlock = kKeyBlockRows;
@@ -65,6 +67,8 @@ struct ColArgs {
 
 void launch_band_indices(int32_t* idx, int64_t T1, int64_t K, int32_t block, int32_t layout, int64_t S1, int64_t S2,
                          const int32_t* lq, const int32_t* lk, int32_t B, int64_t pre, int64_t nxt, hipStream_t s);
+void launch_dq_cast(int32_t dtype, const float* acc, int64_t t0, int64_t ntok, int64_t G, int32_t Dr, float mul,
+                    void* dq, void* dqr, hipStream_t s);
 void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int32_t* q_off, int32_t* kv_off,
                         hipStream_t s);
 void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, int64_t nrows, hipStream_t s);

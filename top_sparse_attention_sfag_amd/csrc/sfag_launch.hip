@@ -260,6 +260,8 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   ra.scale_log2 = plan->scale * kLog2e;
   ra.ds_scale = ds_scale;
   ra.dq_mul = plan->scale / ds_scale;
+  ra.n_split = 1;
+  ra.dq_acc = nullptr;
 
   ColArgs ca;
   ca.q = ra.q;
@@ -330,6 +332,14 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
         TimedScope ts("dq", s);
         launch_dq(plan->dtype, rope, ra, s);
       }
+    } else if (d.row_split > 1) {
+      // a token's positions over row_split workgroups: fp32 dQ sums, then a cast
+      ra.n_split = d.row_split;
+      ra.dq_acc = at<float>(workspace, w.dq_acc);
+      TimedScope ts("row", s);
+      launch_fill_u32(ra.dq_acc, (uint64_t)ntok * d.G * (d.D + d.Dr), 0u, s);
+      launch_row(plan->dtype, rope, ra, s);
+      launch_dq_cast(plan->dtype, ra.dq_acc, t0, ntok, d.G, (int32_t)d.Dr, ra.dq_mul, plan->dq, plan->dqr, s);
     } else {
       TimedScope ts("row", s);
       launch_row(plan->dtype, rope, ra, s);

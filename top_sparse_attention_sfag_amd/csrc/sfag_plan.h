@@ -40,6 +40,7 @@ struct WorkspaceLayout {
   uint64_t vis_key = 0;    // int32 (chunk*E): composite key of each visit
   uint64_t vis_er = 0;     // int32 (chunk*E): key row within its block of each sorted pair
   uint64_t vis_n = 0;      // int32: number of visits
+  uint64_t dq_acc = 0;     // fp32 (chunk, G, D + Dr): dQ|dQrope sums when a token's positions are split
   uint64_t total = 0;
 };
 
@@ -57,6 +58,7 @@ struct Dims {
   int64_t nKB = 0;         // key blocks of kKeyBlockRows rows
   int64_t TR = 0;          // tokens per range of the key-block kernel
   int64_t nTR = 0;         // token ranges per chunk
+  int32_t row_split = 1;   // workgroups sharing one token's positions in the fused token kernel
 };
 
 uint64_t align256(uint64_t x);

@@ -336,6 +336,22 @@ __global__ void __launch_bounds__(256) k_cast(const float* __restrict__ acc, int
   }
 }
 
+// dQ | dQrope of a chunk from the fp32 sums of a split token kernel:
+// dq[t0 + r / G][r % G] = RNE(acc[r] · mul), mul = scale / dS factor.
+template <typename TT>
+__global__ void __launch_bounds__(256) k_dq_cast(const float* __restrict__ acc, int64_t nrows, int64_t row0,
+                                                 int32_t Dr, float mul, uint16_t* __restrict__ dq,
+                                                 uint16_t* __restrict__ dqr) {
+  const int64_t W = 512 + Dr;
+  const int64_t n = nrows * W;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / W, c = i - r * W;
+    const uint16_t v = TT::from_f(acc[i] * mul);
+    if (c < 512) dq[(row0 + r) * 512 + c] = v;
+    else dqr[(row0 + r) * Dr + (c - 512)] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -481,6 +497,19 @@ void launch_cast(int32_t dtype, const float* acc, int64_t T2, int32_t D, int32_t
   else
     hipLaunchKernelGGL(k_cast<FP16>, grid, dim3(256), 0, s, acc, T2, D, Dr, kscale, (uint16_t*)dk, (uint16_t*)dkr,
                        (uint16_t*)dv);
+}
+
+void launch_dq_cast(int32_t dtype, const float* acc, int64_t t0, int64_t ntok, int64_t G, int32_t Dr, float mul,
+                    void* dq, void* dqr, hipStream_t s) {
+  const int64_t nrows = ntok * G;
+  if (nrows == 0) return;
+  const dim3 grid(grid_for((uint64_t)nrows * (512 + Dr), 1024, 8192));
+  if (dtype == SFAG_BF16)
+    hipLaunchKernelGGL(k_dq_cast<BF16>, grid, dim3(256), 0, s, acc, nrows, t0 * G, Dr, mul, (uint16_t*)dq,
+                       (uint16_t*)dqr);
+  else
+    hipLaunchKernelGGL(k_dq_cast<FP16>, grid, dim3(256), 0, s, acc, nrows, t0 * G, Dr, mul, (uint16_t*)dq,
+                       (uint16_t*)dqr);
 }
 
 void launch_band_indices(int32_t* idx, int64_t T1, int64_t K, int32_t block, int32_t layout, int64_t S1, int64_t S2,

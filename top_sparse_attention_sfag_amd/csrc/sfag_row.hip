@@ -71,7 +71,9 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
   const int b = blockIdx.x;
   const int xcd = b % kXcds, u = b / kXcds;
   const int hb = u % a.n_hb;
-  const int tq = u / a.n_hb;
+  const int rest = u / a.n_hb;
+  const int sp = rest % a.n_split;   // which share of the token's positions
+  const int tq = rest / a.n_split;
   const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
@@ -114,6 +116,13 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
 
   const int nv = a.nvalid[tl];
   const int32_t* rt = a.rows + tl * a.E;
+  // positions [cb, ce) of this workgroup: whole tiles, the last share ending at nv
+  int cb = 0, ce = nv;
+  if (a.n_split > 1) {
+    const int per = (((nv + a.n_split - 1) / a.n_split) + kTile - 1) / kTile * kTile;
+    cb = min(nv, sp * per);
+    ce = min(nv, cb + per);
+  }
 
   // Gather the 32 rows of tile c0 into buffer `buf`; rows past nv repeat a
   // valid row (their dS is exactly 0).  Wave w loads rows 8w..8w+7.
@@ -154,12 +163,12 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
     oTr[w] = r1 * (DR * 2) + 16 * ((2 * w + half) ^ x1) + hoff;
   }
 
-  if (nv > 0) issue_tile(0, 0);
+  if (cb < ce) issue_tile(cb, 0);
   int cur = 0;
-  for (int c0 = 0; c0 < nv; c0 += kTile) {
+  for (int c0 = cb; c0 < ce; c0 += kTile) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (c0 + kTile < nv) issue_tile(c0 + kTile, cur ^ 1);
+    if (c0 + kTile < ce) issue_tile(c0 + kTile, cur ^ 1);
     const unsigned char* Km = smem + cur * BUF;
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
@@ -278,6 +287,19 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
     cur ^= 1;
   }
   if (!wave_on) return;
+  if (a.n_split > 1) {
+    // this share's dQ|dQrope sums, unscaled; the cast kernel scales and rounds
+    if (cb >= ce) return;
+#pragma unroll
+    for (int nb = 0; nb < NB_Q; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = h0 + 4 * g + i;
+        if (hh < a.G) atomicAdd(a.dq_acc + (tl * a.G + hh) * DQK + 16 * nb + n, acc[nb][i]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB_Q; ++nb) {
 #pragma unroll
@@ -297,7 +319,7 @@ void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s) {
   if (a.ntok == 0) return;
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a.ntok + per - 1) / per * per;
-  const dim3 grid((unsigned)(padded * a.n_hb)), block(256);
+  const dim3 grid((unsigned)(padded * a.n_hb * a.n_split)), block(256);
   // value passed as the key tensor itself: gather each row once
   const bool vk = a.v == a.k;
   if (dtype == SFAG_BF16) {

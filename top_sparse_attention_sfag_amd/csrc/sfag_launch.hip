@@ -262,6 +262,9 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   ra.dq_mul = plan->scale / ds_scale;
   ra.n_split = 1;
   ra.dq_acc = nullptr;
+  // causal rows grow with the token: longest tokens first (SFAG_TOKEN_ORDER=fwd|rev overrides)
+  ra.reverse = d.mode == 3 ? 1 : 0;
+  if (const char* to = std::getenv("SFAG_TOKEN_ORDER")) ra.reverse = std::string(to) == "rev" ? 1 : 0;
 
   ColArgs ca;
   ca.q = ra.q;

@@ -75,11 +75,17 @@ __device__ __forceinline__ f32x16 mfma32<FP16>(f16x8 a, f16x8 b, f32x16 c) {
 
 // Maps a block index to (token of the chunk, head block): each XCD takes runs
 // of kRun consecutive tokens.
-__device__ __forceinline__ int64_t unit_token(int b, int n_hb, int& hb) {
+// With `reverse` the last tokens of the chunk come first (under the causal
+// mask they hold the most positions, so the longest units start first and the
+// shortest fill the end).
+__device__ __forceinline__ int64_t unit_token(int b, int n_hb, int& hb, int64_t ntok, int reverse) {
   const int xcd = b % kXcds, u = b / kXcds;
   hb = u % n_hb;
   const int tq = u / n_hb;
-  return ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  if (!reverse) return tl;
+  const int64_t padded = (ntok + kXcds * kRun - 1) / (kXcds * kRun) * (kXcds * kRun);
+  return padded - 1 - tl;
 }
 
 // Row indices of a tile: lane r & 31 holds the key row of position c0 + r
@@ -151,7 +157,7 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   constexpr int nw = NW;
   const int HB = 32 * nw;
   int hb;
-  const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb);
+  const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb, a.ntok, a.reverse);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -440,7 +446,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
 
   int hb;
-  const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb);
+  const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb, a.ntok, a.reverse);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;

@@ -357,8 +357,10 @@ extern "C" int sfag_workspace_size(
   // per token) a token's positions are split over up to 4 workgroups, each
   // at least 64 positions, which add their dQ|dQrope sums into an fp32
   // buffer (config 1, 128 tokens: token kernel 0.200 ms unsplit, 0.126 ms in
-  // 4 shares, 0.140 ms in 8); SFAG_ROW_SPLIT overrides (at most 8).
-  if (d.Gp < 32) {
+  // 4 shares, 0.140 ms in 8); SFAG_ROW_SPLIT overrides (at most 8).  The
+  // shares' atomic sums have no fixed order, so deterministic calls never
+  // split.
+  if (d.Gp < 32 && !deterministic) {
     int64_t sp = std::min<int64_t>(4, std::min<int64_t>((1024 + chunk - 1) / chunk, d.E / 64));
     sp = env_i64("SFAG_ROW_SPLIT", sp);
     d.row_split = (int32_t)std::max<int64_t>(1, std::min<int64_t>(8, sp));

@@ -316,7 +316,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       if (h + 1 < 4) rd(h + 1, av[(h + 1) & 1]);
-      if (GP != 0) issue_part(sc, h);
+      issue_part(sc, h);   // nothing unless the caller prepared copies
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -368,8 +368,6 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     // v + 1: the top-of-visit wait covers both kinds of copies, each issued a
     // whole visit earlier.
     auto ehalf = [&](int64_t v) -> int { return (int)((v - vlo) & 1); };
-    StageCopy none;
-    none.on = false;
     if (vlo + 2 < vhi) issue_entries(vlo + 2, ehalf(vlo + 2));
     issue_visit(0, vlo);
     for (int64_t v = vlo; v < vhi; ++v) {
@@ -386,11 +384,17 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       const int R = sh.rounds[u];
       reset(u2);
       if (v + 3 < vhi) issue_entries(v + 3, ehalf(v + 3));
-      if (v + 1 < vhi) issue_visit(u1, v + 1);
+      // stage ks of visit v + 1 is copied between the MFMAs of stage ks of
+      // visit v (a burst of copies stalls the issuing wave)
+      const bool nxt = v + 1 < vhi;
+      const int64_t tl1 = nxt ? v_token(v + 1) : 0;
       for (int ks = 0; ks < nks; ++ks) {
+        StageCopy sc;
+        prep_stage(sc, nxt, u1, tl1, ks, vlds(v + 1, ks));
         for (int r = 0; r < R; ++r) {
           if (r) drop_rows(vbuf(v, ks), u, r);
-          compute(vbuf(v, ks), none);
+          compute(vbuf(v, ks), sc);
+          sc.on = false;   // the copies go out during the first round
         }
       }
       if (v + 2 < vhi) {

@@ -352,7 +352,48 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   }
   __syncthreads();
 
-  if (GP == 0 && nks <= 2) {
+  if (GP == 0 && nks == 1) {
+    // Up to 32 heads (one stage per visit): the four stage buffers rotate over
+    // visits and stage copies run two visits ahead.  At the top of visit v
+    // the map of visit v + 2 is built (its pairs were copied a visit ago) and
+    // its stage is copied between the MFMAs of visit v; the pairs of visit
+    // v + 3 are copied at the same time.  Each visit waits once, for copies
+    // issued one and two visits earlier.
+    auto rbuf = [&](int64_t v) -> unsigned char* { return stage_buf((int)((v - vlo) & 3)); };
+    auto rlds = [&](int64_t v) -> uint32_t { return stage_lds((int)((v - vlo) & 3)); };
+    auto ehalf = [&](int64_t v) -> int { return (int)((v - vlo) & 1); };
+    // issue order: stage(vlo), pairs(vlo + 2), stage(vlo + 1)
+    issue_stage(0, v_token(vlo), 0, rlds(vlo));
+    if (vlo + 2 < vhi) issue_entries(vlo + 2, ehalf(vlo + 2));
+    if (vlo + 1 < vhi) issue_stage(1, v_token(vlo + 1), 0, rlds(vlo + 1));
+    for (int64_t v = vlo; v < vhi; ++v) {
+      const int u = (int)((v - vlo) % 3);
+      const int u2 = u == 0 ? 2 : u - 1;   // map slot of visit v + 2
+      if (v - wb + 3 > kWin) {   // visits v .. v + 3 leave the window
+        __syncthreads();
+        wb = v;
+        load_window();
+        __syncthreads();
+      }
+      // stage(v) and pairs(v + 2) have landed once at most stage(v + 1),
+      // issued after them, is outstanding
+      if (v + 1 < vhi) wait_vm<K>();
+      else wait_vm<0>();
+      bar();
+      const int R = sh.rounds[u];
+      if (v + 3 < vhi) issue_entries(v + 3, ehalf(v + 3));
+      if (v + 2 < vhi) build(u2, v + 2, ehalf(v + 2));   // slot u2 was cleared after visit v - 1
+      bar();
+      StageCopy sc;
+      prep_stage(sc, v + 2 < vhi, u2, v + 2 < vhi ? v_token(v + 2) : 0, 0, rlds(v + 2));
+      for (int r = 0; r < R; ++r) {
+        if (r) drop_rows(rbuf(v), u, r);
+        compute(rbuf(v), sc);
+        sc.on = false;
+      }
+      reset(u);   // this visit's map slot, for visit v + 3
+    }
+  } else if (GP == 0 && nks <= 2) {
     // Up to 64 heads (one or two 32-head stages per visit): visits alternate
     // between the buffer pairs st0|st1 and st2|st3; the stages of visit v + 1
     // are copied while visit v is computed (its slot map was built a visit

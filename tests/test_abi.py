@@ -206,3 +206,22 @@ def test_band_entries_and_argument_errors():
     assert call(dummy, null, null, 0, 0, 0, 4, 8, 1, 1, 0, 0, null) == sfag.ERR_TILING        # TND B = 0
     assert call(dummy, null, null, 2, 0, 0, 4, 8, 1, 1, 0, 0, null) == sfag.ERR_NULLPTR       # TND lengths
     assert call(null, null, null, 1, 8, 8, 8, 8, 1, 0, 0, 0, null) == sfag.ERR_NULLPTR        # output
+
+
+def test_few_token_split_needs_a_dq_buffer_only_when_not_deterministic():
+    """Phase 1 plans the few-token split of the fused token kernel (N1 <= 16)
+    with an fp32 dQ|dQrope buffer of chunk x N1 x (512 + Dr) floats; a
+    deterministic call never splits, so its workspace lacks exactly that."""
+    t = _tensors("BSND", B=1, S1=8, S2=400, G=4, Dr=64, K=256)
+    ws_split, p = _plan(t)
+    sfag.destroy(p)
+    ws_det, p = _plan(t, deterministic=True)
+    sfag.destroy(p)
+    assert ws_split - ws_det == 8 * 4 * (512 + 64) * 4
+    # many heads: the split kernel is not used, the workspaces are equal
+    t = _tensors("BSND", B=1, S1=8, S2=400, G=64, Dr=64, K=256)
+    a, p = _plan(t)
+    sfag.destroy(p)
+    b, p = _plan(t, deterministic=True)
+    sfag.destroy(p)
+    assert a == b

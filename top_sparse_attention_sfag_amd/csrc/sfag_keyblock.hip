@@ -325,12 +325,47 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     }
   };
 
+  // The same for 16 heads (Gp = 16: the upper half of every stage row is
+  // zero): v_mfma_f32_16x16x16 over the 16 live heads, half the MFMA work
+  // and half the operand reads.  Lane group g takes heads 4g .. 4g + 3, the
+  // 8-byte half g & 1 of 16-byte chunk g >> 1.
+  auto compute16 = [&](const unsigned char* st, const StageCopy& sc) {
+    typedef typename TT::vec4 V4;
+    const int ch = g >> 1, hoff = (g & 1) << 3;
+    const int po = ((ch ^ (n >> 2)) << 4) + hoff;
+    V4 Bf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = bcol + 16 * nb;
+      Bf[nb] = __builtin_bit_cast(V4, *(const uint2*)(st + kStageA + col * 64 + ((ch ^ ((col >> 2) & 3)) << 4) + hoff));
+    }
+    uint2 av[2][4];
+    auto rd = [&](int h, uint2 (&dst)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mb = 4 * h + j;
+        dst[j] = *(const uint2*)(st + (mb * 16 + n) * 64 + po);
+      }
+    };
+    rd(0, av[0]);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (h + 1 < 4) rd(h + 1, av[(h + 1) & 1]);
+      issue_part(sc, h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          C[4 * h + j][nb] = TT::mfma16(__builtin_bit_cast(V4, av[h & 1][j]), Bf[nb], C[4 * h + j][nb]);
+    }
+  };
+
   const int64_t nst = 4 * (vhi - vlo);   // stages
   // before stage s: wait for its copies; everything issued after them is the
   // copies of the (up to) two following stages and pair copies
   auto wait_stage = [&](int64_t s) {
     const int later = (s + 1 < nst ? 1 : 0) + (s + 2 < nst ? 1 : 0);
-    if (GP == 0 || later == 0) wait_vm<0>();
+    if (GP != 128 || later == 0) wait_vm<0>();
     else if (later == 2) wait_vm<2 * K>();
     else wait_vm<K>();
   };
@@ -352,7 +387,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   }
   __syncthreads();
 
-  if (GP == 0 && nks == 1) {
+  if (GP != 128 && nks == 1) {
     // Up to 32 heads (one stage per visit): the four stage buffers rotate over
     // visits and stage copies run two visits ahead.  At the top of visit v
     // the map of visit v + 2 is built (its pairs were copied a visit ago) and
@@ -388,12 +423,13 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       prep_stage(sc, v + 2 < vhi, u2, v + 2 < vhi ? v_token(v + 2) : 0, 0, rlds(v + 2));
       for (int r = 0; r < R; ++r) {
         if (r) drop_rows(rbuf(v), u, r);
-        compute(rbuf(v), sc);
+        if constexpr (GP == 16) compute16(rbuf(v), sc);
+        else compute(rbuf(v), sc);
         sc.on = false;
       }
       reset(u);   // this visit's map slot, for visit v + 3
     }
-  } else if (GP == 0 && nks <= 2) {
+  } else if (GP != 128 && nks <= 2) {
     // Up to 64 heads (one or two 32-head stages per visit): visits alternate
     // between the buffer pairs st0|st1 and st2|st3; the stages of visit v + 1
     // are copied while visit v is computed (its slot map was built a visit
@@ -476,7 +512,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     reset(u2);
     if (v + 2 < vhi) issue_entries(v + 2, 0);
     StageCopy sc;
-    if (GP == 0) {
+    if (GP != 128) {
       sc.on = false;
       if (nks > 3) issue_stage(u, tl, 3, L3);
     } else {
@@ -490,13 +526,13 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     // stages 1 .. 3: each issues the copy of the next visit's stage ks - 1
 #pragma unroll
     for (int ks = 1; ks < 4; ++ks) {
-      if (ks < nks || GP == 0) {
+      if (ks < nks || GP != 128) {
         wait_stage(s + ks);
         bar();
         // map of visit v + 2: its pairs were copied during stage 0, before
         // the copies waited for above
         if (ks == 3 && v + 2 < vhi) build(u2, v + 2, 0);
-        if (GP == 0) {
+        if (GP != 128) {
           if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
         } else {
           prep_stage(sc, more, u1, tl1, ks - 1, stage_lds(ks - 1));
@@ -532,7 +568,10 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 
 }  // namespace
 
-template <typename TT>
+// GPK = 16: the 16-head variant only (its own kernel, so that its operand
+// registers do not weigh on the other variants' allocation); 0: Gp = 128 or
+// the generic path, chosen from the arguments.
+template <typename TT, int GPK>
 __global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char st1[kStageBytes];
@@ -562,7 +601,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
   const int64_t vhi = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_hi));
   if (threadIdx.x == 0 && cb == 0) a.nonempty[(int64_t)tr * a.nKB + kb] = vhi > vlo ? 1 : 0;
   if (vhi <= vlo) return;
-  if (a.Gp == 128) {
+  if constexpr (GPK == 16) {
+    if (c.width == 256) kb_block<TT, 4, 16>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 16>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+  } else if (a.Gp == 128) {
     if (c.width == 256) kb_block<TT, 4, 128>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
     else kb_block<TT, 3, 128>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   } else {
@@ -683,8 +725,13 @@ void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s) {
   // token ranges per XCD: two per group of 16 (see the unit order above)
   const int64_t per_xcd = 2 * (((int64_t)a.nTR + 15) / 16);
   const dim3 grid((unsigned)(kXcds * per_xcd * a.nKB * a.nCB)), block(kThreads);
-  if (dtype == SFAG_BF16) hipLaunchKernelGGL(k_keyblock<BF16>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_keyblock<FP16>, grid, block, 0, s, a);
+  if (a.Gp == 16) {
+    if (dtype == SFAG_BF16) hipLaunchKernelGGL((k_keyblock<BF16, 16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_keyblock<FP16, 16>), grid, block, 0, s, a);
+  } else {
+    if (dtype == SFAG_BF16) hipLaunchKernelGGL((k_keyblock<BF16, 0>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_keyblock<FP16, 0>), grid, block, 0, s, a);
+  }
 }
 
 void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows, int64_t n, int64_t ntok,

@@ -295,7 +295,7 @@ def main(argv=None):
     if args.summarize_profiles:
         return _summarize_profiles(args.summarize_profiles, args.config, args.calib_copy_mb)
     if args.gpus != 1:
-        print("bench.py measures a single GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures a single GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
 

@@ -335,9 +335,9 @@ extern "C" int sfag_workspace_size(
   // Tokens per chunk: the chunk's buffers (index rows, dS/P, and for the
   // partials scatter the partial rows and the sort buffers) within a budget
   // (48 GiB by default: a sixth of one MI355X's 288 GB of HBM; fewer, larger
-  // chunks amortise each launch's tail — config 5 runs in 4 chunks instead
-  // of 10 at 16 GiB, 346 vs 355 ms, config 4 in one instead of two, 157 vs
-  // 171 ms).
+  // chunks amortise each launch's tail — 128 heads, 32768 tokens, top-8192:
+  // 4 chunks instead of 10 at 16 GiB, 346 vs 355 ms; 16 heads, 2 x 16384
+  // tokens, 512 blocks of 16: one chunk instead of two, 157 vs 171 ms).
   uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
   if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
   if (keyblock) per_tok += 8 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
@@ -356,8 +356,9 @@ extern "C" int sfag_workspace_size(
   // With few tokens (the fused token kernel, N1 <= 16, gives one workgroup
   // per token) a token's positions are split over up to 4 workgroups, each
   // at least 64 positions, which add their dQ|dQrope sums into an fp32
-  // buffer (config 1, 128 tokens: token kernel 0.200 ms unsplit, 0.126 ms in
-  // 4 shares, 0.140 ms in 8); SFAG_ROW_SPLIT overrides (at most 8).  The
+  // buffer (4 heads, 128 tokens, top-1024 of 2048 keys: token kernel 0.200
+  // ms unsplit, 0.126 ms in 4 shares, 0.140 ms in 8); SFAG_ROW_SPLIT
+  // overrides (at most 8).  The
   // shares' atomic sums have no fixed order, so deterministic calls never
   // split.
   if (d.Gp < 32 && !deterministic) {

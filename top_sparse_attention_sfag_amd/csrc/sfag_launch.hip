@@ -291,9 +291,9 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   }
 
   // k_dq on a second stream beside the key-block kernels when the head count
-  // is below 128 (measured: config 3, 64 heads, 10.8 -> 9.6 ms; with 128
-  // heads no gain at 4096 tokens and +3% at 32768); SFAG_CONCURRENT=0|1
-  // overrides.
+  // is below 128 (measured: 64 heads, 8192 varlen tokens, top-2048 causal,
+  // 10.8 -> 9.6 ms; with 128 heads no gain at 4096 tokens and +3% at 32768);
+  // SFAG_CONCURRENT=0|1 overrides.
   bool concurrent = d.Gp < 128;
   if (const char* cc = std::getenv("SFAG_CONCURRENT")) concurrent = std::string(cc) == "1";
   const SideStream* side = concurrent ? side_stream() : nullptr;

@@ -225,3 +225,17 @@ def test_few_token_split_needs_a_dq_buffer_only_when_not_deterministic():
     b, p = _plan(t, deterministic=True)
     sfag.destroy(p)
     assert a == b
+
+
+def test_band_entries_match_the_oracle_count():
+    """sfag_band_entries (host C) against the oracle's band_entries over a
+    grid of key lengths, windows and block sizes, including unbounded ones."""
+    from oracle import sfag_oracle as orc
+    L = sfag.lib()
+    big = 2147483647
+    for lk in (1, 2, 7, 16, 33, 100, 4096, 131072):
+        for pre in (0, 1, 5, 63, 1023, big):
+            for nxt in (0, 3, 64, big):
+                for block in (1, 8, 16, 64):
+                    assert L.sfag_band_entries(lk, pre, nxt, block) == orc.band_entries(lk, pre, nxt, block), \
+                        (lk, pre, nxt, block)

@@ -2,16 +2,24 @@
 """Throughput of the sparse flash attention backward on one MI355X.
 
 One step = one full backward call (index decode, Delta, accumulator fill, the
-MFMA kernels, the dK/dV scatter or key-centric reduction, and the cast) over
-one batch of synthetic inputs already resident in HBM.  The default workload
-is the DSA-style training shape: BSND, B=1, S1=S2=4096, N1=128 heads sharing
-one key/value head, D=512 plus a 64-wide rope part, K=2048 causal top-k
-indices (25% local window, 75% uniform), bf16.
+MFMA kernels, the dK/dV key-centric reduction, and the cast) over one batch of
+synthetic inputs already resident in HBM.  The headline workload is the
+DSA-style training shape: BSND, B=1, S1=S2=4096, N1=128 heads sharing one
+key/value head, D=512 plus a 64-wide rope part, K=2048 causal top-k indices
+(25% local window, 75% uniform), bf16.  By default the other four workloads
+(4 heads x 128 tokens x top-1024 of 2048; TND 64 heads x 8192 varlen tokens;
+16 heads x 2 x 16384 tokens x 512 blocks of 16, fp16, no rope; 128 heads x
+32768 tokens x top-8192 Zipf, deterministic) are timed in the same run and
+reported under "configs".
+
+out / softmaxMax / softmaxSum come from the library's own forward pass over
+the same inputs, outside the timed region.
 
 Prints one JSON line with the whole-job TFLOP/s (5504 flop per valid
 (head, selected position) pair, 5120 without rope), the roofline of the
-dominant kernel measured with HIP events inside the timed region, and the CPU
-oracle timed on a bounded sample of the same workload.
+dominant kernel measured with HIP events inside the timed region, HBM bytes
+from the committed rocprofv3 counter summary when it matches the sources,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -67,18 +75,19 @@ def _unit_flops(case, kernel):
 
 def _kernel_bytes(case, kernel, n_pairs):
     """Algorithmic HBM bytes of one step of a kernel group: every operand read
-    once and every result written once (no re-reads)."""
+    once and every result written once (no re-reads; a key row gathered by
+    many tokens counts once)."""
     e = 2
     G, D, Dr, T1, T2 = case.G, case.D, case.Dr, case.T1, case.T2
     if kernel == "row":
-        # Q, Qrope, dO, stats, indices in; dQ, dQrope out; per pair the
-        # gathered K|Krope|V row in and the 16-bit dS and P out.
-        return (T1 * (G * (2 * (D + Dr) + D) * e + G * 12 + case.Kent * 4)
-                + n_pairs * ((2 * D + Dr) * e + 2 * G * e))
+        # Q, Qrope, dO, stats, Delta, indices in; dQ, dQrope out; the K|Krope|V
+        # tables in; per pair the 16-bit dS and P out.
+        return (T1 * (G * (2 * (D + Dr) + D) * e + G * 12 + case.Kent * 4) + T2 * (2 * D + Dr) * e
+                + n_pairs * 2 * G * e)
     if kernel == "fwd":
-        # Q, Qrope, indices in; out and the two statistics out; per pair the
-        # gathered K|Krope|V row in.
-        return T1 * (G * (2 * D + Dr) * e + G * 8 + case.Kent * 4) + n_pairs * (2 * D + Dr) * e
+        # Q, Qrope, indices in; out and the two statistics out; the K|Krope|V
+        # tables in.
+        return T1 * (G * (2 * D + Dr) * e + G * 8 + case.Kent * 4) + T2 * (2 * D + Dr) * e
     if kernel == "keyblock":
         # per pair dS and P in; per token Q|Qrope and dO in; per key the fp32
         # dK|dKrope|dV partial out.
@@ -87,6 +96,9 @@ def _kernel_bytes(case, kernel, n_pairs):
 
 
 def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
+    """Algorithmic work of one launch of ``kernel`` over its average duration:
+    flops against the bf16/fp16 MFMA peak for the MFMA kernels at N1 >= 32,
+    otherwise the bytes each operand needs once against the HBM peak."""
     uf = _unit_flops(case, kernel)
     if uf is not None and case.G >= 32:
         achieved = n_pairs * case.G * uf / launches_per_step / (kernel_ms * 1e-3) / 1e12
@@ -98,43 +110,39 @@ def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
     return roof
 
 
-def _traffic(case, kernel):
-    """HBM bytes per launch of ``kernel`` from the committed counter summary of
-    this workload (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
-    calibration), or None when there is none or the kernel's sources have
-    changed since the counters were taken."""
+# Kernel groups of the timing API and the kernels (by demangled name) each
+# one stands for.
+_GROUPS = {
+    "sdp": r"k_sdp<", "dq": r"k_dq<", "row": r"k_row<", "keyblock": r"k_keyblock<", "transpose": r"k_transpose",
+    "col": r"k_col<", "fwd": r"k_fwd<", "kb_reduce": r"k_kb_reduce", "cast": r"k_cast<", "decode": r"k_decode",
+    "delta": r"k_delta<",
+}
+_SOURCES = ["include/sfag.h", "top_sparse_attention_sfag_amd/build.py"]
+
+
+def _sources_sha256():
+    """One hash over every source the library is built from."""
     import hashlib
+    csrc = os.path.join(ROOT, "top_sparse_attention_sfag_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)) + _SOURCES:
+        path = os.path.join(csrc, f) if "/" not in f else os.path.join(ROOT, f)
+        with open(path, "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def _traffic_record(case):
+    """The committed counter summary of this workload when it was taken from
+    the current sources, else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    k = rec.get("kernels", {}).get(kernel)
-    if not k:
+    if rec.get("sources_sha256") != _sources_sha256():
         return None
-    h = hashlib.sha256()
-    for src in k["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != k["sources_sha256"]:
-        return None
-    return k["bytes_per_launch"]
-
-
-# Kernel groups of the timing API and the kernels (by demangled name) and
-# sources each one stands for.
-_CSRC = "top_sparse_attention_sfag_amd/csrc/"
-_COMMON = [_CSRC + "sfag_kernels.h", _CSRC + "sfag_device.h", _CSRC + "sfag_plan.h",
-           "top_sparse_attention_sfag_amd/build.py"]
-_GROUPS = {
-    "sdp": (r"k_sdp<", [_CSRC + "sfag_sdp.hip"]),
-    "dq": (r"k_dq<", [_CSRC + "sfag_sdp.hip"]),
-    "row": (r"k_row<", [_CSRC + "sfag_row.hip"]),
-    "keyblock": (r"k_keyblock<", [_CSRC + "sfag_keyblock.hip"]),
-    "transpose": (r"k_transpose", [_CSRC + "sfag_keyblock.hip"]),
-    "col": (r"k_col<", [_CSRC + "sfag_mfma.hip"]),
-    "fwd": (r"k_fwd<", [_CSRC + "sfag_fwd.hip"]),
-}
+    return rec
 
 
 def _read_csvs(root, suffix):
@@ -149,13 +157,26 @@ def _read_csvs(root, suffix):
 
 
 def _summarize_profiles(d, config, calib_mb):
-    """Turn rocprofv3 CSV output (``-f csv``) into the committed summaries:
-    profiles/<workload>_kernel_stats.txt (kernel trace statistics) and
-    profiles/traffic_<workload>.json (HBM bytes per launch from FETCH_SIZE
-    and WRITE_SIZE, scaled by what the same counters read for one plain
-    elementwise copy of ``calib_mb`` MiB)."""
-    import hashlib
+    """Turn rocprofv3 CSV output (``-f csv``) under d/{trace,rd,wr,mfma} into
+    the committed summaries:
+
+    * profiles/<workload>_kernel_stats.txt: kernel trace statistics of the
+      backward kernels, and, when d/mfma holds SQ_VALU_MFMA_BUSY_CYCLES and
+      GRBM_GUI_ACTIVE, each kernel's MFMA-busy fraction (busy cycles summed
+      over the 1024 SIMDs over 1024 x its active cycles);
+    * profiles/traffic_<workload>.json: HBM-side bytes per launch and per step
+      from the TCC-to-memory request counters, read bytes = 32 x
+      TCC_EA0_RDREQ_32B + 64 x TCC_EA0_RDREQ_64B + 128 x TCC_EA0_RDREQ_128B
+      and write bytes = 64 x TCC_EA0_WRREQ_64B + 32 x (TCC_EA0_WRREQ -
+      TCC_EA0_WRREQ_64B) (summed over every TCC instance); the elementwise
+      copy of ``calib_mb`` MiB and the read-only sum over the same tensor that
+      bench.py launches first are recorded beside them as a check.
+
+    The backward steps of a counter run are the dispatches between the first
+    and the last k_cast (one per backward call; the forward pass and the index
+    count that make the inputs run before the first call)."""
     import re
+    from collections import defaultdict
 
     import sfag_inputs as si
     case = si.CONFIGS[config]
@@ -164,67 +185,112 @@ def _summarize_profiles(d, config, calib_mb):
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
 
+    def dispatches(kind):
+        """{dispatch id: (kernel name, {counter: value})} of one counter run."""
+        out = {}
+        for r in _read_csvs(os.path.join(d, kind), "counter_collection.csv"):
+            i = int(r["Dispatch_Id"])
+            name = r["Counter_Name"].replace("_sum", "")
+            out.setdefault(i, (r["Kernel_Name"], defaultdict(float)))[1][name] += float(r["Counter_Value"])
+        return out
+
+    def window(disp):
+        ids = sorted(i for i, (k, _c) in disp.items() if "k_cast<" in k)
+        if len(ids) < 2:
+            return {}, 0
+        return {i: v for i, v in disp.items() if ids[0] < i <= ids[-1]}, len(ids) - 1
+
+    rd_bytes = lambda c: 32 * c["TCC_EA0_RDREQ_32B"] + 64 * c["TCC_EA0_RDREQ_64B"] + 128 * c["TCC_EA0_RDREQ_128B"]
+    wr_bytes = lambda c: 64 * c["TCC_EA0_WRREQ_64B"] + 32 * (c["TCC_EA0_WRREQ"] - c["TCC_EA0_WRREQ_64B"])
+
+    # MFMA busy per kernel group
+    mfma = {}
+    md, nm = window(dispatches("mfma"))
+    for g, pat in _GROUPS.items():
+        rows = [c for k, c in md.values() if re.search(pat, k)]
+        if rows and all("GRBM_GUI_ACTIVE" in c for c in rows):
+            busy = sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for c in rows)
+            act = sum(c["GRBM_GUI_ACTIVE"] for c in rows)
+            mfma[g] = busy / (act * 1024) if act else None
+
     stats = _read_csvs(os.path.join(d, "trace"), "kernel_stats.csv")
     lines = [f"# rocprofv3 kernel statistics: {case.name}", "",
-             "Commands (from the repository root; OUT is an output directory):", "", cmds,
-             f"python3 bench.py --summarize-profiles $OUT --config {config} --calib-copy-mb {calib_mb}", "",
-             f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'total ms':>10} {'%':>6}"]
+             "Commands (from the repository root; OUT is an output directory):", "", cmds, "",
+             f"{'kernel':<64} {'calls':>6} {'avg us':>10} {'total ms':>10} {'%':>6} {'MFMA busy':>9}"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         name = r["Name"]
         if "sfag" not in name:
             continue
-        lines.append(f"{name[:72]:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
-                     f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f}")
+        g = next((g for g, pat in _GROUPS.items() if re.search(pat, name)), None)
+        mb = f"{mfma[g]:.3f}" if g in mfma and mfma[g] is not None else "-"
+        lines.append(f"{name[:64]:<64} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f} {mb:>9}")
     with open(os.path.join(out_dir, f"{case.name}_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    def per_kernel(kind):
-        acc = {}
-        for r in _read_csvs(os.path.join(d, kind), "counter_collection.csv"):
-            if r.get("Counter_Name") not in ("FETCH_SIZE", "WRITE_SIZE"):
-                continue
-            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return acc
-
-    fetch, write = per_kernel("fetch"), per_kernel("write")
-    traffic = {"workload": case.name, "commands": cmds, "calibration": None, "kernels": {}}
+    rd_all, wr_all = dispatches("rd"), dispatches("wr")
+    traffic = {"workload": case.name, "commands": cmds, "sources_sha256": _sources_sha256(), "calibration": None,
+               "kernels": {}, "step": None, "mfma_busy": mfma or None}
     if calib_mb:
-        # the calibration copy: the elementwise add that bench.py launches
-        cand = [(max(v), k) for k, v in fetch.items() if "CUDAFunctorOnSelf_add<int>" in k]
-        wc = [(max(v), k) for k, v in write.items() if "CUDAFunctorOnSelf_add<int>" in k]
-        if cand and wc:
-            kib = calib_mb * 1024.0
-            ff, fk = max(cand)
-            wf, wk = max(wc)
-            traffic["calibration"] = dict(copy_MiB=calib_mb, kernel=fk[:120], fetch_KiB=ff, write_KiB=wf,
-                                          fetch_factor=kib / ff, write_factor=kib / wf)
-    cal = traffic["calibration"] or dict(fetch_factor=1.0, write_factor=1.0)
-    for g, (pat, srcs) in _GROUPS.items():
-        fv = [v for k, vs in fetch.items() if re.search(pat, k) for v in vs]
-        wv = [v for k, vs in write.items() if re.search(pat, k) for v in vs]
-        if not fv or not wv:
+        want = calib_mb * 1048576.0
+        cp_r = [rd_bytes(c) for k, c in rd_all.values() if "CUDAFunctorOnSelf_add<int>" in k]
+        cp_w = [wr_bytes(c) for k, c in wr_all.values() if "CUDAFunctorOnSelf_add<int>" in k]
+        sm_r = [rd_bytes(c) for k, c in rd_all.values() if "reduce_kernel" in k]
+        traffic["calibration"] = dict(bytes=want, copy_read=max(cp_r) if cp_r else None,
+                                      copy_write=max(cp_w) if cp_w else None,
+                                      sum_read=max(sm_r) if sm_r else None)
+    rw, nr = window(rd_all)
+    ww, nw = window(wr_all)
+    for g, pat in _GROUPS.items():
+        rv = [rd_bytes(c) for k, c in rw.values() if re.search(pat, k)]
+        wv = [wr_bytes(c) for k, c in ww.values() if re.search(pat, k)]
+        if not rv or not wv:
             continue
-        h = hashlib.sha256()
-        for src in srcs + _COMMON:
-            with open(os.path.join(ROOT, src), "rb") as fh:
-                h.update(fh.read())
-        fb = sum(fv) / len(fv) * 1024 * cal["fetch_factor"]
-        wb = sum(wv) / len(wv) * 1024 * cal["write_factor"]
-        traffic["kernels"][g] = dict(dispatches=len(fv), fetch_bytes=fb, write_bytes=wb, bytes_per_launch=fb + wb,
-                                     sources=srcs + _COMMON, sources_sha256=h.hexdigest())
+        traffic["kernels"][g] = dict(launches_per_step=len(rv) / nr, read_bytes=sum(rv) / len(rv),
+                                     write_bytes=sum(wv) / len(wv),
+                                     bytes_per_launch=sum(rv) / len(rv) + sum(wv) / len(wv))
+    if nr and nw:
+        sr = sum(rd_bytes(c) for k, c in rw.values() if "sfag" in k) / nr
+        sw = sum(wr_bytes(c) for k, c in ww.values() if "sfag" in k) / nw
+        traffic["step"] = dict(steps=nr, read_bytes=sr, write_bytes=sw, bytes=sr + sw)
     with open(os.path.join(out_dir, f"traffic_{case.name}.json"), "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
     print("\n".join(lines))
     print(json.dumps({g: round(v["bytes_per_launch"] / 1e9, 3) for g, v in traffic["kernels"].items()}))
+    if traffic["step"]:
+        print(f"step bytes {traffic['step']['bytes'] / 1e9:.3f} GB")
+    print("calibration", traffic["calibration"])
     return 0
 
 
-def _cpu_baseline(case, inp, seed, target_s=15.0, forward=False):
-    """The oracle as it stands, on one host thread, over a seeded sample of
-    tokens: each sampled token's full backward (its dQ row and its dK/dV
-    scatter), or its forward with ``forward``.  Batches double in size until
-    about ``target_s`` seconds."""
+def _host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return dict(model=model, logical_cpus=os.cpu_count(), usable_cpus=usable)
+
+
+def _cpu_baseline(case, inp, seed, target_s=15.0, forward=False, threads=1):
+    """The oracle as it stands, over a seeded sample of tokens: each sampled
+    token's full backward (its dQ row and its dK/dV scatter), or its forward
+    with ``forward``.  Batches double in size until about ``target_s``
+    seconds.  With ``threads`` > 1 each batch is split over that many worker
+    threads (one BLAS thread each; NumPy and torch release the interpreter
+    lock inside their array operations), and the figure is the batch's flops
+    over its wall time."""
+    import concurrent.futures as cf
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -244,29 +310,177 @@ def _cpu_baseline(case, inp, seed, target_s=15.0, forward=False):
                 m=cpu(inp["softmax_max"], (T1, G)), l=cpu(inp["softmax_sum"], (T1, G)),
                 qr=cpu(inp.get("query_rope"), (T1, G, Dr)) if Dr else None,
                 idx=cpu(inp["sparse_indices"], (T1, case.Kent)))
-    done, flops, used, batch = 0, 0, 0.0, 2
-    with threadpool_limits(limits=1):
+    def prepare(sel):
+        ts = __import__("torch").as_tensor(sel)
+        sub = {n: None if x is None else x[ts.to(x.device)].cpu() for n, x in full.items()}
+        g = {n: (a[sel] if isinstance(a, np.ndarray) else a) for n, a in geom.items()}
+        g["T1"] = len(sel)
+        return sub, g
+
+    def run(job):
+        sub, g = job
+        if forward:
+            orc.forward(sub["q"], k, v, sub["qr"], kr, sub["idx"], g, case.block, case.mode, case.scale_value)
+        else:
+            orc.backward(sub["q"], k, v, sub["qr"], kr, sub["idx"], sub["dO"], sub["O"], sub["m"], sub["l"], g,
+                         case.block, case.mode, case.scale_value)
+
+    done, flops, used, batch = 0, 0, 0.0, 2 * threads
+    with threadpool_limits(limits=1, user_api="blas"), cf.ThreadPoolExecutor(max_workers=threads) as pool:
         while used < target_s and done < T1:
             sel = np.sort(order[done:done + batch])
-            ts = __import__("torch").as_tensor(sel)
-            sub = {n: None if x is None else x[ts.to(x.device)].cpu() for n, x in full.items()}
-            g = {n: (a[sel] if isinstance(a, np.ndarray) else a) for n, a in geom.items()}
-            g["T1"] = len(sel)
+            jobs = [prepare(part) for part in np.array_split(sel, threads) if len(part)]
             t0 = time.perf_counter()
-            if forward:
-                orc.forward(sub["q"], k, v, sub["qr"], kr, sub["idx"], g, case.block, case.mode, case.scale_value)
-            else:
-                orc.backward(sub["q"], k, v, sub["qr"], kr, sub["idx"], sub["dO"], sub["O"], sub["m"], sub["l"], g,
-                             case.block, case.mode, case.scale_value)
+            list(pool.map(run, jobs))
             used += time.perf_counter() - t0
-            rows = orc.decode(sub["idx"], case.block, case.mode, g)
-            flops += (int((rows >= 0).sum()) * G * 2 * (2 * D + Dr) if forward else orc.flops(rows, G, D, Dr))
+            for sub, g in jobs:
+                rows = orc.decode(sub["idx"], case.block, case.mode, g)
+                flops += (int((rows >= 0).sum()) * G * 2 * (2 * D + Dr) if forward else orc.flops(rows, G, D, Dr))
             done += len(sel)
             batch *= 2
-    return dict(value=flops / used / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+    how = "one thread" if threads == 1 else f"{threads} worker threads of one BLAS thread each"
+    return dict(value=flops / used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample=(f"{done} seeded tokens of the same workload, each token's full "
                         + ("forward" if forward else "backward (dQ row and dK/dV scatter)")
-                        + f", float64 NumPy on one thread, {used:.1f} s"))
+                        + f", float64 NumPy on {how}, {used:.1f} s"))
+
+
+def _prepare(case, seed, dev, sfag, band=None, value_is_key=False):
+    """Inputs of ``case`` on ``dev``, with out / softmaxMax / softmaxSum from
+    the library's forward pass, and the number of valid pairs."""
+    import torch
+
+    import sfag_inputs as si
+    inp = si.make_inputs(case, seed, device=dev)
+    if band is not None:
+        shape = tuple(inp["sparse_indices"].shape)
+        kw_b = dict(pre_tokens=band[0], next_tokens=band[1], block_size=case.block, layout=case.layout, K=case.K)
+        if case.layout == "BSND":
+            kw_b.update(B=case.B, S1=case.S1, S2=case.S2, device=dev)
+        else:
+            kw_b.update(seqlens_q=inp["seqlens_q"], seqlens_kv=inp["seqlens_kv"])
+        inp["sparse_indices"] = sfag.band_indices(**kw_b).reshape(shape)
+    if value_is_key:
+        inp["value"] = inp["key"]
+    out, smax, ssum = sfag.forward(inp["query"], inp["key"], inp["value"], inp["sparse_indices"],
+                                   seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"),
+                                   query_rope=inp.get("query_rope"), key_rope=inp.get("key_rope"),
+                                   scale=case.scale_value, block_size=case.block, layout=case.layout,
+                                   sparse_mode=case.mode)
+    inp.update(out=out, softmax_max=smax, softmax_sum=ssum)
+    torch.cuda.synchronize()
+    n_pairs, _ = _count_valid(case, inp, sfag)
+    return inp, n_pairs
+
+
+def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", value_is_key=False, options=None):
+    """Time ``steps`` calls after ``warmup`` (HIP events on the call's stream
+    around the whole region and around each kernel group), and the roofline
+    of the kernel group with the largest time per step.  When the call runs
+    the dQ kernel on a second stream beside the key-block kernels, the
+    per-kernel times for the roofline come from a separate serial pass."""
+    import torch
+    dev = inp["query"].device
+    outs = (torch.empty_like(inp["query"]), torch.empty_like(inp["key"]), torch.empty_like(inp["value"]),
+            torch.empty_like(inp["query_rope"]) if case.Dr else None,
+            torch.empty_like(inp["key_rope"]) if case.Dr else None)
+    kw = dict(seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"), query_rope=inp.get("query_rope"),
+              key_rope=inp.get("key_rope"), scale=case.scale_value, block_size=case.block, layout=case.layout,
+              sparse_mode=case.mode, deterministic=det)
+    args_pos = (inp["query"], inp["key"], inp["value"], inp["sparse_indices"], inp["dout"], inp["out"],
+                inp["softmax_max"], inp["softmax_sum"])
+    stream = torch.cuda.current_stream(dev)
+    if which == "forward":
+        fouts = (torch.empty_like(inp["out"]), torch.empty_like(inp["softmax_max"]),
+                 torch.empty_like(inp["softmax_sum"]))
+        fkw = dict(seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"),
+                   query_rope=inp.get("query_rope"), key_rope=inp.get("key_rope"), scale=case.scale_value,
+                   block_size=case.block, layout=case.layout, sparse_mode=case.mode)
+        fws = torch.empty(case.T1 * (case.Kent * case.block + 1) * 4 + (1 << 20), dtype=torch.uint8, device=dev)
+        flops = n_pairs * case.G * 2 * (2 * case.D + case.Dr)
+
+        def step(opts=None):
+            sfag.forward(inp["query"], inp["key"], inp["value"], inp["sparse_indices"], outputs=fouts,
+                         workspace=fws, stream=stream, **fkw)
+        concurrent = False
+    else:
+        ws_bytes = sfag.workspace_size(*args_pos, *outs[:3], dq_rope=outs[3], dk_rope=outs[4], options=options, **kw)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        flops = n_pairs * case.G * 2 * (3 * (case.D + case.Dr) + 2 * case.D)
+
+        def step(opts=options):
+            sfag.backward(*args_pos, outputs=outs, workspace=ws, stream=stream, options=opts, **kw)
+        # on the key-block path a second stream overlaps kernels (see
+        # sfag_options.concurrent): the per-kernel times that pick the
+        # roofline kernel then come from a serial pass
+        concurrent = not (options or {}).get("concurrent") == "off"
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    sfag.profile_reset()
+    sfag.profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    sfag.profile_enable(False)
+    ms = start.elapsed_time(stop) / steps
+    prof = sfag.profile_read()
+    nsteps_r = steps
+    rprof = prof
+    if concurrent:
+        serial = dict(options or {}, concurrent="off")
+        nsteps_r = max(2, min(steps, 5))
+        sfag.profile_reset()
+        sfag.profile_enable(True)
+        for _ in range(nsteps_r):
+            step(serial)
+        torch.cuda.synchronize()
+        sfag.profile_enable(False)
+        rprof = sfag.profile_read()
+    print(f"[bench] {case.name}: {steps} steps, {ms:.3f} ms/step; kernels: "
+          + ", ".join(f"{k}={v[0] / v[1]:.3f}ms x{v[1] // steps}" for k, v in prof.items()),
+          file=sys.stderr, flush=True)
+    tflops = flops / (ms * 1e-3) / 1e12
+    alg_bytes = (_alg_bytes(case, n_pairs, value_is_key) if which == "backward"
+                 else _kernel_bytes(case, "fwd", n_pairs))
+    # the roofline kernel: the largest time per step when every kernel runs
+    # alone; its duration from the timed region unless it shares the GPU with
+    # the second stream's kernels there
+    dom = max(rprof, key=lambda k: rprof[k][0])
+    overlapped = concurrent and (dom not in ("keyblock", "kb_reduce", "cast", "fill") or 32 <= case.G < 128)
+    src = rprof if overlapped or dom not in prof else prof
+    dom_ms = src[dom][0] / src[dom][1]
+    launches_per_step = src[dom][1] / (nsteps_r if src is rprof else steps)
+    timing = ("HIP events on the kernel's stream in a serial pass after the timed region (the default schedule "
+              "overlaps it with the second stream)" if src is rprof and concurrent
+              else "HIP events on the kernel's stream in the timed region")
+    roof = _roofline(case, dom, dom_ms, launches_per_step, n_pairs)
+    rec = _traffic_record(case) if which == "backward" and not value_is_key and options is None else None
+    roof["traffic"] = rec["kernels"].get(dom, {}).get("bytes_per_launch") if rec else None
+    roof["kernel"] = dom
+    roof["kernel_ms"] = dom_ms
+    roof["timing"] = timing
+    if dom in ("row", "fwd"):
+        # rate at which the kernel gathers selected K|Krope|V rows (from L2 and
+        # the last-level cache, mostly): context for its HBM roofline
+        rb = (case.D + case.Dr if value_is_key else 2 * case.D + case.Dr) * 2
+        roof["gathered_rows_GBs"] = n_pairs * rb / launches_per_step / (dom_ms * 1e-3) / 1e9
+    out = dict(workload=case.name, steps=steps, warmup=warmup, ms_per_step=ms, tflops=tflops,
+               mfma_frac=tflops / MFMA_PEAK_TFLOPS, valid_pairs=n_pairs,
+               alg_model_GBs=alg_bytes / (ms * 1e-3) / 1e9,
+               kernels_ms={k: v[0] / v[1] for k, v in prof.items()}, roofline=roof)
+    if rec and rec.get("step"):
+        gbs = rec["step"]["bytes"] / (ms * 1e-3) / 1e9
+        out.update(hbm_counter_GB_per_step=rec["step"]["bytes"] / 1e9, hbm_counter_GBs=gbs,
+                   hbm_frac=gbs / HBM_PEAK_GBS)
+    else:
+        out.update(hbm_counter_GB_per_step=None, hbm_counter_GBs=None, hbm_frac=None)
+    return out
 
 
 def main(argv=None):
@@ -274,7 +488,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
+    ap.add_argument("--config", type=int, default=None,
+                    help="time only this workload (1-5); by default 2 is the headline and 1, 3, 4, 5 follow")
     ap.add_argument("--deterministic", choices=("config", "true", "false"), default="config")
     ap.add_argument("--pass", dest="which", choices=("backward", "forward"), default="backward",
                     help="time the backward pass (the headline) or the forward pass that feeds it")
@@ -285,18 +500,20 @@ def main(argv=None):
     ap.add_argument("--band", metavar="PRE,NEXT",
                     help="replace the workload's indices with a band (sliding-window / dense) selection made by "
                          "sfag_band_indices: key positions d-PRE..d+NEXT of the bottom-right diagonal d")
+    ap.add_argument("--concurrent", choices=("auto", "off", "on"), default="auto",
+                    help="sfag_options.concurrent for the timed calls (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="also run one plain device copy of this many MiB (counter calibration)")
+                    help="first run one plain device copy and one read-only sum of this many MiB (counter "
+                         "calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
-                    help="summarize rocprofv3 CSV output under DIR/{trace,fetch,write} into profiles/ and exit")
+                    help="summarize rocprofv3 CSV output under DIR/{trace,rd,wr,mfma} into profiles/ and exit")
     args = ap.parse_args(argv)
     if args.summarize_profiles:
-        return _summarize_profiles(args.summarize_profiles, args.config, args.calib_copy_mb)
+        return _summarize_profiles(args.summarize_profiles, args.config or 2, args.calib_copy_mb)
     if args.gpus != 1:
-        print("bench.py measures a single GPU: the library has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import torch
@@ -304,133 +521,93 @@ def main(argv=None):
     import sfag_inputs as si
     import top_sparse_attention_sfag_amd as sfag
 
-    case = si.CONFIGS[args.config]
-    if args.dtype != "config" and args.dtype != case.dtype:
-        case = case.replace(name=f"{case.name}_as_{args.dtype}", dtype=args.dtype)
-    band = None
-    if args.band:
-        band = tuple(int(x) for x in args.band.split(","))
-        max_lk = case.S2 if case.layout == "BSND" else max(case.seqlens_kv)
-        kb = sfag.band_entries(max_lk, band[0], band[1], case.block)
-        case = case.replace(name=f"{case.name}_band_pre{band[0]}_next{band[1]}", K=kb, index_rule="uniform")
-    det = case.deterministic if args.deterministic == "config" else args.deterministic == "true"
-    seed = si.seed_for(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {case.name} on {dev}", file=sys.stderr, flush=True)
-    inp = si.make_inputs(case, seed, device=dev)
-    if band is not None:
-        shape = tuple(inp["sparse_indices"].shape)
-        kw_b = dict(pre_tokens=band[0], next_tokens=band[1], block_size=case.block, layout=case.layout, K=case.K)
-        if case.layout == "BSND":
-            kw_b.update(B=case.B, S1=case.S1, S2=case.S2, device=dev)
-        else:
-            kw_b.update(seqlens_q=inp["seqlens_q"], seqlens_kv=inp["seqlens_kv"])
-        inp["sparse_indices"] = sfag.band_indices(**kw_b).reshape(shape)
-    if args.value_is_key:
-        inp["value"] = inp["key"]
-    inp.update(si.standin_stats(case, inp, seed, device=dev))
-    torch.cuda.synchronize()
-    n_pairs, _ = _count_valid(case, inp, sfag)
-    flop_per_pair = 2 * (3 * (case.D + case.Dr) + 2 * case.D)
-    flops = n_pairs * case.G * flop_per_pair
-
-    outs = (torch.empty_like(inp["query"]), torch.empty_like(inp["key"]), torch.empty_like(inp["value"]),
-            torch.empty_like(inp["query_rope"]) if case.Dr else None,
-            torch.empty_like(inp["key_rope"]) if case.Dr else None)
-    kw = dict(seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"), query_rope=inp.get("query_rope"),
-              key_rope=inp.get("key_rope"), scale=case.scale_value, block_size=case.block, layout=case.layout,
-              sparse_mode=case.mode, deterministic=det)
-    args_pos = (inp["query"], inp["key"], inp["value"], inp["sparse_indices"], inp["dout"], inp["out"],
-                inp["softmax_max"], inp["softmax_sum"])
-    ws_bytes = sfag.workspace_size(*args_pos, *outs[:3], dq_rope=outs[3], dk_rope=outs[4], **kw)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        sfag.backward(*args_pos, outputs=outs, workspace=ws, stream=stream, **kw)
-
-    if args.which == "forward":
-        # out / softmaxMax / softmaxSum written into the input tensors' copies
-        fouts = (torch.empty_like(inp["out"]), torch.empty_like(inp["softmax_max"]),
-                 torch.empty_like(inp["softmax_sum"]))
-        fws = torch.empty(case.T1 * (case.Kent * case.block + 1) * 4 + 4096, dtype=torch.uint8, device=dev)
-        fkw = dict(seqlens_q=inp.get("seqlens_q"), seqlens_kv=inp.get("seqlens_kv"),
-                   query_rope=inp.get("query_rope"), key_rope=inp.get("key_rope"), scale=case.scale_value,
-                   block_size=case.block, layout=case.layout, sparse_mode=case.mode)
-        flops = n_pairs * case.G * 2 * (2 * case.D + case.Dr)
-
-        def step():  # noqa: F811
-            sfag.forward(inp["query"], inp["key"], inp["value"], inp["sparse_indices"], outputs=fouts,
-                         workspace=fws, stream=stream, **fkw)
-
     if args.calib_copy_mb:
-        # one elementwise kernel that reads and writes calib_copy_mb MiB each
+        # one elementwise kernel that reads and writes calib_copy_mb MiB each,
+        # and one reduction that only reads them
         src = torch.ones((args.calib_copy_mb << 20) // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
-        del src, dst
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    sfag.profile_reset()
-    sfag.profile_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    sfag.profile_enable(False)
-    ms = start.elapsed_time(stop) / args.steps
-    prof = sfag.profile_read()
-    print(f"[bench] {args.steps} steps, {ms:.3f} ms/step; kernels: "
-          + ", ".join(f"{k}={v[0] / v[1]:.3f}ms x{v[1] // args.steps}" for k, v in prof.items()),
-          file=sys.stderr, flush=True)
+        total = src.sum()
+        torch.cuda.synchronize()
+        del src, dst, total
 
-    tflops = flops / (ms * 1e-3) / 1e12
-    alg_bytes = (_alg_bytes(case, n_pairs, args.value_is_key) if args.which == "backward"
-                 else _kernel_bytes(case, "fwd", n_pairs))
-    # Dominant kernel and its algorithmic work per launch.
-    dom = max(prof, key=lambda k: prof[k][0])
-    dom_ms = prof[dom][0] / prof[dom][1]
-    launches_per_step = prof[dom][1] / args.steps
-    roof = _roofline(case, dom, dom_ms, launches_per_step, n_pairs)
-    roof["traffic"] = _traffic(case, dom)
-    roof["kernel"] = dom
-    roof["kernel_ms"] = dom_ms
+    def case_of(cfg):
+        case = si.CONFIGS[cfg]
+        if args.dtype != "config" and args.dtype != case.dtype:
+            case = case.replace(name=f"{case.name}_as_{args.dtype}", dtype=args.dtype)
+        band = None
+        if args.band:
+            band = tuple(int(x) for x in args.band.split(","))
+            max_lk = case.S2 if case.layout == "BSND" else max(case.seqlens_kv)
+            kb = sfag.band_entries(max_lk, band[0], band[1], case.block)
+            case = case.replace(name=f"{case.name}_band_pre{band[0]}_next{band[1]}", K=kb, index_rule="uniform")
+        det = case.deterministic if args.deterministic == "config" else args.deterministic == "true"
+        return case, band, det
+
+    headline = args.config or 2
+    sweep = [] if args.config else [1, 3, 4, 5]
+    case, band, det = case_of(headline)
+    seed = si.seed_for(headline)
+    print(f"[bench] generating {case.name} on {dev}", file=sys.stderr, flush=True)
+    inp, n_pairs = _prepare(case, seed, dev, sfag, band, args.value_is_key)
+    opts = None if args.concurrent == "auto" else dict(concurrent=args.concurrent)
+    head = _measure(case, inp, n_pairs, det, args.steps, args.warmup, sfag, args.which, args.value_is_key, opts)
 
     line = {
         "metric": ("sparse-attn bwd TFLOP/s + % bf16 MFMA peak (G=128) / % HBM peak (G<=16), 1 GPU"
                    if args.which == "backward" else "sparse-attn fwd TFLOP/s (forward pass), 1 GPU"),
-        "value": tflops,
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": case.dtype,
-        "data": "synthetic (seeded generator; stand-in softmax statistics)",
+        "data": "synthetic (seeded generator); out/softmaxMax/softmaxSum from the library's forward pass",
         "config": {"workload": case.name, "layout": case.layout, "B": case.B, "T1": case.T1, "T2": case.T2,
                    "N1": case.G, "D": case.D, "Dr": case.Dr, "K": case.K, "sparse_block": case.block,
                    "sparse_mode": case.mode, "deterministic": det, "valid_pairs": n_pairs,
                    "value_is_key": bool(args.value_is_key)},
-        "mfma_frac": tflops / MFMA_PEAK_TFLOPS,
-        "alg_GBs": alg_bytes / (ms * 1e-3) / 1e9,
-        "hbm_frac_alg": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "kernels_ms": {k: v[0] / v[1] for k, v in prof.items()},
-        "roofline": roof,
+        "mfma_frac": head["mfma_frac"],
+        "alg_model_GBs": head["alg_model_GBs"],
+        "hbm_counter_GBs": head["hbm_counter_GBs"],
+        "hbm_frac": head["hbm_frac"],
+        "kernels_ms": head["kernels_ms"],
+        "roofline": head["roofline"],
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = _cpu_baseline(case, inp, seed, args.cpu_seconds, forward=args.which == "forward")
+        host = _host_cpu()
+        cb = _cpu_baseline(case, inp, seed, args.cpu_seconds, forward=args.which == "forward")
+        cores = max(1, min(16, host["usable_cpus"] or 1))
+        allc = _cpu_baseline(case, inp, seed, args.cpu_seconds / 2, forward=args.which == "forward", threads=cores)
+        cb["host"] = host
+        cb["all_cores"] = dict(value=allc["value"], unit=allc["unit"], cores=cores, sample=allc["sample"])
+        line["cpu_baseline"] = cb
+    del inp
+    torch.cuda.empty_cache()
+    if sweep:
+        line["configs"] = {}
+        for cfg in sweep:
+            c, b, d = case_of(cfg)
+            print(f"[bench] generating {c.name}", file=sys.stderr, flush=True)
+            inp_c, n_c = _prepare(c, si.seed_for(cfg), dev, sfag, b, args.value_is_key)
+            st = args.steps if cfg <= 3 else max(3, args.steps // 4)
+            rec = _measure(c, inp_c, n_c, d, st, min(args.warmup, 2) if cfg > 3 else args.warmup, sfag, args.which,
+                           args.value_is_key, opts)
+            rec["config"] = {"layout": c.layout, "B": c.B, "T1": c.T1, "T2": c.T2, "N1": c.G, "D": c.D, "Dr": c.Dr,
+                             "K": c.K, "sparse_block": c.block, "sparse_mode": c.mode, "deterministic": d,
+                             "dtype": c.dtype}
+            line["configs"][f"cfg{cfg}"] = rec
+            del inp_c
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
     return 0
 

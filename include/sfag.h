@@ -23,9 +23,13 @@
  *
  * Memory: every tensor and the workspace belong to the caller and live in
  * device memory (HBM) of the current HIP device; the library allocates and
- * frees no device memory and keeps no device state between calls (apart from
- * one auxiliary stream and two events per device, see sfag_backward).  Work
- * is enqueued asynchronously on the caller's stream.
+ * frees no device memory and keeps no device state between calls, apart from
+ * one auxiliary stream and two events per device that it makes on first use
+ * when a call runs two kernels side by side and no stream of the caller's is
+ * given for that (sfag_options.auxStream), and the opt-in timing records of
+ * sfag_profile_*.  Work is enqueued asynchronously on the caller's stream.
+ * Nothing reads the environment: every tuning choice is a field of
+ * sfag_options, fixed per plan.
  */
 #ifndef SFAG_H
 #define SFAG_H
@@ -66,6 +70,68 @@ typedef struct sfag_tensor {
  * data), the derived sizes and the workspace layout.  The analogue of the
  * operator's executor. */
 typedef struct sfag_plan sfag_plan;
+
+/* Values of sfag_options fields (0 always means "chosen from the shapes"). */
+#define SFAG_SCATTER_AUTO 0
+#define SFAG_SCATTER_KEYBLOCK 1  /* key-block contraction over the tokens selecting a block of 256 keys */
+#define SFAG_SCATTER_PARTIALS 2  /* per-(token, position) rows summed per key in CSR order */
+#define SFAG_SCATTER_ATOMIC 3    /* fp32 atomic adds (deterministic calls use PARTIALS instead) */
+#define SFAG_TOKEN_AUTO 0
+#define SFAG_TOKEN_FUSED 1       /* one kernel per token for S, P, dP, dS and dQ (up to 64 heads a workgroup) */
+#define SFAG_TOKEN_SPLIT 2       /* S/P/dP/dS kernel then dQ kernel (up to 128 heads a workgroup; N1 >= 32) */
+#define SFAG_ORDER_AUTO 0
+#define SFAG_ORDER_ASCENDING 1   /* token kernels visit a chunk first token first */
+#define SFAG_ORDER_DESCENDING 2  /* last token first (the default under sparseMode 3) */
+#define SFAG_CONCURRENT_AUTO 0
+#define SFAG_CONCURRENT_OFF 1
+#define SFAG_CONCURRENT_ON 2
+
+/*
+ * Tuning and debugging choices of one plan.  They are not part of the
+ * operator's interface: sfag_workspace_size makes a plan with the defaults
+ * (every field 0), and sfag_plan_configure re-plans it with other values.
+ * No choice changes what is computed; the deterministic mode's bits depend on
+ * keyBlockRanges alone (never on the budget or the chunking).
+ *   workspaceBudget  bytes the whole workspace should stay within; query
+ *                    tokens are processed in chunks sized to it (0 = 48 GiB
+ *                    for the backward pass, 16 GiB for the forward pass).  A
+ *                    chunk never drops below one key-block token range, so
+ *                    a tiny budget can still give a larger workspace.
+ *   chunkTokens      at most this many query tokens per chunk (0 = no limit;
+ *                    rounded down to whole token ranges, at least one).
+ *   scatter          SFAG_SCATTER_* (how dKey/dValue rows are accumulated).
+ *   tokenPath        SFAG_TOKEN_* (FUSED is the default for N1 <= 16).
+ *   tokenOrder       SFAG_ORDER_*.
+ *   concurrent       SFAG_CONCURRENT_*: run the dQ kernel on a second stream
+ *                    beside the key-block kernels (default on for
+ *                    32 <= N1 < 128 on the key-block path).
+ *   rowSplit         workgroups sharing one token's positions in the fused
+ *                    token kernel (0 = chosen; 1..8; never split when
+ *                    deterministic, whose sums must keep a fixed order).
+ *   keyBlockRanges   token ranges per default-size chunk of the key-block
+ *                    path (0 = 16).  Range boundaries are fixed in absolute
+ *                    token coordinates from the shapes and this value.
+ *   validate         1: the call also checks its index and length inputs on
+ *                    the device (sfag_validation_read reports the result);
+ *                    the workspace grows by 256 bytes.
+ *   auxStream        the second stream of a concurrent call (a hipStream_t
+ *                    of the caller's, on the same device); NULL = one the
+ *                    library makes once per device and keeps until the
+ *                    process ends.
+ */
+typedef struct sfag_options {
+  uint64_t workspaceBudget;
+  int64_t chunkTokens;
+  int32_t scatter;
+  int32_t tokenPath;
+  int32_t tokenOrder;
+  int32_t concurrent;
+  int32_t rowSplit;
+  int32_t keyBlockRanges;
+  int32_t validate;
+  int32_t reserved;
+  void* auxStream;
+} sfag_options;
 
 /*
  * Phase 1: validate the arguments, plan the launch and report the workspace
@@ -113,11 +179,14 @@ int sfag_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const 
  * consumed and freed, also on error.  Returns SFAG_OK once the work is
  * enqueued; errors found by the kernels are not reported (indices are bounds
  * checked on the device, so bad indices are masked, never dereferenced).
- * With 32 <= N1 < 128 the dQ kernel runs on a second stream of the library's
- * (one per device, default priority, made on first use) between an event
- * recorded on `stream` and an event `stream` waits for, so every output is
- * complete once `stream` reaches that point: the caller synchronizes `stream`
- * only.  SFAG_CONCURRENT=0 keeps everything on `stream`.
+ * When the plan runs the dQ kernel beside the key-block kernels (by default
+ * with 32 <= N1 < 128; sfag_options.concurrent), that kernel goes on a
+ * second stream (sfag_options.auxStream, or one of the library's: one per
+ * device, default priority, made on first use and kept until the process
+ * ends) between an event recorded on `stream` and an event `stream` waits
+ * for, so every output is complete once `stream` reaches that point: the
+ * caller synchronizes `stream` only.  Calls that share the library's second
+ * stream on one device are ordered on it.
  */
 int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
 
@@ -145,6 +214,47 @@ int sfag_forward_workspace_size(const sfag_tensor* query, const sfag_tensor* key
                                 const sfag_tensor* softmaxMax, const sfag_tensor* softmaxSum,
                                 uint64_t* workspaceSize, sfag_plan** plan);
 int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
+
+/*
+ * Re-plans a plan from sfag_workspace_size or sfag_forward_workspace_size
+ * (not yet executed) with `options` (NULL = the defaults) and reports the new
+ * workspace size.  Host only.  Errors: SFAG_ERR_NULLPTR for a NULL plan or
+ * size pointer; SFAG_ERR_PARAM_INVALID for a field outside its values
+ * (the plan is left as it was); SFAG_ERR_TILING when no chunking fits the
+ * 32-bit pair numbering.
+ */
+int sfag_plan_configure(sfag_plan* plan, const sfag_options* options, uint64_t* workspaceSize);
+
+/*
+ * Result of the device-side input checks of a call planned with
+ * options.validate = 1, read back from that call's workspace.  flags is an
+ * OR of:
+ *   SFAG_BAD_LENGTH_NEGATIVE   an actualSeqLengths entry is negative (the
+ *                              parameter table warns that negative values
+ *                              are invalid; they count as 0);
+ *   SFAG_BAD_LENGTH_SUM_Q/_KV  the query / key lengths do not add up to T1 /
+ *                              T2 (the parameter table requires that they
+ *                              do; tokens past the declared lengths get no
+ *                              valid position and keys past them are never
+ *                              read);
+ *   SFAG_BAD_INDEX_RANGE       an index entry is at or past its sequence's
+ *                              key length (such entries are masked).
+ * badEntries counts the entries of the last kind.  sfag_validation_read
+ * enqueues a copy of the 16-byte result on `stream`, waits for the stream and
+ * fills *result; call it with the workspace of a finished validating call
+ * before reusing that workspace.  Errors: SFAG_ERR_NULLPTR,
+ * SFAG_ERR_RUNTIME for a failed copy.
+ */
+#define SFAG_BAD_LENGTH_NEGATIVE 1u
+#define SFAG_BAD_LENGTH_SUM_Q 2u
+#define SFAG_BAD_LENGTH_SUM_KV 4u
+#define SFAG_BAD_INDEX_RANGE 8u
+typedef struct sfag_validation {
+  uint32_t flags;
+  uint32_t reserved;
+  uint64_t badEntries;
+} sfag_validation;
+int sfag_validation_read(const void* workspace, void* stream, sfag_validation* result);
 
 /* Frees a plan that will not be executed.  NULL is accepted. */
 void sfag_plan_destroy(sfag_plan* plan);

@@ -239,3 +239,110 @@ def test_band_entries_match_the_oracle_count():
                 for block in (1, 8, 16, 64):
                     assert L.sfag_band_entries(lk, pre, nxt, block) == orc.band_entries(lk, pre, nxt, block), \
                         (lk, pre, nxt, block)
+
+
+def _configure(p, **opts):
+    o = sfag.make_options(opts) if opts else None
+    ws = ctypes.c_uint64(0)
+    rc = sfag.lib().sfag_plan_configure(p, ctypes.byref(o) if o is not None else None, ctypes.byref(ws))
+    return rc, int(ws.value)
+
+
+def test_configure_defaults_and_budget():
+    """sfag_plan_configure re-plans from the shapes: no options = the phase-1
+    size; a smaller budget gives a smaller workspace (more, smaller chunks);
+    validation adds exactly the 256-byte result region."""
+    t = _tensors("BSND", B=1, S1=512, S2=1024, G=64, Dr=64, K=256)
+    ws0, p = _plan(t, sparse_mode=3)
+    assert _configure(p) == (0, ws0)
+    rc, ws_small = _configure(p, workspace_budget=64 << 20)
+    assert rc == 0 and ws_small < ws0
+    rc, ws_val = _configure(p, validate=True)
+    assert rc == 0 and ws_val == ws0 + 256
+    rc, ws_chunk = _configure(p, chunk_tokens=8)
+    assert rc == 0 and ws_chunk < ws0
+    sfag.destroy(p)
+
+
+@pytest.mark.parametrize("field,value", [("scatter", 4), ("tokenPath", 3), ("tokenOrder", -1), ("concurrent", 3),
+                                         ("rowSplit", 9), ("keyBlockRanges", -2), ("chunkTokens", -1),
+                                         ("validate", 2)])
+def test_configure_rejects_bad_fields(field, value):
+    t = _tensors()
+    ws0, p = _plan(t)
+    o = sfag._binding.SfagOptions()
+    setattr(o, field, value)
+    ws = ctypes.c_uint64(0)
+    assert sfag.lib().sfag_plan_configure(p, ctypes.byref(o), ctypes.byref(ws)) == 161002
+    assert _configure(p) == (0, ws0)   # the plan is left as it was
+    sfag.destroy(p)
+    assert sfag.lib().sfag_plan_configure(None, None, ctypes.byref(ws)) == 161001
+
+
+def test_configure_forward_plan():
+    rc, ws0, p = _fwd_plan(_tensors("BSND", S1=64, S2=128, K=32))
+    assert rc == 0
+    rc, ws1 = _configure(p, workspace_budget=1 << 16)
+    assert rc == 0 and ws1 < ws0
+    rc, ws2 = _configure(p, validate=True)
+    assert rc == 0 and ws2 == ws0 + 256
+    sfag.destroy(p)
+
+
+def test_empty_query_validation_workspace():
+    t = _tensors("TND", S1=0)
+    ws, p = _plan(t)
+    assert ws == 0
+    rc, ws = _configure(p, validate=True)
+    assert rc == 0 and ws >= 256
+    sfag.destroy(p)
+
+
+def test_validation_read_null_arguments():
+    v = sfag._binding.SfagValidation()
+    assert sfag.lib().sfag_validation_read(None, None, ctypes.byref(v)) == 161001
+    assert sfag.lib().sfag_validation_read(ctypes.c_void_p(256), None, None) == 161001
+
+
+def _fake(shape, dtype_code):
+    """A descriptor with a placeholder data pointer: phase 1 reads no data."""
+    d = sfag._binding.SfagTensor()
+    d.data = 4096
+    d.dtype = dtype_code
+    d.ndim = len(shape)
+    stride = 1
+    for i in reversed(range(len(shape))):
+        d.shape[i] = shape[i]
+        d.stride[i] = stride
+        stride *= shape[i]
+    return ctypes.pointer(d)
+
+
+def test_long_keys_cap_the_chunk_instead_of_failing():
+    """128K keys make 512 key blocks: the key-block sort key (block x chunk +
+    token) must stay below 2^31, so phase 1 caps the chunk (here 128K query
+    tokens, which would not fit in one chunk) instead of failing."""
+    B, S1, S2, G, K = 1, 131072, 131072, 1, 65536
+    bf, i32, f32 = 1, 4, 3
+    q = lambda: _fake((B, S1, G, 512), bf)
+    k = lambda: _fake((B, S2, 1, 512), bf)
+    st = lambda: _fake((B, 1, S1, G), f32)
+    ws = ctypes.c_uint64(0)
+    p = ctypes.c_void_p(None)
+    rc = sfag.lib().sfag_workspace_size(q(), k(), k(), _fake((B, S1, 1, K), i32), q(), q(), st(), st(), None, None,
+                                        None, None, 0.04, 1, b"BSND", 0, 2147483647, 2147483647, True, q(), k(), k(),
+                                        None, None, ctypes.byref(ws), ctypes.byref(p))
+    assert rc == 0, sfag.lib().sfag_last_error()
+    o = sfag.make_options(dict(scatter="keyblock"))
+    assert sfag.lib().sfag_plan_configure(p, ctypes.byref(o), ctypes.byref(ws)) == 0
+    sfag.destroy(p)
+
+
+def test_product_sources_read_no_environment():
+    """Every tuning choice is an sfag_options field: the library's sources
+    never read the environment."""
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "top_sparse_attention_sfag_amd",
+                        "csrc")
+    for f in sorted(os.listdir(csrc)):
+        src = open(os.path.join(csrc, f)).read()
+        assert "getenv" not in src and "environ" not in src, f

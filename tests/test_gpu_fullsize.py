@@ -1,14 +1,33 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (default chunking and scatter path, deterministic as the
 workload states).  The oracle cannot run these whole, so it computes sampled
-output rows one by one: dQ/dQueryRope rows of sampled tokens (each depends only
-on its own token) and dK/dV/dKeyRope rows of sampled key rows, including the
-most-selected one (each is the sum over the pairs that select it, and the
-saved statistics make every pair independent of the rest of its token's row).
-Inputs are generated on the GPU; the softmax statistics are the generator's
-stand-ins, which the backward pass takes as given.  Rows that no valid
-position selects must be exactly 0 everywhere.
+output rows one by one:
+
+* dQ / dQueryRope of 64 tokens, one drawn from each of 64 equal strata of the
+  token range (so every chunk, every key-block token range and both ends of a
+  causal sequence are visited), its residue mod 8 set to the stratum's, so the
+  token kernels' workgroups of every XCD are checked; plus the first and last
+  token.  Each such token gets forward statistics from the oracle's forward
+  pass (its out, softmaxMax and softmaxSum inputs are overwritten before the
+  GPU run); the other tokens keep the generator's stand-in statistics, which
+  the backward pass takes as given inputs just the same.
+* dK / dV / dKeyRope of the 5 most-selected key rows and of one live key row
+  drawn from each of 27 equal strata of the key range.  Each is the sum over
+  every (token, position) selecting it, which the saved statistics make
+  independent of the rest of the token's row.
+
+Every sampled row is held to the tolerance on its own (relative L2 of the
+row: dQ/dQueryRope of a token <= 5e-3, dK/dV/dKeyRope of a key row <= 1e-2),
+not only the pooled error.  A row whose reference norm is below 1% of the
+median sampled row norm is measured against that 1% instead of its own norm
+(the first token of a causal sequence has one key, so P = 1, dP equals Delta
+and its dQ is exactly 0).  Rows that no valid position selects must be
+exactly 0.  The worst row error per tensor is printed and, with
+``--margins-dir``, written there as JSON.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,51 +39,112 @@ from tests._helpers import call_backward, geom_of, rel_l2
 pytestmark = pytest.mark.gpu
 
 TOL = dict(dq=5e-3, dqr=5e-3, dk=1e-2, dv=1e-2, dkr=1e-2)
+N_TOKEN_STRATA, N_KEY_STRATA, N_HOT = 64, 27, 5
+
+
+def sample_tokens(T1, rng):
+    edges = np.linspace(0, T1, N_TOKEN_STRATA + 1).astype(np.int64)
+    out = [0, T1 - 1]
+    for i in range(N_TOKEN_STRATA):
+        lo, hi = int(edges[i]), int(edges[i + 1])
+        if hi <= lo:
+            continue
+        t = int(rng.integers(lo, hi))
+        t = t - (t % 8) + (i % 8)          # the stratum's residue mod 8, inside the stratum if it fits
+        out.append(min(max(t, lo), hi - 1))
+    return np.unique(np.asarray(out, dtype=np.int64))
+
+
+def sample_keys(counts, rng):
+    T2 = len(counts)
+    hot = np.argsort(-counts, kind="stable")[:N_HOT]
+    edges = np.linspace(0, T2, N_KEY_STRATA + 1).astype(np.int64)
+    out = list(hot)
+    for i in range(N_KEY_STRATA):
+        live = np.nonzero(counts[edges[i]:edges[i + 1]])[0]
+        if len(live):
+            out.append(int(edges[i] + rng.choice(live)))
+    return np.unique(np.asarray(out, dtype=np.int64))
+
+
+def _forward_stats(case, inp, tokens, geom):
+    """Oracle forward of ``tokens`` only (their index rows and geometry)."""
+    sub = lambda x, w: None if x is None else x.reshape(case.T1, -1, w)[torch.as_tensor(tokens, device=x.device)]
+    G, D, Dr = case.G, case.D, case.Dr
+    idx = inp["sparse_indices"].reshape(case.T1, case.Kent)[torch.as_tensor(tokens, device="cuda")].cpu()
+    g = {n: (a[tokens] if isinstance(a, np.ndarray) else a) for n, a in geom.items()}
+    g["T1"] = len(tokens)
+    q = sub(inp["query"], D).reshape(len(tokens), G, D)
+    qr = sub(inp.get("query_rope"), Dr).reshape(len(tokens), G, Dr) if Dr else None
+    return orc.forward(q, inp["key"].reshape(case.T2, D), inp["value"].reshape(case.T2, D), qr,
+                       inp["key_rope"].reshape(case.T2, Dr) if Dr else None, idx, g, case.block, case.mode,
+                       case.scale_value)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_sampled(cfg):
+def test_full_size_sampled(cfg, request):
     case = si.CONFIGS[cfg]
     seed = si.seed_for(cfg)
     print(f"full-size {case.name} seed {seed}", flush=True)
     inp = si.make_inputs(case, seed, device="cuda")
     inp.update(si.standin_stats(case, inp, seed, device="cuda"))
+    geom = geom_of(case)
+    rng = np.random.default_rng(seed)
+    tokens = sample_tokens(case.T1, rng)
+
+    # forward-consistent statistics for the sampled tokens
+    O, M, L = _forward_stats(case, inp, tokens, geom)
+    T = torch.as_tensor(tokens, device="cuda")
+    inp["out"].view(case.T1, case.G, case.D)[T] = torch.from_numpy(O).to("cuda").to(inp["out"].dtype)
+    inp["softmax_max"].view(case.T1, case.G)[T] = torch.from_numpy(M.astype(np.float32)).to("cuda")
+    inp["softmax_sum"].view(case.T1, case.G)[T] = torch.from_numpy(L.astype(np.float32)).to("cuda")
+    print(f"tokens {len(tokens)} (forward statistics from the oracle)", flush=True)
+
     outs = call_backward(case, inp)
     torch.cuda.synchronize()
     dq, dk, dv, dqr, dkr = outs
+
     idx = inp["sparse_indices"].reshape(case.T1, case.Kent).cpu()
-    m = inp["softmax_max"].reshape(case.T1, case.G)
-    l = inp["softmax_sum"].reshape(case.T1, case.G)
-    geom = geom_of(case)
     rows = orc.decode(idx, case.block, case.mode, geom)
     counts = np.bincount(rows[rows >= 0], minlength=case.T2)
-    rng = np.random.default_rng(seed)
-    tokens = np.unique(np.concatenate([[0, case.T1 - 1, case.T1 // 2], rng.choice(case.T1, 3, replace=False)]))
-    live_keys = np.nonzero(counts)[0]
-    keys = np.unique(np.concatenate([[int(np.argmax(counts))], rng.choice(live_keys, 3, replace=False)]))
-    print(f"tokens {tokens.tolist()} keys {keys.tolist()} (max hits {counts.max()})", flush=True)
+    keys = sample_keys(counts, rng)
+    print(f"keys {len(keys)} (max hits {counts.max()}, hits of the sampled keys "
+          f"{int(counts[keys].min())}..{int(counts[keys].max())})", flush=True)
     ref = orc.backward_rows(inp["query"].reshape(case.T1, case.G, case.D),
                             inp["key"].reshape(case.T2, case.D), inp["value"].reshape(case.T2, case.D),
                             inp["query_rope"].reshape(case.T1, case.G, case.Dr) if case.Dr else None,
                             inp["key_rope"].reshape(case.T2, case.Dr) if case.Dr else None,
                             idx, inp["dout"].reshape(case.T1, case.G, case.D),
-                            inp["out"].reshape(case.T1, case.G, case.D), m, l, geom, case.block,
-                            case.mode, case.scale_value, tokens=tokens, keys=keys, rows=rows)
-    T = torch.as_tensor(tokens, device="cuda")
+                            inp["out"].reshape(case.T1, case.G, case.D),
+                            inp["softmax_max"].reshape(case.T1, case.G), inp["softmax_sum"].reshape(case.T1, case.G),
+                            geom, case.block, case.mode, case.scale_value, tokens=tokens, keys=keys, rows=rows)
     Kt = torch.as_tensor(keys, device="cuda")
     got = dict(dq=dq.reshape(case.T1, case.G, case.D)[T], dk=dk.reshape(case.T2, case.D)[Kt],
                dv=dv.reshape(case.T2, case.D)[Kt])
     if case.Dr:
         got["dqr"] = dqr.reshape(case.T1, case.G, case.Dr)[T]
         got["dkr"] = dkr.reshape(case.T2, case.Dr)[Kt]
-    errs = {}
+    worst, pooled = {}, {}
+    failures = []
     for n, x in got.items():
         x = x.float().cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(x)), n
-        errs[n] = rel_l2(x, ref[n])
-    print(case.name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    for n, e in errs.items():
-        assert e <= TOL[n], (n, e)
+        ids = tokens if n in ("dq", "dqr") else keys
+        norms = np.array([np.linalg.norm(ref[n][i]) for i in range(len(ids))])
+        floor = 0.01 * np.median(norms[norms > 0]) if np.any(norms > 0) else 1.0
+        errs = [float(np.linalg.norm(x[i] - ref[n][i]) / max(norms[i], floor)) for i in range(len(ids))]
+        i_w = int(np.argmax(errs))
+        worst[n] = dict(err=errs[i_w], row=int(ids[i_w]), tol=TOL[n])
+        pooled[n] = rel_l2(x, ref[n])
+        failures += [(n, int(ids[i]), e) for i, e in enumerate(errs) if not e <= TOL[n]]
+    rec = dict(workload=case.name, tokens=len(tokens), keys=len(keys), worst_row=worst, pooled=pooled)
+    print("MARGINS " + json.dumps(rec), flush=True)
+    out_dir = request.config.getoption("--margins-dir")
+    if out_dir:
+        os.makedirs(out_dir, exist_ok=True)
+        with open(os.path.join(out_dir, f"{case.name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    assert not failures, failures[:10]
     never = torch.as_tensor(counts == 0, device="cuda")
     for x, w in ((dk, case.D), (dv, case.D), (dkr, case.Dr)):
         if x is not None:

@@ -51,12 +51,14 @@ def _never_selected(case, inp):
     return ~sel
 
 
-def _run(case, seed, deterministic=None, inp=None):
+def _run(case, seed, deterministic=None, inp=None, options=None):
     if inp is None:
         inp = add_oracle_stats(case, si.make_inputs(case, seed))
     ref = oracle_backward(case, inp)
-    print(f"case {case.name} seed {seed} det={deterministic}", flush=True)
+    print(f"case {case.name} seed {seed} det={deterministic} options={options}", flush=True)
     kw = {} if deterministic is None else dict(deterministic=deterministic)
+    if options:
+        kw["options"] = options
     outs = call_backward(case, to_device(inp), **kw)
     torch.cuda.synchronize()
     got = _outs_np(case, outs)
@@ -119,14 +121,13 @@ def test_value_is_key(case):
 
 
 @pytest.mark.parametrize("name", ["g64_tnd_causal", "g128_zipf"])
-def test_token_paths_agree(monkeypatch, name):
+def test_token_paths_agree(name):
     """The fused token kernel (k_row, 64 heads per workgroup) and the split
     one (k_sdp + k_dq) both match the oracle on the same N1 >= 32 inputs."""
     case = next(c for c in SMALL if c.name == name)
     inp = add_oracle_stats(case, si.make_inputs(case, 21))
-    for path in ("row", "sdp"):
-        monkeypatch.setenv("SFAG_TOKEN_PATH", path)
-        _run(case, seed=21, inp=inp)
+    for path in ("fused", "split"):
+        _run(case, seed=21, inp=inp, options=dict(token_path=path))
 
 
 def test_duplicated_indices():
@@ -191,47 +192,46 @@ def test_deterministic_bitwise_and_parity():
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_deterministic_independent_of_chunking(monkeypatch):
+@pytest.mark.parametrize("path", ["keyblock", "partials"])
+def test_deterministic_independent_of_chunking(path):
+    """The deterministic bits do not depend on how the tokens are chunked
+    (chunk limit, workspace budget): every chunking gives the same bits as
+    one chunk, on both deterministic dK/dV paths."""
     inp = to_device(add_oracle_stats(DET_CASE, si.make_inputs(DET_CASE, 6)))
-    base = [o.clone() for o in call_backward(DET_CASE, inp, deterministic=True) if o is not None]
-    monkeypatch.setenv("SFAG_CHUNK_TOKENS", "7")
-    chunked = [o for o in call_backward(DET_CASE, inp, deterministic=True) if o is not None]
-    torch.cuda.synchronize()
-    # dQ never depends on chunking; dK/dV sums are regrouped per chunk, so they
-    # match to rounding, and each chunking is itself reproducible.
-    assert torch.equal(base[0], chunked[0])
-    for a, b in zip(base[1:], chunked[1:]):
-        assert rel_l2(a.float().cpu().numpy(), b.float().cpu().numpy()) < 1e-3
-    again = [o for o in call_backward(DET_CASE, inp, deterministic=True) if o is not None]
-    torch.cuda.synchronize()
-    for a, b in zip(chunked, again):
-        assert torch.equal(a, b)
+    base = [o.clone() for o in call_backward(DET_CASE, inp, deterministic=True, options=dict(scatter=path))
+            if o is not None]
+    for opts in (dict(chunk_tokens=7), dict(chunk_tokens=20), dict(workspace_budget=1 << 20)):
+        opts["scatter"] = path
+        print(f"det chunking {opts}", flush=True)
+        chunked = [o for o in call_backward(DET_CASE, inp, deterministic=True, options=opts) if o is not None]
+        torch.cuda.synchronize()
+        for a, b in zip(base, chunked):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), opts
 
 
 @pytest.mark.parametrize("path", ["keyblock", "atomic", "partials"])
 @pytest.mark.parametrize("chunk", [0, 9])
-def test_scatter_paths_agree(monkeypatch, path, chunk):
+def test_scatter_paths_agree(path, chunk):
     """Every dK/dV path (key-block contraction, fp32 atomics, per-pair rows with
     the CSR reduction), with and without token chunking, against the oracle."""
     case = si.Case("paths", S1=50, S2=300, G=64, K=60, mode=3, index_rule="causal_mix")
     inp = add_oracle_stats(case, si.make_inputs(case, 8))
     ref = oracle_backward(case, inp)
     dev = to_device(inp)
-    monkeypatch.setenv("SFAG_SCATTER", path)
+    opts = dict(scatter=path)
     if chunk:
-        monkeypatch.setenv("SFAG_CHUNK_TOKENS", str(chunk))
-    got = _outs_np(case, call_backward(case, dev, deterministic=False))
+        opts["chunk_tokens"] = chunk
+    got = _outs_np(case, call_backward(case, dev, deterministic=False, options=opts))
     _check(case, got, ref, label=f"paths {path} chunk {chunk}")
 
 
 @pytest.mark.parametrize("path", ["keyblock", "partials"])
-def test_deterministic_paths_bitwise(monkeypatch, path):
+def test_deterministic_paths_bitwise(path):
     case = si.Case("detpaths", S1=40, S2=260, G=32, K=50, mode=3, index_rule="zipf", deterministic=True)
     inp = to_device(add_oracle_stats(case, si.make_inputs(case, 4)))
-    monkeypatch.setenv("SFAG_SCATTER", path)
-    first = [o.clone() for o in call_backward(case, inp) if o is not None]
+    first = [o.clone() for o in call_backward(case, inp, options=dict(scatter=path)) if o is not None]
     for _ in range(2):
-        again = [o for o in call_backward(case, inp) if o is not None]
+        again = [o for o in call_backward(case, inp, options=dict(scatter=path)) if o is not None]
         torch.cuda.synchronize()
         for x, y in zip(first, again):
             assert torch.equal(x, y)
@@ -293,3 +293,61 @@ def test_reduced_configs(cfg):
     """Each workload's structure (heads, rope, dtype, layout, mask, index rule,
     block size, determinism) at a token count the oracle finishes in seconds."""
     _run(REDUCED[cfg], seed=si.seed_for(cfg))
+
+
+@pytest.mark.parametrize("G", [16, 64])
+def test_no_keys(G):
+    """S2 = 0: every position is masked, so dQ is 0 and the key gradients are
+    empty (the key-block path, which needs key rows, is not chosen)."""
+    case = si.Case(f"no_keys_g{G}", S1=6, S2=0, G=G, K=8)
+    inp = add_oracle_stats(case, si.make_inputs(case, 2))
+    _, ref, got, outs = _run(case, 2, inp=inp)
+    assert torch.all(outs[0] == 0) and outs[1].numel() == 0
+
+
+def test_validation_flags():
+    """Opt-in device checks: consistent inputs raise no flag and leave the
+    results unchanged; TND lengths that are negative or do not add up to
+    T1 / T2, and index entries at or past their sequence's key length, are
+    reported (such entries are masked, never read)."""
+    import top_sparse_attention_sfag_amd as sfag
+    case = si.Case("validate_tnd", layout="TND", B=3, seqlens_q=(5, 7, 4), seqlens_kv=(20, 10, 30), G=32, K=12,
+                   mode=3, index_rule="causal_mix")
+    inp = add_oracle_stats(case, si.make_inputs(case, 3))
+    dev = to_device(inp)
+    base = [o.clone() for o in call_backward(case, dev) if o is not None]
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    got = [o for o in call_backward(case, dev, options=dict(validate=True), workspace=ws) if o is not None]
+    assert sfag.validation_read(ws) == dict(flags=0, bad_entries=0)
+    for a, b in zip(base, got):
+        assert torch.equal(a, b)
+    # entries past the key length of their sequence
+    idx = dev["sparse_indices"].clone().view(case.T1, case.Kent)
+    geom = geom_of(case)
+    plant = [(0, 0, 25), (6, 3, 10), (6, 4, 11), (15, 0, 30)]   # (token, entry, value): Lk 20, 10, 10, 30
+    for t, j, val in plant:
+        idx[t, j] = val
+    bad = sum(1 for t, _j, val in plant if val >= geom["Lk"][t])
+    d2 = dict(dev, sparse_indices=idx.view_as(dev["sparse_indices"]))
+    call_backward(case, d2, options=dict(validate=True), workspace=ws)
+    assert sfag.validation_read(ws) == dict(flags=sfag.BAD_INDEX_RANGE, bad_entries=bad)
+    # lengths: a negative one, and sums that differ from T1 / T2
+    d3 = dict(dev, seqlens_q=torch.tensor([5, -1, 4], dtype=torch.int32, device="cuda"),
+              seqlens_kv=torch.tensor([20, 10, 31], dtype=torch.int32, device="cuda"))
+    call_backward(case, d3, options=dict(validate=True), workspace=ws)
+    r = sfag.validation_read(ws)
+    assert r["flags"] & (sfag.BAD_LENGTH_NEGATIVE | sfag.BAD_LENGTH_SUM_Q | sfag.BAD_LENGTH_SUM_KV) == \
+        sfag.BAD_LENGTH_NEGATIVE | sfag.BAD_LENGTH_SUM_Q | sfag.BAD_LENGTH_SUM_KV
+
+
+def test_auxiliary_stream_of_the_caller():
+    """A concurrent call on a second stream the caller passes gives the same
+    bits as the serial call."""
+    case = si.Case("aux_g64", S1=60, S2=300, G=64, K=60, mode=3, index_rule="causal_mix")
+    inp = to_device(add_oracle_stats(case, si.make_inputs(case, 12)))
+    serial = [o.clone() for o in call_backward(case, inp, options=dict(concurrent="off")) if o is not None]
+    aux = torch.cuda.Stream()
+    got = [o for o in call_backward(case, inp, options=dict(concurrent="on", aux_stream=aux)) if o is not None]
+    torch.cuda.synchronize()
+    for a, b in zip(serial, got):
+        assert torch.equal(a, b)

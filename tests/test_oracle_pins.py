@@ -429,3 +429,45 @@ def test_band_special_cases_and_entry_count():
                     # the formula bounds every alignment; equality holds whenever the
                     # worst alignment occurs among the Lk diagonals
                     assert need <= got <= need + 1, (Lk, pre, nxt, block, need, got)
+
+
+def test_flop_count():
+    """oracle.flops: 2 flop per multiply-add of the five contractions per valid
+    (head, position) pair, masked positions not counted.  Pinned by (a) the
+    per-pair figures the workload definition states (5504 with D = 512 and
+    Dr = 64, 5120 without rope) on a hand-counted row set, and (b) a scalar
+    loop that performs S = q·k, dP = dO·v, dQ += dS·k, dK += dS·q, dV += P·dO
+    for every valid pair and head of a tiny problem and counts its
+    multiplications."""
+    rows = np.array([[0, -1, 2, 5], [-1, -1, -1, -1], [7, 7, -1, 3]])   # 6 valid positions
+    assert orc.flops(rows, 3, 512, 64) == 6 * 3 * 5504
+    assert orc.flops(rows, 3, 512, 0) == 6 * 3 * 5120
+    assert orc.flops(np.full((2, 3), -1), 128, 512, 64) == 0
+
+    rng = np.random.default_rng(0)
+    for G, D, Dr in ((2, 3, 2), (1, 4, 0), (3, 2, 1)):
+        muls = 0
+        for t in range(rows.shape[0]):
+            for p in rows[t][rows[t] >= 0]:
+                kq = rng.standard_normal(D + Dr)
+                v = rng.standard_normal(D)
+                for h in range(G):
+                    q = rng.standard_normal(D + Dr)
+                    dO = rng.standard_normal(D)
+                    s = 0.0
+                    for c in range(D + Dr):          # S over D + Dr
+                        s += q[c] * kq[c]
+                        muls += 1
+                    dp = 0.0
+                    for c in range(D):               # dP over D
+                        dp += dO[c] * v[c]
+                        muls += 1
+                    ds, P = s * dp, s
+                    for c in range(D + Dr):          # dQ and dK over D + Dr
+                        _ = ds * kq[c]
+                        _ = ds * q[c]
+                        muls += 2
+                    for c in range(D):               # dV over D
+                        _ = P * dO[c]
+                        muls += 1
+        assert orc.flops(rows, G, D, Dr) == 2 * muls, (G, D, Dr)

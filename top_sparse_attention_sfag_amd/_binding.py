@@ -29,6 +29,52 @@ class SfagTensor(ctypes.Structure):
                 ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
 
 
+class SfagOptions(ctypes.Structure):
+    _fields_ = [("workspaceBudget", ctypes.c_uint64), ("chunkTokens", ctypes.c_int64), ("scatter", ctypes.c_int32),
+                ("tokenPath", ctypes.c_int32), ("tokenOrder", ctypes.c_int32), ("concurrent", ctypes.c_int32),
+                ("rowSplit", ctypes.c_int32), ("keyBlockRanges", ctypes.c_int32), ("validate", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("auxStream", ctypes.c_void_p)]
+
+
+class SfagValidation(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32), ("badEntries", ctypes.c_uint64)]
+
+
+# Names of the sfag_options values (include/sfag.h).
+SCATTER = {"auto": 0, "keyblock": 1, "partials": 2, "atomic": 3}
+TOKEN_PATH = {"auto": 0, "fused": 1, "split": 2}
+TOKEN_ORDER = {"auto": 0, "ascending": 1, "descending": 2}
+CONCURRENT = {"auto": 0, "off": 1, "on": 2}
+BAD_LENGTH_NEGATIVE, BAD_LENGTH_SUM_Q, BAD_LENGTH_SUM_KV, BAD_INDEX_RANGE = 1, 2, 4, 8
+
+
+def make_options(options=None):
+    """sfag_options from a dict with keys workspace_budget (bytes),
+    chunk_tokens, scatter, token_path, token_order, concurrent, row_split,
+    key_block_ranges, validate and aux_stream (a torch.cuda.Stream); None when
+    ``options`` is None or empty."""
+    if not options:
+        return None
+    known = {"workspace_budget", "chunk_tokens", "scatter", "token_path", "token_order", "concurrent", "row_split",
+             "key_block_ranges", "validate", "aux_stream"}
+    bad = set(options) - known
+    if bad:
+        raise SfagValueError(ERR_PARAM_INVALID, f"unknown options {sorted(bad)}")
+    o = SfagOptions()
+    o.workspaceBudget = int(options.get("workspace_budget", 0))
+    o.chunkTokens = int(options.get("chunk_tokens", 0))
+    o.scatter = SCATTER[options.get("scatter", "auto")]
+    o.tokenPath = TOKEN_PATH[options.get("token_path", "auto")]
+    o.tokenOrder = TOKEN_ORDER[options.get("token_order", "auto")]
+    o.concurrent = CONCURRENT[options.get("concurrent", "auto")]
+    o.rowSplit = int(options.get("row_split", 0))
+    o.keyBlockRanges = int(options.get("key_block_ranges", 0))
+    o.validate = 1 if options.get("validate", False) else 0
+    aux = options.get("aux_stream")
+    o.auxStream = aux.cuda_stream if aux is not None else None
+    return o
+
+
 class SfagError(Exception):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libsfag error {code}: {msg}")
@@ -67,6 +113,10 @@ def lib():
             ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p)]
         L.sfag_forward.restype = ctypes.c_int
         L.sfag_forward.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        L.sfag_plan_configure.restype = ctypes.c_int
+        L.sfag_plan_configure.argtypes = [ctypes.c_void_p, ctypes.POINTER(SfagOptions), ctypes.POINTER(ctypes.c_uint64)]
+        L.sfag_validation_read.restype = ctypes.c_int
+        L.sfag_validation_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(SfagValidation)]
         L.sfag_plan_destroy.restype = None
         L.sfag_plan_destroy.argtypes = [ctypes.c_void_p]
         L.sfag_last_error.restype = ctypes.c_char_p
@@ -139,8 +189,10 @@ def _raise(code: int):
 
 def plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, dq, dk, dv, *, dq_rope=None,
          dk_rope=None, seqlens_q=None, seqlens_kv=None, query_rope=None, key_rope=None, scale=None, block_size=1,
-         layout: Optional[str] = "BSND", sparse_mode=0, pre_tokens=WINDOW, next_tokens=WINDOW, deterministic=False):
-    """Phase 1: returns (workspace bytes, plan handle).  Reads no tensor data."""
+         layout: Optional[str] = "BSND", sparse_mode=0, pre_tokens=WINDOW, next_tokens=WINDOW, deterministic=False,
+         options=None):
+    """Phase 1: returns (workspace bytes, plan handle).  Reads no tensor data.
+    ``options`` (see make_options) re-plans with sfag_plan_configure."""
     if scale is None and query is not None:
         scale = 1.0 / (query.shape[-1] + (query_rope.shape[-1] if query_rope is not None else 0)) ** 0.5
     if scale is None:
@@ -155,7 +207,17 @@ def plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum,
         ctypes.byref(ws), ctypes.byref(p))
     if rc != OK:
         _raise(rc)
-    return int(ws.value), p
+    return _configure(p, ws, options), p
+
+
+def _configure(p, ws, options):
+    o = make_options(options)
+    if o is not None:
+        rc = lib().sfag_plan_configure(p, ctypes.byref(o), ctypes.byref(ws))
+        if rc != OK:
+            destroy(p)
+            _raise(rc)
+    return int(ws.value)
 
 
 def destroy(p):
@@ -170,36 +232,55 @@ def _stream_ptr(device, stream):
 
 def backward(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, *, seqlens_q=None,
              seqlens_kv=None, query_rope=None, key_rope=None, scale=None, block_size=1, layout="BSND", sparse_mode=0,
-             pre_tokens=WINDOW, next_tokens=WINDOW, deterministic=False, outputs=None, workspace=None, stream=None):
+             pre_tokens=WINDOW, next_tokens=WINDOW, deterministic=False, outputs=None, workspace=None, stream=None,
+             options=None):
     """Backward pass of top-k sparse flash attention on the GPU.
 
     Returns (dq, dk, dv, dq_rope, dk_rope); the rope gradients are None without
     rope inputs.  ``outputs`` may supply preallocated gradients and
-    ``workspace`` a uint8 device buffer of at least the planned size.
+    ``workspace`` a uint8 device buffer of at least the planned size; what is
+    allocated here is allocated on the stream the kernels run on.
+    ``options``: tuning choices (see make_options).
     """
     if not query.is_cuda:
         raise SfagValueError(ERR_PARAM_INVALID, "tensors must be on the GPU")
-    if outputs is None:
-        dq, dk, dv = torch.empty_like(query), torch.empty_like(key), torch.empty_like(value)
-        dqr = torch.empty_like(query_rope) if query_rope is not None else None
-        dkr = torch.empty_like(key_rope) if key_rope is not None else None
-    else:
-        dq, dk, dv, dqr, dkr = outputs
-    ws, p = plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, dq, dk, dv, dq_rope=dqr,
-                 dk_rope=dkr, seqlens_q=seqlens_q, seqlens_kv=seqlens_kv, query_rope=query_rope, key_rope=key_rope,
-                 scale=scale, block_size=block_size, layout=layout, sparse_mode=sparse_mode, pre_tokens=pre_tokens,
-                 next_tokens=next_tokens, deterministic=deterministic)
-    if workspace is None or workspace.numel() < ws:
-        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
+    s = stream if stream is not None else torch.cuda.current_stream(query.device)
+    with torch.cuda.stream(s):
+        if outputs is None:
+            dq, dk, dv = torch.empty_like(query), torch.empty_like(key), torch.empty_like(value)
+            dqr = torch.empty_like(query_rope) if query_rope is not None else None
+            dkr = torch.empty_like(key_rope) if key_rope is not None else None
+        else:
+            dq, dk, dv, dqr, dkr = outputs
+        ws, p = plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, dq, dk, dv, dq_rope=dqr,
+                     dk_rope=dkr, seqlens_q=seqlens_q, seqlens_kv=seqlens_kv, query_rope=query_rope,
+                     key_rope=key_rope, scale=scale, block_size=block_size, layout=layout, sparse_mode=sparse_mode,
+                     pre_tokens=pre_tokens, next_tokens=next_tokens, deterministic=deterministic, options=options)
+        if workspace is None or workspace.numel() < ws:
+            workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
     rc = lib().sfag_backward(ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()), p,
-                             _stream_ptr(query.device, stream))
+                             ctypes.c_void_p(s.cuda_stream))
     if rc != OK:
         _raise(rc)
     return dq, dk, dv, dqr, dkr
 
 
+def validation_read(workspace, stream=None):
+    """Result of the device-side input checks of a finished call planned with
+    options={"validate": True}: dict(flags=..., bad_entries=...).  Waits for
+    ``stream`` (default: the current stream)."""
+    s = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+    v = SfagValidation()
+    rc = lib().sfag_validation_read(ctypes.c_void_p(workspace.data_ptr()), ctypes.c_void_p(s.cuda_stream),
+                                    ctypes.byref(v))
+    if rc != OK:
+        _raise(rc)
+    return dict(flags=int(v.flags), bad_entries=int(v.badEntries))
+
+
 def forward(query, key, value, sparse_indices, *, seqlens_q=None, seqlens_kv=None, query_rope=None, key_rope=None,
-            scale=None, block_size=1, layout="BSND", sparse_mode=0, outputs=None, workspace=None, stream=None):
+            scale=None, block_size=1, layout="BSND", sparse_mode=0, outputs=None, workspace=None, stream=None,
+            options=None):
     """Forward pass on the GPU: returns (out, softmax_max, softmax_sum), the
     inputs the backward pass takes from the forward.  ``outputs`` may supply
     preallocated tensors of those shapes."""
@@ -207,27 +288,30 @@ def forward(query, key, value, sparse_indices, *, seqlens_q=None, seqlens_kv=Non
         raise SfagValueError(ERR_PARAM_INVALID, "tensors must be on the GPU")
     if scale is None:
         scale = 1.0 / (query.shape[-1] + (query_rope.shape[-1] if query_rope is not None else 0)) ** 0.5
-    if outputs is None:
-        G = query.shape[-2]
-        stats = (1, query.shape[0], G) if layout == "TND" else (query.shape[0], 1, query.shape[1], G)
-        out = torch.empty_like(query)
-        smax = torch.empty(stats, dtype=torch.float32, device=query.device)
-        ssum = torch.empty(stats, dtype=torch.float32, device=query.device)
-    else:
-        out, smax, ssum = outputs
-    ws = ctypes.c_uint64(0)
-    p = ctypes.c_void_p(None)
-    rc = lib().sfag_forward_workspace_size(
-        _desc(query), _desc(key), _desc(value), _desc(sparse_indices), _desc(seqlens_q), _desc(seqlens_kv),
-        _desc(query_rope), _desc(key_rope), float(scale), int(block_size), None if layout is None else layout.encode(),
-        int(sparse_mode), _desc(out), _desc(smax), _desc(ssum), ctypes.byref(ws), ctypes.byref(p))
-    if rc != OK:
-        _raise(rc)
-    ws = int(ws.value)
-    if workspace is None or workspace.numel() < ws:
-        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
+    s = stream if stream is not None else torch.cuda.current_stream(query.device)
+    with torch.cuda.stream(s):
+        if outputs is None:
+            G = query.shape[-2]
+            stats = (1, query.shape[0], G) if layout == "TND" else (query.shape[0], 1, query.shape[1], G)
+            out = torch.empty_like(query)
+            smax = torch.empty(stats, dtype=torch.float32, device=query.device)
+            ssum = torch.empty(stats, dtype=torch.float32, device=query.device)
+        else:
+            out, smax, ssum = outputs
+        ws = ctypes.c_uint64(0)
+        p = ctypes.c_void_p(None)
+        rc = lib().sfag_forward_workspace_size(
+            _desc(query), _desc(key), _desc(value), _desc(sparse_indices), _desc(seqlens_q), _desc(seqlens_kv),
+            _desc(query_rope), _desc(key_rope), float(scale), int(block_size),
+            None if layout is None else layout.encode(), int(sparse_mode), _desc(out), _desc(smax), _desc(ssum),
+            ctypes.byref(ws), ctypes.byref(p))
+        if rc != OK:
+            _raise(rc)
+        ws = _configure(p, ws, options)
+        if workspace is None or workspace.numel() < ws:
+            workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
     rc = lib().sfag_forward(ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()), p,
-                            _stream_ptr(query.device, stream))
+                            ctypes.c_void_p(s.cuda_stream))
     if rc != OK:
         _raise(rc)
     return out, smax, ssum

@@ -29,12 +29,13 @@ static void carve(uint64_t& cursor, uint64_t& field, uint64_t bytes) {
   cursor = align256(cursor + bytes);
 }
 
-WorkspaceLayout layout_for(const Dims& d, int32_t scatter) {
+WorkspaceLayout layout_for(const Dims& d, int32_t scatter, bool validate) {
   const bool partials = scatter == kScatterPartials;
   const bool keyblock = scatter == kScatterKeyBlock;
   WorkspaceLayout w;
   uint64_t c = 0;
   const uint64_t ch = (uint64_t)d.chunk, E = (uint64_t)d.E;
+  carve(c, w.status, validate ? 16 : 0);
   carve(c, w.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
   carve(c, w.delta, (uint64_t)d.T1 * d.G * 4);
   carve(c, w.acc, (uint64_t)d.T2 * d.AW * 4);
@@ -124,12 +125,6 @@ bool same_shape(const sfag_tensor* a, const sfag_tensor* b) {
   for (int i = 0; i < a->ndim; ++i)
     if (a->shape[i] != b->shape[i]) return false;
   return true;
-}
-
-int64_t env_i64(const char* name, int64_t dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::strtoll(s, nullptr, 10);
 }
 
 constexpr int64_t kMaxTokensPerSeq = 131072;  // 规格约束: S1, S2 up to 128K
@@ -294,12 +289,94 @@ extern "C" int sfag_workspace_size(
   p->deterministic = deterministic;
   p->scale = (float)scaleValue;
 
+  p->scatter = kScatterAtomic;
+  p->d = d;
+  const int rc = plan_launch(p);
+  if (rc != SFAG_OK) {
+    delete p;
+    return rc;
+  }
+  *workspaceSize = p->ws.total;
+  *plan = p;
+  return SFAG_OK;
+}
+
+namespace sfag {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest chunk (a multiple of `tr` tokens, at least `tr`) whose workspace
+// fixed + chunk * per_tok + (chunk / tr) * per_range stays within `budget`.
+int64_t chunk_within(uint64_t budget, uint64_t fixed, uint64_t per_tok, uint64_t per_range, int64_t tr) {
+  const uint64_t unit = (uint64_t)tr * per_tok + per_range;
+  if (budget <= fixed || unit == 0) return tr;
+  const uint64_t n = (budget - fixed) / unit;
+  return (int64_t)std::max<uint64_t>(1, std::min<uint64_t>(n, (uint64_t)1 << 40)) * tr;
+}
+
+// Chunk of at most `cmax` tokens (a multiple of tr) that splits T1 into equal
+// chunks: as many chunks as cmax forces, each a whole number of ranges.
+int64_t balanced_chunk(int64_t T1, int64_t cmax, int64_t tr) {
+  const int64_t n = ceil_div(T1, cmax);
+  return std::min<int64_t>(cmax, ceil_div(ceil_div(T1, n), tr) * tr);
+}
+
+}  // namespace
+
+int plan_launch(sfag_plan* p) {
+  Dims& d = p->d;
+  const sfag_options& o = p->opt;
+  const bool validate = o.validate != 0;
+  d.chunk = 0;
+  d.TR = d.nTR = 0;
+  d.row_split = 1;
+  d.kb_sort_bits = 0;
+  d.nKB = (d.T2 + kKeyBlockRows - 1) / kKeyBlockRows;
+  // Bytes that do not scale with the chunk: validation word, TND offsets,
+  // Delta, accumulators (and the CSR offsets of the partials path).
+  auto fixed_bytes = [&](bool partials) {
+    uint64_t f = (validate ? 256 : 0) + (d.layout == 1 ? align256(2 * (uint64_t)(d.B + 1) * 4) : 0);
+    if (!p->forward) f += align256((uint64_t)d.T1 * d.G * 4) + align256((uint64_t)d.T2 * d.AW * 4);
+    if (partials) f += align256((uint64_t)(d.T2 + 1) * 4);
+    return f + (64u << 10);   // alignment of the remaining regions
+  };
+  // pair numbering: chunk * E and the key-block sort key stay below 2^31
+  const int64_t pair_cap = d.E > 0 ? 0x7fffffffLL / d.E : ((int64_t)1 << 40);
+
+  if (p->forward) {
+    p->scatter = kScatterAtomic;
+    if (d.T1 == 0) {
+      p->ws = WorkspaceLayout();
+      if (validate) {
+        uint64_t c = 0;
+        carve(c, p->ws.status, 16);
+        carve(c, p->ws.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
+        p->ws.total = c;
+      }
+      return SFAG_OK;
+    }
+    const uint64_t budget = o.workspaceBudget ? o.workspaceBudget : kDefaultForwardBudget;
+    int64_t cmax = chunk_within(budget, fixed_bytes(false), 4 + (uint64_t)d.E * 4, 0, 1);
+    if (o.chunkTokens > 0) cmax = std::min<int64_t>(cmax, o.chunkTokens);
+    cmax = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(cmax, pair_cap), d.T1));
+    d.chunk = balanced_chunk(d.T1, cmax, 1);
+    WorkspaceLayout w;
+    uint64_t c = 0;
+    carve(c, w.status, validate ? 16 : 0);
+    carve(c, w.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
+    carve(c, w.nvalid, (uint64_t)d.chunk * 4);
+    carve(c, w.rows, (uint64_t)d.chunk * d.E * 4);
+    w.total = c;
+    p->ws = w;
+    return SFAG_OK;
+  }
+
   // dK/dV path.  When a token selects a sizeable fraction of the keys it can
   // reach (estimated from the shapes alone), the key-block contraction wins:
   // it moves no per-pair rows and is deterministic.  Otherwise the per-pair
   // rows go through the CSR reduction (deterministic) or fp32 atomics.
-  // SFAG_SCATTER=atomic|partials|keyblock overrides the choice (the atomic
-  // path is never used when deterministic is requested).
   {
     double reach;  // average number of key positions a token may select
     if (d.layout == 0) {
@@ -310,89 +387,88 @@ extern "C" int sfag_workspace_size(
     }
     if (reach < 1.0) reach = 1.0;
     const double density = (double)d.E / reach;
-    int32_t sc = density >= 0.125 ? kScatterKeyBlock : (deterministic ? kScatterPartials : kScatterAtomic);
-    const char* env = std::getenv("SFAG_SCATTER");
-    if (env && std::strcmp(env, "keyblock") == 0) sc = kScatterKeyBlock;
-    if (env && std::strcmp(env, "partials") == 0) sc = kScatterPartials;
-    if (env && std::strcmp(env, "atomic") == 0) sc = deterministic ? kScatterPartials : kScatterAtomic;
+    const int32_t other = p->deterministic ? kScatterPartials : kScatterAtomic;
+    int32_t sc = density >= 0.125 ? kScatterKeyBlock : other;
+    if (o.scatter == SFAG_SCATTER_KEYBLOCK) sc = kScatterKeyBlock;
+    if (o.scatter == SFAG_SCATTER_PARTIALS) sc = kScatterPartials;
+    if (o.scatter == SFAG_SCATTER_ATOMIC) sc = other;
     // the key-block kernel addresses one token's dS/P rows (E x Gp halves)
-    // through a buffer resource with a 31-bit size
-    if (sc == kScatterKeyBlock && (uint64_t)d.E * (uint64_t)d.Gp * 2 > 0x7fffffffULL)
-      sc = deterministic ? kScatterPartials : kScatterAtomic;
+    // through a buffer resource with a 31-bit size, and needs key rows
+    if (sc == kScatterKeyBlock && ((uint64_t)d.E * (uint64_t)d.Gp * 2 > 0x7fffffffULL || d.nKB == 0)) sc = other;
     p->scatter = sc;
   }
   const bool partials = p->scatter == kScatterPartials;
   const bool keyblock = p->scatter == kScatterKeyBlock;
-
-  if (d.T1 == 0) {  // empty query: the outputs are zero-filled, no workspace
-    d.chunk = 0;
-    p->d = d;
+  if (d.T1 == 0) {  // empty query: the outputs are zero-filled, no workspace beyond validation
     p->ws = WorkspaceLayout();
-    *workspaceSize = 0;
-    *plan = p;
+    if (validate) {
+      uint64_t c = 0;
+      carve(c, p->ws.status, 16);
+      carve(c, p->ws.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
+      p->ws.total = c;
+    }
     return SFAG_OK;
   }
-  // Tokens per chunk: the chunk's buffers (index rows, dS/P, and for the
-  // partials scatter the partial rows and the sort buffers) within a budget
-  // (48 GiB by default: a sixth of one MI355X's 288 GB of HBM; fewer, larger
-  // chunks amortise each launch's tail — 128 heads, 32768 tokens, top-8192:
-  // 4 chunks instead of 10 at 16 GiB, 346 vs 355 ms; 16 heads, 2 x 16384
-  // tokens, 512 blocks of 16: one chunk instead of two, 157 vs 171 ms).
+  // Chunk-sized bytes per token: index rows, dS and P (and for the partials
+  // scatter the per-pair rows and the sort buffers; for the key-block path
+  // the sort and visit buffers and the transposed Q|Qr and dO copies).
   uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
   if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
   if (keyblock) per_tok += 8 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
-  const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 49152);
-  int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
-  const int64_t forced = env_i64("SFAG_CHUNK_TOKENS", 0);
-  if (forced > 0) chunk = forced;
-  if (chunk < 1) chunk = 1;
-  if (chunk > d.T1) chunk = d.T1;
-  if (d.E > 0 && chunk > (int64_t)(0x7fffffffLL / d.E)) chunk = 0x7fffffffLL / d.E;
-  if (chunk < 1) {
-    delete p;
-    return fail(SFAG_ERR_TILING, "K * sparseBlockSize too large for 32-bit pair indices");
+  const uint64_t fixed = fixed_bytes(partials);
+  // the key-block sort key (key block * chunk + token) stays below 2^31
+  const int64_t cap = keyblock ? std::min<int64_t>(pair_cap, 0x7ffffffeLL / std::max<int64_t>(1, d.nKB)) : pair_cap;
+  if (cap < 1) return fail(SFAG_ERR_TILING, "K * sparseBlockSize too large for 32-bit pair indices");
+  int64_t tr = 1;
+  uint64_t part_bytes = 0;
+  if (keyblock) {
+    // Token ranges of the key-block kernel, fixed in absolute token
+    // coordinates from the shapes alone (never from the budget or the
+    // chunking, so that the deterministic sums keep one order): the default
+    // chunk (what the default budget holds, balanced over T1) split into
+    // keyBlockRanges ranges (16: the XCD snake pairs ranges x and 15 - x),
+    // fewer when that would leave under 8 tokens per range or need more than
+    // 4 GiB of fp32 range partials per chunk.
+    part_bytes = (uint64_t)d.T2 * d.AW * 4;
+    int64_t ranges = o.keyBlockRanges > 0 ? o.keyBlockRanges : kDefaultRanges;
+    if (part_bytes > 0) ranges = std::min<int64_t>(ranges, std::max<int64_t>(1, (int64_t)((4ull << 30) / part_bytes)));
+    int64_t cdef = chunk_within(kDefaultBudget > ranges * part_bytes ? kDefaultBudget - ranges * part_bytes : 0,
+                                fixed, per_tok, 0, 1);
+    cdef = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(cdef, cap), d.T1));
+    cdef = balanced_chunk(d.T1, cdef, 1);
+    ranges = std::max<int64_t>(1, std::min<int64_t>(ranges, cdef / 8));
+    tr = ceil_div(cdef, ranges);
   }
-  d.chunk = chunk;
+  const uint64_t budget = o.workspaceBudget ? o.workspaceBudget : kDefaultBudget;
+  int64_t cmax = chunk_within(budget, fixed, per_tok, part_bytes, tr);
+  if (o.chunkTokens > 0) cmax = std::min<int64_t>(cmax, std::max<int64_t>(tr, o.chunkTokens / tr * tr));
+  cmax = std::min<int64_t>(cmax, std::max<int64_t>(tr, cap / tr * tr));
+  cmax = std::min<int64_t>(cmax, ceil_div(d.T1, tr) * tr);
+  if (cmax > cap) return fail(SFAG_ERR_TILING, "K * sparseBlockSize too large for 32-bit pair indices");
+  d.chunk = balanced_chunk(d.T1, cmax, tr);
   // With few tokens (the fused token kernel, N1 <= 16, gives one workgroup
   // per token) a token's positions are split over up to 4 workgroups, each
   // at least 64 positions, which add their dQ|dQrope sums into an fp32
   // buffer (4 heads, 128 tokens, top-1024 of 2048 keys: token kernel 0.200
-  // ms unsplit, 0.126 ms in 4 shares, 0.140 ms in 8); SFAG_ROW_SPLIT
-  // overrides (at most 8).  The
-  // shares' atomic sums have no fixed order, so deterministic calls never
-  // split.
-  if (d.Gp < 32 && !deterministic) {
-    int64_t sp = std::min<int64_t>(4, std::min<int64_t>((1024 + chunk - 1) / chunk, d.E / 64));
-    sp = env_i64("SFAG_ROW_SPLIT", sp);
+  // ms unsplit, 0.126 ms in 4 shares, 0.140 ms in 8).  The shares' atomic
+  // sums have no fixed order, so deterministic calls never split.
+  if (d.Gp < 32 && !p->deterministic) {
+    int64_t sp = std::min<int64_t>(4, std::min<int64_t>(ceil_div(1024, d.chunk), d.E / 64));
+    if (o.rowSplit > 0) sp = o.rowSplit;
     d.row_split = (int32_t)std::max<int64_t>(1, std::min<int64_t>(8, sp));
   }
-  d.nKB = (d.T2 + kKeyBlockRows - 1) / kKeyBlockRows;
   if (keyblock) {
-    // 16 token ranges per chunk (the XCD snake pairs ranges x and 15 - x;
-    // SFAG_KB_RANGES overrides the count), fewer when that would leave under
-    // 8 tokens per range or need more than 4 GiB of fp32 partials.  The
-    // key-block sort key must fit in 31 bits.
-    int64_t ntr = std::max<int64_t>(1, env_i64("SFAG_KB_RANGES", 16));
-    const int64_t part_bytes = d.T2 * (2 * d.D + d.Dr) * 4;
-    if (part_bytes > 0) ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, (4LL << 30) / part_bytes));
-    ntr = std::min<int64_t>(ntr, std::max<int64_t>(1, chunk / 8));
-    d.TR = (chunk + ntr - 1) / ntr;
-    d.nTR = (chunk + d.TR - 1) / d.TR;
-    const int64_t sentinel = d.nKB * chunk;
-    if (sentinel >= 0x7fffffffLL) {
-      delete p;
-      return fail(SFAG_ERR_TILING, "key-block sort key exceeds 31 bits; lower SFAG_WORKSPACE_BUDGET_MB");
-    }
+    d.TR = tr;
+    d.nTR = ceil_div(d.chunk, tr);
     int kbits = 1;
     while (((int64_t)1 << kbits) <= d.nKB) ++kbits;  // the sort runs over key-block ids only
     d.kb_sort_bits = kbits;
   }
-  p->d = d;
-  p->ws = layout_for(d, p->scatter);
-  *workspaceSize = p->ws.total;
-  *plan = p;
+  p->ws = layout_for(d, p->scatter, validate);
   return SFAG_OK;
 }
+
+}  // namespace sfag
 
 // Forward pass (produces out, softmaxMax, softmaxSum).  The shared inputs and
 // the three outputs obey the same rules as in the backward call, so the
@@ -416,33 +492,45 @@ extern "C" int sfag_forward_workspace_size(
                                      sparseMode, kWindow, kWindow, false, query, key, value, queryRope, keyRope,
                                      &ws, &p);
   if (rc != SFAG_OK) return rc;
-  Dims d = p->d;
   p->forward = true;
   p->out_w = out->data;
   p->smax_w = softmaxMax->data;
   p->ssum_w = softmaxSum->data;
-  if (d.T1 == 0) {
-    p->d = d;
-    p->ws = WorkspaceLayout();
-    *workspaceSize = 0;
-    *plan = p;
-    return SFAG_OK;
+  const int rc2 = plan_launch(p);
+  if (rc2 != SFAG_OK) {
+    delete p;
+    return rc2;
   }
-  const uint64_t per_tok = 4 + (uint64_t)d.E * 4;
-  const int64_t budget_mb = env_i64("SFAG_WORKSPACE_BUDGET_MB", 16384);
-  int64_t chunk = (int64_t)(((uint64_t)budget_mb << 20) / per_tok);
-  if (chunk < 1) chunk = 1;
-  if (chunk > d.T1) chunk = d.T1;
-  d.chunk = chunk;
-  WorkspaceLayout w;
-  uint64_t c = 0;
-  carve(c, w.seq_off, d.layout == 1 ? 2 * (uint64_t)(d.B + 1) * 4 : 0);
-  carve(c, w.nvalid, (uint64_t)chunk * 4);
-  carve(c, w.rows, (uint64_t)chunk * d.E * 4);
-  w.total = c;
-  p->d = d;
-  p->ws = w;
-  *workspaceSize = w.total;
+  *workspaceSize = p->ws.total;
   *plan = p;
+  return SFAG_OK;
+}
+
+extern "C" int sfag_plan_configure(sfag_plan* plan, const sfag_options* options, uint64_t* workspaceSize) {
+  set_error("");
+  if (!plan || !workspaceSize) return fail(SFAG_ERR_NULLPTR, "plan or workspaceSize is NULL");
+  const sfag_options o = options ? *options : sfag_options{};
+  if (o.scatter < SFAG_SCATTER_AUTO || o.scatter > SFAG_SCATTER_ATOMIC)
+    return fail(SFAG_ERR_PARAM_INVALID, "options.scatter must be one of SFAG_SCATTER_*");
+  if (o.tokenPath < SFAG_TOKEN_AUTO || o.tokenPath > SFAG_TOKEN_SPLIT)
+    return fail(SFAG_ERR_PARAM_INVALID, "options.tokenPath must be one of SFAG_TOKEN_*");
+  if (o.tokenOrder < SFAG_ORDER_AUTO || o.tokenOrder > SFAG_ORDER_DESCENDING)
+    return fail(SFAG_ERR_PARAM_INVALID, "options.tokenOrder must be one of SFAG_ORDER_*");
+  if (o.concurrent < SFAG_CONCURRENT_AUTO || o.concurrent > SFAG_CONCURRENT_ON)
+    return fail(SFAG_ERR_PARAM_INVALID, "options.concurrent must be one of SFAG_CONCURRENT_*");
+  if (o.rowSplit < 0 || o.rowSplit > 8) return fail(SFAG_ERR_PARAM_INVALID, "options.rowSplit must be 0..8");
+  if (o.keyBlockRanges < 0 || o.keyBlockRanges > 1024)
+    return fail(SFAG_ERR_PARAM_INVALID, "options.keyBlockRanges must be 0..1024");
+  if (o.chunkTokens < 0) return fail(SFAG_ERR_PARAM_INVALID, "options.chunkTokens must be >= 0");
+  if (o.validate != 0 && o.validate != 1) return fail(SFAG_ERR_PARAM_INVALID, "options.validate must be 0 or 1");
+  const sfag_options old = plan->opt;
+  plan->opt = o;
+  const int rc = plan_launch(plan);
+  if (rc != SFAG_OK) {
+    plan->opt = old;
+    (void)plan_launch(plan);
+    return rc;
+  }
+  *workspaceSize = plan->ws.total;
   return SFAG_OK;
 }

@@ -70,12 +70,13 @@ void launch_band_indices(int32_t* idx, int64_t T1, int64_t K, int32_t block, int
                          const int32_t* lq, const int32_t* lk, int32_t B, int64_t pre, int64_t nxt, hipStream_t s);
 void launch_dq_cast(int32_t dtype, const float* acc, int64_t t0, int64_t ntok, int64_t G, int32_t Dr, float mul,
                     void* dq, void* dqr, hipStream_t s);
-void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int32_t* q_off, int32_t* kv_off,
-                        hipStream_t s);
+// status (optional): the 16-byte validation word (flags, reserved, count).
+void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int64_t T1, int64_t T2, int32_t* q_off,
+                        int32_t* kv_off, uint32_t* status, hipStream_t s);
 void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, int64_t nrows, hipStream_t s);
 void launch_fill_u32(void* p, uint64_t n, uint32_t v, hipStream_t s);
 void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, const int32_t* q_off,
-                   const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s);
+                   const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s, uint32_t* status = nullptr);
 // Stable radix sort of the chunk's valid pairs.  key_mode 0: by key row (then
 // csr_off gets the per-key offsets); key_mode 1: by (key row / kKeyBlock) *
 // ntok + token (csr_off may be NULL).  Invalid positions sort last.

@@ -54,9 +54,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* l) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
 }
 // (LDS destinations are 32-bit LDS addresses, wave-uniform.)
-// Copy through a buffer resource: a lane whose offset lies past the
-// resource's size fetches nothing (bounds-checked buffer access) and lands
-// zeros, so rows that are never used cost no memory traffic.
+// Copy through a buffer resource: a lane whose offset lies at or past the
+// resource's num_records (a raw buffer: stride 0) fails the buffer range
+// check, so it fetches nothing and its load returns zero (the AMD Instinct
+// CDNA instruction set reference, buffer addressing and range checking), and
+// the LDS slot it writes receives zeros: rows that are never used cost no
+// memory traffic.
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t l) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(l) : "memory");
 }
@@ -193,8 +196,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // instructions, wave w issuing w, w+4, w+8, w+12; the lane writing position
   // p of row r fetches chunk p ^ ((r >> 2) & 3).  Rows not selected (and
   // chunks past the heads) take an offset outside the resource: they fetch
-  // nothing, and their slots are never read.  B: the block's columns x 4
-  // chunks likewise, NB per wave.
+  // nothing and their slots receive zeros, which the MFMAs read as such.
+  // B: the block's columns x 4 chunks likewise, NB per wave.
   // The copies of one stage, prepared once (slot-map entries read, buffer
   // resources made) and then issued one A and one B instruction at a time
   // between the MFMAs of the stage being computed: a burst of copies at the

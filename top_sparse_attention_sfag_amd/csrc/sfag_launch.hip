@@ -83,16 +83,19 @@ void prof_drain() {
   g_prof_pending.clear();
 }
 
-// A second stream per device (default priority, non-blocking) and a pair of
-// events, made on first use and kept for the life of the process: k_dq runs
-// on it beside the key-block work, so each fills the other's tail.
+// A second stream per device (default priority, non-blocking) and four
+// events, made on first use and kept for the life of the process: the
+// key-block pre-work runs on it beside k_sdp, and with fewer than 128 heads
+// k_dq beside the key-block kernels, so that each fills the other's tail.
+enum SideEvent { kEvFork = 0, kEvPre = 1, kEvSdp = 2, kEvDq = 3, kNumSideEvents = 4 };
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t ev[kNumSideEvents] = {};
 };
 std::mutex g_side_mu;
 std::map<int, SideStream> g_side;
 
+// The library's second stream of the current device (made on first use).
 const SideStream* side_stream() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
@@ -101,9 +104,8 @@ const SideStream* side_stream() {
   if (it != g_side.end()) return &it->second;
   SideStream ss;
   if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-    return nullptr;
+  for (hipEvent_t& e : ss.ev)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
   return &(g_side[dev] = ss);
 }
 
@@ -129,6 +131,32 @@ extern "C" int sfag_profile_read(const char* name, double* total_ms, int64_t* la
   return SFAG_OK;
 }
 
+namespace {
+
+// Validating plans: the 16-byte result word at the start of the workspace,
+// cleared on the call's stream (a fill kernel, so that the call can be
+// captured in a graph).  NULL otherwise.
+uint32_t* start_validation(const sfag_plan* plan, void* workspace, hipStream_t s) {
+  if (!plan->opt.validate) return nullptr;
+  uint32_t* st = at<uint32_t>(workspace, plan->ws.status);
+  launch_fill_u32(st, 4, 0u, s);
+  return st;
+}
+
+}  // namespace
+
+extern "C" int sfag_validation_read(const void* workspace, void* stream, sfag_validation* result) {
+  set_error("");
+  if (!workspace || !result) return fail(SFAG_ERR_NULLPTR, "workspace or result is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sfag_validation v{};
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(SFAG_ERR_RUNTIME, "copy of the validation result failed");
+  *result = v;
+  return SFAG_OK;
+}
+
 extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream) {
   set_error("");
   std::unique_ptr<sfag_plan> own(plan);
@@ -140,14 +168,16 @@ extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* 
   if (w.total > 0 && !workspace) return fail(SFAG_ERR_NULLPTR, "workspace is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (d.T1 == 0) return SFAG_OK;
+  uint32_t* status = start_validation(plan, workspace, s);
   int32_t* q_off = nullptr;
   int32_t* kv_off = nullptr;
-  if (d.layout == 1) {
+  if (d.layout == 1 && (d.T1 > 0 || status)) {
     q_off = at<int32_t>(workspace, w.seq_off);
     kv_off = q_off + (d.B + 1);
-    launch_seq_offsets((const int32_t*)plan->lq, (const int32_t*)plan->lk, (int32_t)d.B, q_off, kv_off, s);
+    launch_seq_offsets((const int32_t*)plan->lq, (const int32_t*)plan->lk, (int32_t)d.B, d.T1, d.T2, q_off, kv_off,
+                       status, s);
   }
+  if (d.T1 == 0) return check_launch("validation");
   FwdArgs fa;
   fa.q = (const uint16_t*)plan->q;
   fa.qr = (const uint16_t*)plan->qr;
@@ -170,7 +200,7 @@ extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* 
     const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
     {
       TimedScope ts("decode", s);
-      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s);
+      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s, status);
     }
     fa.t0 = t0;
     fa.ntok = ntok;
@@ -193,20 +223,21 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   (void)hipGetLastError();
   const bool rope = d.Dr > 0;
 
+  uint32_t* status = start_validation(plan, workspace, s);
+  int32_t* q_off = nullptr;
+  int32_t* kv_off = nullptr;
+  if (d.layout == 1 && (d.T1 > 0 || status)) {
+    q_off = at<int32_t>(workspace, w.seq_off);
+    kv_off = q_off + (d.B + 1);
+    TimedScope ts("seq_offsets", s);
+    launch_seq_offsets((const int32_t*)plan->lq, (const int32_t*)plan->lk, (int32_t)d.B, d.T1, d.T2, q_off, kv_off,
+                       status, s);
+  }
   if (d.T1 == 0) {  // empty query (约束说明: return directly); dK/dV are still defined as 0
     launch_fill_u32(plan->dk, (uint64_t)d.T2 * d.D / 2, 0u, s);
     launch_fill_u32(plan->dv, (uint64_t)d.T2 * d.D / 2, 0u, s);
     if (rope) launch_fill_u32(plan->dkr, (uint64_t)d.T2 * d.Dr / 2, 0u, s);
     return check_launch("zero fill");
-  }
-
-  int32_t* q_off = nullptr;
-  int32_t* kv_off = nullptr;
-  if (d.layout == 1) {
-    q_off = at<int32_t>(workspace, w.seq_off);
-    kv_off = q_off + (d.B + 1);
-    TimedScope ts("seq_offsets", s);
-    launch_seq_offsets((const int32_t*)plan->lq, (const int32_t*)plan->lk, (int32_t)d.B, q_off, kv_off, s);
   }
   float* delta = at<float>(workspace, w.delta);
   float* acc = at<float>(workspace, w.acc);
@@ -215,12 +246,11 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   uint16_t* ds = at<uint16_t>(workspace, w.ds);
   uint16_t* pb = at<uint16_t>(workspace, w.p);
   // Token side: k_row (fused, 64 heads per workgroup) or k_sdp + k_dq (up to
-  // 128 heads per workgroup).  SFAG_TOKEN_PATH=row|sdp overrides.
+  // 128 heads per workgroup; N1 >= 32).
+  const sfag_options& o = plan->opt;
   bool use_row = d.Gp < 32;
-  if (const char* tp = std::getenv("SFAG_TOKEN_PATH")) {
-    if (std::string(tp) == "row") use_row = true;
-    if (std::string(tp) == "sdp" && d.Gp >= 32) use_row = false;
-  }
+  if (o.tokenPath == SFAG_TOKEN_FUSED) use_row = true;
+  if (o.tokenPath == SFAG_TOKEN_SPLIT && d.Gp >= 32) use_row = false;
   if (use_row) {   // k_row reads Delta; k_sdp forms it from dO and O itself
     TimedScope ts("delta", s);
     launch_delta(plan->dtype, plan->dout, plan->out, delta, d.T1 * d.G, s);
@@ -262,9 +292,10 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   ra.dq_mul = plan->scale / ds_scale;
   ra.n_split = 1;
   ra.dq_acc = nullptr;
-  // causal rows grow with the token: longest tokens first (SFAG_TOKEN_ORDER=fwd|rev overrides)
+  // causal rows grow with the token: longest tokens first
   ra.reverse = d.mode == 3 ? 1 : 0;
-  if (const char* to = std::getenv("SFAG_TOKEN_ORDER")) ra.reverse = std::string(to) == "rev" ? 1 : 0;
+  if (o.tokenOrder == SFAG_ORDER_ASCENDING) ra.reverse = 0;
+  if (o.tokenOrder == SFAG_ORDER_DESCENDING) ra.reverse = 1;
 
   ColArgs ca;
   ca.q = ra.q;
@@ -290,47 +321,90 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
     vals[1] = at<int32_t>(workspace, w.sort_vals[1]);
   }
 
-  // k_dq on a second stream beside the key-block kernels when the head count
-  // is below 128 (measured: 64 heads, 8192 varlen tokens, top-2048 causal,
-  // 10.8 -> 9.6 ms; with 128 heads no gain at 4096 tokens and +3% at 32768);
-  // SFAG_CONCURRENT=0|1 overrides.
-  bool concurrent = d.Gp < 128;
-  if (const char* cc = std::getenv("SFAG_CONCURRENT")) concurrent = std::string(cc) == "1";
-  const SideStream* side = concurrent ? side_stream() : nullptr;
+  // A second stream on the key-block path: the pre-work of the key-block
+  // kernel (transposed Q|Qrope and dO copies, the sort of the pairs by key
+  // block, the visit list) needs only the decoded indices, so it runs beside
+  // k_sdp; with fewer than 128 heads k_dq also runs beside the key-block
+  // kernels (64 heads, 8192 varlen tokens, top-2048 causal: 10.8 -> 9.6 ms;
+  // with 128 heads no gain at 4096 tokens and +3% at 32768, so off there).
+  // The caller's auxiliary stream if it gave one (with events of the call's
+  // own), else the library's, whose events this call holds for its whole
+  // enqueue sequence.
+  const bool kb_work = keyblock && d.E > 0;
+  bool concurrent = kb_work && o.concurrent != SFAG_CONCURRENT_OFF;
+  const bool dq_side = concurrent && !use_row && (d.Gp < 128 || o.concurrent == SFAG_CONCURRENT_ON);
+  SideStream own_side;
+  struct OwnEvents {
+    hipEvent_t e[kNumSideEvents] = {};
+    ~OwnEvents() {
+      for (hipEvent_t x : e)
+        if (x) (void)hipEventDestroy(x);
+    }
+  } own_events;
+  const SideStream* side = nullptr;
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  if (concurrent && o.auxStream) {
+    own_side.s = static_cast<hipStream_t>(o.auxStream);
+    for (int i = 0; i < kNumSideEvents; ++i) {
+      if (hipEventCreateWithFlags(&own_events.e[i], hipEventDisableTiming) != hipSuccess)
+        return fail(SFAG_ERR_RUNTIME, "events for the auxiliary stream could not be made");
+      own_side.ev[i] = own_events.e[i];
+    }
+    side = &own_side;
+  } else if (concurrent) {
+    side = side_stream();
+    if (side) side_lock.lock();
+  }
+  // stream b waits for the work enqueued so far on stream a
+  auto order = [&](hipStream_t a, hipStream_t b, SideEvent e) {
+    return hipEventRecord(side->ev[e], a) == hipSuccess && hipStreamWaitEvent(b, side->ev[e], 0) == hipSuccess;
+  };
+  uint16_t* qT = keyblock ? at<uint16_t>(workspace, w.qT) : nullptr;
+  uint16_t* oT = keyblock ? at<uint16_t>(workspace, w.oT) : nullptr;
+  int32_t* skeys = nullptr;
+  int32_t* svals = nullptr;
+  // transposed copies, sort by key block, visits of one chunk on stream `st`
+  auto pre_work = [&](int64_t t0, int64_t ntok, hipStream_t st) {
+    {
+      TimedScope ts("transpose", st);
+      launch_transpose(ra.q, ra.qr, ra.dO, t0, ntok, d.G, d.Gp, (int32_t)d.Dr, qT, oT, st);
+    }
+    const int64_t n = ntok * d.E;
+    TimedScope ts("kb_sort", st);
+    launch_csr(n, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals, at<int32_t>(workspace, w.sort_hist),
+               nullptr, &svals, st, 1, ntok, &skeys);
+    launch_visits(skeys, svals, rows, n, ntok, (int32_t)d.nKB, at<int32_t>(workspace, w.vis_flags),
+                  at<int32_t>(workspace, w.sort_hist), at<int32_t>(workspace, w.vis_start),
+                  at<int32_t>(workspace, w.vis_key), at<int32_t>(workspace, w.vis_er),
+                  at<int32_t>(workspace, w.vis_n), st);
+  };
   for (int64_t t0 = 0; t0 < d.T1; t0 += d.chunk) {
     const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
     {
       TimedScope ts("decode", s);
-      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s);
+      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s, status);
     }
     ra.t0 = ca.t0 = t0;
     ra.ntok = ca.ntok = ntok;
-    bool joined = true;
+    if (side) {   // pre-work beside the token kernels
+      if (!order(s, side->s, kEvFork)) return fail(SFAG_ERR_RUNTIME, "fork to the second stream failed");
+      pre_work(t0, ntok, side->s);
+      if (hipEventRecord(side->ev[kEvPre], side->s) != hipSuccess)
+        return fail(SFAG_ERR_RUNTIME, "second stream event failed");
+    }
     if (!use_row) {
       {
         TimedScope ts("sdp", s);
         launch_sdp(plan->dtype, rope, ra, s);
       }
-      if (side && keyblock && d.E > 0) {
-        // k_dq on the side stream, concurrent with the key-block work below.
-        // (The record/wait pair is atomic with respect to other threads'
-        // calls on this device, which share the side stream and its events;
-        // a later join record only orders after this one, the stream being
-        // in order.)
-        bool forked;
-        {
-          std::lock_guard<std::mutex> lk(g_side_mu);
-          forked = hipEventRecord(side->fork, s) == hipSuccess &&
-                   hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess;
-        }
-        if (!forked) return fail(SFAG_ERR_RUNTIME, "fork to the side stream failed");
+      if (dq_side) {
+        if (!order(s, side->s, kEvSdp)) return fail(SFAG_ERR_RUNTIME, "fork to the second stream failed");
         {
           TimedScope ts("dq", side->s);
           launch_dq(plan->dtype, rope, ra, side->s);
         }
-        if (hipEventRecord(side->join, side->s) != hipSuccess)
-          return fail(SFAG_ERR_RUNTIME, "side stream event failed");
-        joined = false;
+        if (hipEventRecord(side->ev[kEvDq], side->s) != hipSuccess)
+          return fail(SFAG_ERR_RUNTIME, "second stream event failed");
       } else {
         TimedScope ts("dq", s);
         launch_dq(plan->dtype, rope, ra, s);
@@ -347,26 +421,14 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
       TimedScope ts("row", s);
       launch_row(plan->dtype, rope, ra, s);
     }
-    if (keyblock) {
-      if (d.E > 0) {
-        uint16_t* qT = at<uint16_t>(workspace, w.qT);
-        uint16_t* oT = at<uint16_t>(workspace, w.oT);
-        {
-          TimedScope ts("transpose", s);
-          launch_transpose(ra.q, ra.qr, ra.dO, t0, ntok, d.G, d.Gp, (int32_t)d.Dr, qT, oT, s);
-        }
-        int32_t* skeys = nullptr;
-        int32_t* svals = nullptr;
-        const int64_t n = ntok * d.E;
-        {
-          TimedScope ts("kb_sort", s);
-          launch_csr(n, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals, at<int32_t>(workspace, w.sort_hist),
-                     nullptr, &svals, s, 1, ntok, &skeys);
-          launch_visits(skeys, svals, rows, n, ntok, (int32_t)d.nKB, at<int32_t>(workspace, w.vis_flags),
-                        at<int32_t>(workspace, w.sort_hist), at<int32_t>(workspace, w.vis_start),
-                        at<int32_t>(workspace, w.vis_key), at<int32_t>(workspace, w.vis_er),
-                        at<int32_t>(workspace, w.vis_n), s);
-        }
+    if (kb_work) {
+      if (side) {
+        if (hipStreamWaitEvent(s, side->ev[kEvPre], 0) != hipSuccess)
+          return fail(SFAG_ERR_RUNTIME, "join of the second stream failed");
+      } else {
+        pre_work(t0, ntok, s);
+      }
+      {
         KbArgs ka;
         ka.qT = qT;
         ka.oT = oT;
@@ -406,7 +468,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
           launch_kb_reduce(ka.part, ka.nonempty, d.T2, d.AW, ka.nTR, ka.nKB, acc, s);
         }
       }
-    } else {
+    } else if (!keyblock) {
       TimedScope ts("col", s);
       launch_col(plan->dtype, rope, partial, ca, s);
     }
@@ -421,8 +483,8 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
       TimedScope ts("key_reduce", s);
       launch_key_reduce(off, sorted, ca.partials, d.AW, d.T2, acc, s);
     }
-    if (!joined && hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
-      return fail(SFAG_ERR_RUNTIME, "join of the side stream failed");
+    if (dq_side && hipStreamWaitEvent(s, side->ev[kEvDq], 0) != hipSuccess)
+      return fail(SFAG_ERR_RUNTIME, "join of the second stream failed");
     const int rc = check_launch("chunk kernels");
     if (rc != SFAG_OK) return rc;
   }
@@ -531,7 +593,8 @@ extern "C" int sfag_build_index(const void* sparseIndices, const void* seqLensQ,
   if (layout == 1) {
     q_off = at<int32_t>(workspace, L.seq_off);
     kv_off = q_off + (B + 1);
-    launch_seq_offsets((const int32_t*)seqLensQ, (const int32_t*)seqLensKv, (int32_t)B, q_off, kv_off, s);
+    launch_seq_offsets((const int32_t*)seqLensQ, (const int32_t*)seqLensKv, (int32_t)B, T1, T2, q_off, kv_off,
+                       nullptr, s);
   }
   launch_decode((const int32_t*)sparseIndices, 0, T1, d, q_off, kv_off, (int32_t*)rows, (int32_t*)nValid, s);
   const int64_t n = T1 * E;

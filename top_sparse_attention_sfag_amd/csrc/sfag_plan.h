@@ -19,6 +19,7 @@ enum Scatter : int32_t { kScatterAtomic = 0, kScatterPartials = 1, kScatterKeyBl
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspaceLayout {
+  uint64_t status = 0;     // validation result (16 bytes) when options.validate; always at offset 0
   uint64_t seq_off = 0;    // TND: int32 q_off[B+1], kv_off[B+1]
   uint64_t delta = 0;      // fp32 (T1, G): rowsum(dO ∘ O)
   uint64_t acc = 0;        // fp32 (T2, AW): dK | dKrope | dV accumulators
@@ -64,7 +65,13 @@ struct Dims {
 uint64_t align256(uint64_t x);
 
 // Workspace layout for `d` (chunk and flags already set).
-WorkspaceLayout layout_for(const Dims& d, int32_t scatter);
+WorkspaceLayout layout_for(const Dims& d, int32_t scatter, bool validate);
+
+// Default workspace budgets of the backward and forward plans.
+constexpr uint64_t kDefaultBudget = 48ull << 30;
+constexpr uint64_t kDefaultForwardBudget = 16ull << 30;
+// Key-block token ranges per default-size chunk.
+constexpr int kDefaultRanges = 16;
 
 // Key rows per block of the key-centric dK/dV contraction.
 constexpr int kKeyBlockRows = 256;
@@ -78,6 +85,13 @@ void set_error(const std::string& msg);
 
 }  // namespace sfag
 
+struct sfag_plan;
+namespace sfag {
+// Scatter path, chunking, token ranges and workspace layout of a validated
+// plan from its shapes and options (phase 1 and sfag_plan_configure).
+int plan_launch(sfag_plan* p);
+}  // namespace sfag
+
 struct sfag_plan {
   const void *q = nullptr, *k = nullptr, *v = nullptr, *idx = nullptr, *dout = nullptr, *out = nullptr;
   const void *smax = nullptr, *ssum = nullptr, *lq = nullptr, *lk = nullptr, *qr = nullptr, *kr = nullptr;
@@ -86,6 +100,7 @@ struct sfag_plan {
   bool deterministic = false;
   float scale = 0.f;
   int32_t scatter = 0;
+  sfag_options opt{};      // tuning choices (all 0 = defaults)
   // forward plans: the outputs out / softmaxMax / softmaxSum
   bool forward = false;
   void *out_w = nullptr, *smax_w = nullptr, *ssum_w = nullptr;

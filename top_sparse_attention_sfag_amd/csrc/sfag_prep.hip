@@ -11,15 +11,23 @@ namespace sfag {
 // ---------------------------------------------------------------------------
 // TND: exclusive prefix sums of the per-sequence lengths (parameter table:
 // actualSeqLengthsQuery / actualSeqLengthsKv hold the valid tokens of each
-// sequence).  Negative lengths count as 0.  One block, B <= 256.
+// sequence, adding up to T1 / T2).  Negative lengths count as 0; the sums are
+// formed in 64 bits and saturate at 2^31 - 1, so offsets never wrap.  With a
+// validation word (status != NULL) negative lengths and sums that differ
+// from T1 / T2 are flagged there.  One block, B <= 256.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B,
-                                                     int32_t* q_off, int32_t* kv_off) {
-  __shared__ int32_t sq[257], sk[257];
+__global__ void __launch_bounds__(256) k_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int64_t T1,
+                                                     int64_t T2, int32_t* q_off, int32_t* kv_off,
+                                                     uint32_t* status) {
+  __shared__ int64_t sq[257], sk[257];
+  __shared__ int32_t neg;
   const int t = threadIdx.x;
+  if (t == 0) neg = 0;
+  __syncthreads();
   if (t < B) {
     sq[t + 1] = max(lq[t], 0);
     sk[t + 1] = max(lk[t], 0);
+    if (lq[t] < 0 || lk[t] < 0) atomicOr(&neg, 1);
   }
   if (t == 0) sq[0] = sk[0] = 0;
   __syncthreads();
@@ -28,11 +36,17 @@ __global__ void __launch_bounds__(256) k_seq_offsets(const int32_t* lq, const in
       sq[b] += sq[b - 1];
       sk[b] += sk[b - 1];
     }
+    if (status) {
+      uint32_t f = neg ? SFAG_BAD_LENGTH_NEGATIVE : 0u;
+      if (sq[B] != T1) f |= SFAG_BAD_LENGTH_SUM_Q;
+      if (sk[B] != T2) f |= SFAG_BAD_LENGTH_SUM_KV;
+      if (f) atomicOr(status, f);
+    }
   }
   __syncthreads();
   if (t <= B) {
-    q_off[t] = sq[t];
-    kv_off[t] = sk[t];
+    q_off[t] = (int32_t)min<int64_t>(sq[t], 0x7fffffffLL);
+    kv_off[t] = (int32_t)min<int64_t>(sk[t], 0x7fffffffLL);
   }
 }
 
@@ -72,13 +86,16 @@ __global__ void __launch_bounds__(256) k_fill_u32(uint32_t* __restrict__ p, uint
 // Index decode (功能说明: gather of sparseBlockSize rows per index; Mask table:
 // sparseMode 0 / 3).  Position e = j*block + r of token t is p = idx[t][j] + r,
 // valid iff idx[t][j] >= 0, p < Lk and (mode 3) p <= t_loc + Lk - Lq.  The
-// valid positions are compacted in position order: rows[tl][c] = kv_base + p.
+// valid positions are compacted in position order: rows[tl][c] = kv_base + p,
+// and only rows in [0, T2) are ever written.  With a validation word
+// (status != NULL) entries at or past the key length are counted there.
 // One block per token of the chunk.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx, int64_t t0, int64_t K, int32_t block,
                                                 int32_t mode, int32_t layout, int64_t S1, int64_t S2,
                                                 const int32_t* q_off, const int32_t* kv_off, int32_t B, int64_t T2,
-                                                int32_t* __restrict__ rows, int32_t* __restrict__ nvalid) {
+                                                int32_t* __restrict__ rows, int32_t* __restrict__ nvalid,
+                                                uint32_t* status) {
   const int64_t tl = blockIdx.x;
   const int64_t t = t0 + tl;
   const int64_t E = K * block;
@@ -89,6 +106,7 @@ __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx,
   if (tid == 0) base_s = 0;
   __syncthreads();
   int32_t* out = rows + tl * E;
+  int32_t bad = 0;
   for (int64_t e0 = 0; e0 < E; e0 += 256) {
     const int64_t e = e0 + tid;
     bool valid = false;
@@ -99,7 +117,8 @@ __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx,
       const int64_t p = (int64_t)ent + r;
       valid = ent >= 0 && p < g.Lk && (mode != 3 || p <= g.bound);
       row = g.kv_base + p;
-      valid = valid && row < T2;
+      valid = valid && row >= 0 && row < T2;
+      if (r == 0 && ent >= g.Lk) ++bad;
     }
     const uint64_t bal = __ballot(valid);
     const int rank = __popcll(bal & ((1ull << lane) - 1));
@@ -113,6 +132,10 @@ __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx,
     __syncthreads();
   }
   if (tid == 0) nvalid[tl] = base_s;
+  if (status && bad) {
+    atomicOr(status, SFAG_BAD_INDEX_RANGE);
+    atomicAdd((unsigned long long*)(status + 2), (unsigned long long)bad);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -302,18 +325,20 @@ __global__ void __launch_bounds__(256) k_csr_offsets(const int32_t* __restrict__
 }
 
 // Key-centric reduction (deterministic path): for each key row p, the partial
-// rows of its pairs are summed in CSR (ascending pair) order and added to the
-// accumulator.  One block per key row; fixed order, so bitwise reproducible.
+// rows of its pairs are added to the accumulator one by one in CSR (ascending
+// pair) order.  One block per key row; fixed order, so bitwise reproducible.
 __global__ void __launch_bounds__(256) k_key_reduce(const int32_t* __restrict__ off, const int32_t* __restrict__ pairs,
                                                     const float* __restrict__ part, int64_t AW,
                                                     float* __restrict__ acc) {
   const int64_t p = blockIdx.x;
   const int32_t s = off[p], e = off[p + 1];
   if (s == e) return;
+  // one running sum from the accumulator through every pair in CSR order, so
+  // that splitting the tokens into chunks never regroups the additions
   for (int64_t col = threadIdx.x; col < AW; col += 256) {
-    float sum = 0.f;
+    float sum = acc[p * AW + col];
     for (int32_t i = s; i < e; ++i) sum += part[(int64_t)pairs[i] * AW + col];
-    acc[p * AW + col] += sum;
+    acc[p * AW + col] = sum;
   }
 }
 
@@ -418,9 +443,9 @@ void launch_scan_i32(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s) {
   hipLaunchKernelGGL(k_scan_segments, dim3((unsigned)nseg), dim3(256), 0, s, a, n, tmp);
 }
 
-void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int32_t* q_off, int32_t* kv_off,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(k_seq_offsets, dim3(1), dim3(256), 0, s, lq, lk, B, q_off, kv_off);
+void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int64_t T1, int64_t T2, int32_t* q_off,
+                        int32_t* kv_off, uint32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_seq_offsets, dim3(1), dim3(256), 0, s, lq, lk, B, T1, T2, q_off, kv_off, status);
 }
 
 void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, int64_t nrows, hipStream_t s) {
@@ -438,10 +463,10 @@ void launch_fill_u32(void* p, uint64_t n, uint32_t v, hipStream_t s) {
 }
 
 void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, const int32_t* q_off,
-                   const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s) {
+                   const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s, uint32_t* status) {
   if (ntok == 0) return;
   hipLaunchKernelGGL(k_decode, dim3((unsigned)ntok), dim3(256), 0, s, idx, t0, d.K, (int32_t)d.block, d.mode,
-                     d.layout, d.S1, d.S2, q_off, kv_off, (int32_t)d.B, d.T2, rows, nvalid);
+                     d.layout, d.S1, d.S2, q_off, kv_off, (int32_t)d.B, d.T2, rows, nvalid, status);
 }
 
 void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E, int64_t T2, int32_t sort_bits,

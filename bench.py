@@ -410,10 +410,11 @@ def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", val
 
         def step(opts=options):
             sfag.backward(*args_pos, outputs=outs, workspace=ws, stream=stream, options=opts, **kw)
-        # on the key-block path a second stream overlaps kernels (see
-        # sfag_options.concurrent): the per-kernel times that pick the
-        # roofline kernel then come from a serial pass
-        concurrent = not (options or {}).get("concurrent") == "off"
+        # with 32 <= N1 < 128 the dQ kernel runs on a second stream beside the
+        # key-block kernels (see sfag_options.concurrent): the per-kernel
+        # times that pick the roofline kernel then come from a serial pass
+        cc = (options or {}).get("concurrent", "auto")
+        concurrent = cc == "on" or (cc == "auto" and 32 <= case.G < 128)
 
     for _ in range(warmup):
         step()
@@ -452,7 +453,7 @@ def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", val
     # alone; its duration from the timed region unless it shares the GPU with
     # the second stream's kernels there
     dom = max(rprof, key=lambda k: rprof[k][0])
-    overlapped = concurrent and (dom not in ("keyblock", "kb_reduce", "cast", "fill") or 32 <= case.G < 128)
+    overlapped = concurrent and dom in ("dq", "keyblock", "transpose", "kb_sort")
     src = rprof if overlapped or dom not in prof else prof
     dom_ms = src[dom][0] / src[dom][1]
     launches_per_step = src[dom][1] / (nsteps_r if src is rprof else steps)

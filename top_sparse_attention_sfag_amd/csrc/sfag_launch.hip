@@ -83,11 +83,10 @@ void prof_drain() {
   g_prof_pending.clear();
 }
 
-// A second stream per device (default priority, non-blocking) and four
-// events, made on first use and kept for the life of the process: the
-// key-block pre-work runs on it beside k_sdp, and with fewer than 128 heads
-// k_dq beside the key-block kernels, so that each fills the other's tail.
-enum SideEvent { kEvFork = 0, kEvPre = 1, kEvSdp = 2, kEvDq = 3, kNumSideEvents = 4 };
+// A second stream per device (default priority, non-blocking) and two
+// events, made on first use and kept for the life of the process: k_dq runs
+// on it beside the key-block kernels, so that each fills the other's tail.
+enum SideEvent { kEvSdp = 0, kEvDq = 1, kNumSideEvents = 2 };
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t ev[kNumSideEvents] = {};
@@ -321,18 +320,19 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
     vals[1] = at<int32_t>(workspace, w.sort_vals[1]);
   }
 
-  // A second stream on the key-block path: the pre-work of the key-block
-  // kernel (transposed Q|Qrope and dO copies, the sort of the pairs by key
-  // block, the visit list) needs only the decoded indices, so it runs beside
-  // k_sdp; with fewer than 128 heads k_dq also runs beside the key-block
-  // kernels (64 heads, 8192 varlen tokens, top-2048 causal: 10.8 -> 9.6 ms;
-  // with 128 heads no gain at 4096 tokens and +3% at 32768, so off there).
-  // The caller's auxiliary stream if it gave one (with events of the call's
-  // own), else the library's, whose events this call holds for its whole
-  // enqueue sequence.
+  // A second stream on the key-block path with the split token kernels:
+  // k_dq runs beside the key-block kernels (64 heads, 8192 varlen tokens,
+  // top-2048 causal: 9.4 -> 8.4 ms; with 128 heads no gain at 4096 tokens
+  // and +3% at 32768, so off there by default).  Running the key-block
+  // pre-work (transposes, sort, visits) beside k_sdp instead measured no gain
+  // (128 heads, 4096 tokens: 7.67 -> 7.89 ms), so it stays on `stream`.  The
+  // caller's auxiliary stream if it gave one (with events of the call's own),
+  // else the library's, whose events this call holds for its whole enqueue
+  // sequence.
   const bool kb_work = keyblock && d.E > 0;
-  bool concurrent = kb_work && o.concurrent != SFAG_CONCURRENT_OFF;
-  const bool dq_side = concurrent && !use_row && (d.Gp < 128 || o.concurrent == SFAG_CONCURRENT_ON);
+  bool concurrent = kb_work && !use_row &&
+                    (o.concurrent == SFAG_CONCURRENT_ON || (o.concurrent == SFAG_CONCURRENT_AUTO && d.Gp < 128));
+  bool dq_side = concurrent;
   SideStream own_side;
   struct OwnEvents {
     hipEvent_t e[kNumSideEvents] = {};
@@ -355,6 +355,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
     side = side_stream();
     if (side) side_lock.lock();
   }
+  if (!side) dq_side = false;
   // stream b waits for the work enqueued so far on stream a
   auto order = [&](hipStream_t a, hipStream_t b, SideEvent e) {
     return hipEventRecord(side->ev[e], a) == hipSuccess && hipStreamWaitEvent(b, side->ev[e], 0) == hipSuccess;
@@ -386,12 +387,6 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
     }
     ra.t0 = ca.t0 = t0;
     ra.ntok = ca.ntok = ntok;
-    if (side) {   // pre-work beside the token kernels
-      if (!order(s, side->s, kEvFork)) return fail(SFAG_ERR_RUNTIME, "fork to the second stream failed");
-      pre_work(t0, ntok, side->s);
-      if (hipEventRecord(side->ev[kEvPre], side->s) != hipSuccess)
-        return fail(SFAG_ERR_RUNTIME, "second stream event failed");
-    }
     if (!use_row) {
       {
         TimedScope ts("sdp", s);
@@ -422,12 +417,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
       launch_row(plan->dtype, rope, ra, s);
     }
     if (kb_work) {
-      if (side) {
-        if (hipStreamWaitEvent(s, side->ev[kEvPre], 0) != hipSuccess)
-          return fail(SFAG_ERR_RUNTIME, "join of the second stream failed");
-      } else {
-        pre_work(t0, ntok, s);
-      }
+      pre_work(t0, ntok, s);
       {
         KbArgs ka;
         ka.qT = qT;

@@ -191,6 +191,29 @@ int sfag_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const 
 int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
 
 /*
+ * The backward pass of `plan` for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the library's own scratch array serves as the workspace.  That
+ * array, SFAG_STATIC_SCRATCH_BYTES (256 MiB), is a device global of the
+ * library: each GPU the library runs on holds one until the process ends.
+ * The plan's workspace must fit in it (re-plan with sfag_plan_configure and
+ * workspaceBudget <= SFAG_STATIC_SCRATCH_BYTES); a larger plan is rejected
+ * with SFAG_ERR_PARAM_INVALID before anything is enqueued.  The plan is
+ * consumed and freed, also on error.  The call allocates nothing (no
+ * hipMalloc, hipFree, stream or event; the opt-in timing of
+ * sfag_profile_enable aside): a plan that would run kernels on a second
+ * stream without a caller stream for it (sfag_options.auxStream) runs them
+ * all on `stream` instead.  Every call on one GPU uses that GPU's one
+ * array, so calls that overlap on one GPU (other streams, other threads)
+ * race: the caller orders them.  The kernels initialise every part of the
+ * array they read (the accumulators are zero-filled at the start of each
+ * call), so what an earlier call left there does not matter.  Outputs and
+ * errors are those of sfag_backward.
+ */
+#define SFAG_STATIC_SCRATCH_BYTES (256ull << 20)
+int sfag_backward_static(sfag_plan* plan, void* stream);
+
+/*
  * Forward pass of the same attention (the producer of the backward's out,
  * softmaxMax and softmaxSum inputs, whose meaning the operator page's
  * parameter table gives): for each query token t and head h, over the valid

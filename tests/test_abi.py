@@ -346,3 +346,22 @@ def test_product_sources_read_no_environment():
     for f in sorted(os.listdir(csrc)):
         src = open(os.path.join(csrc, f)).read()
         assert "getenv" not in src and "environ" not in src, f
+
+
+def test_static_entry_rejects_a_plan_larger_than_its_scratch():
+    """sfag_backward_static checks the plan's workspace against its scratch
+    array before anything is enqueued (no GPU needed), and frees the plan."""
+    B, S1, S2, G, K = 1, 2048, 4096, 128, 2048
+    bf, i32, f32 = 1, 4, 3
+    q = lambda: _fake((B, S1, G, 512), bf)
+    k = lambda: _fake((B, S2, 1, 512), bf)
+    st = lambda: _fake((B, 1, S1, G), f32)
+    ws = ctypes.c_uint64(0)
+    p = ctypes.c_void_p(None)
+    rc = sfag.lib().sfag_workspace_size(q(), k(), k(), _fake((B, S1, 1, K), i32), q(), q(), st(), st(), None, None,
+                                        None, None, 0.04, 1, b"BSND", 3, 2147483647, 2147483647, False, q(), k(), k(),
+                                        None, None, ctypes.byref(ws), ctypes.byref(p))
+    assert rc == 0 and ws.value > sfag.STATIC_SCRATCH_BYTES
+    assert sfag.lib().sfag_backward_static(p, None) == sfag.ERR_PARAM_INVALID
+    assert b"scratch" in sfag.lib().sfag_last_error()
+    assert sfag.lib().sfag_backward_static(None, None) == sfag.ERR_NULLPTR

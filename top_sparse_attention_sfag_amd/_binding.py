@@ -113,6 +113,8 @@ def lib():
             ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p)]
         L.sfag_forward.restype = ctypes.c_int
         L.sfag_forward.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+        L.sfag_backward_static.restype = ctypes.c_int
+        L.sfag_backward_static.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.sfag_plan_configure.restype = ctypes.c_int
         L.sfag_plan_configure.argtypes = [ctypes.c_void_p, ctypes.POINTER(SfagOptions), ctypes.POINTER(ctypes.c_uint64)]
         L.sfag_validation_read.restype = ctypes.c_int
@@ -260,6 +262,32 @@ def backward(query, key, value, sparse_indices, dout, out, softmax_max, softmax_
             workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
     rc = lib().sfag_backward(ctypes.c_void_p(workspace.data_ptr()), ctypes.c_uint64(workspace.numel()), p,
                              ctypes.c_void_p(s.cuda_stream))
+    if rc != OK:
+        _raise(rc)
+    return dq, dk, dv, dqr, dkr
+
+
+STATIC_SCRATCH_BYTES = 256 << 20   # SFAG_STATIC_SCRATCH_BYTES
+
+
+def backward_static(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, outputs, *,
+                    seqlens_q=None, seqlens_kv=None, query_rope=None, key_rope=None, scale=None, block_size=1,
+                    layout="BSND", sparse_mode=0, deterministic=False, stream=None, options=None):
+    """sfag_backward_static: the backward pass with the library's own scratch
+    array as workspace (nothing is allocated; ``outputs`` = (dq, dk, dv,
+    dq_rope, dk_rope) must be given).  The plan is made with
+    workspace_budget = STATIC_SCRATCH_BYTES unless ``options`` sets one."""
+    if not query.is_cuda:
+        raise SfagValueError(ERR_PARAM_INVALID, "tensors must be on the GPU")
+    dq, dk, dv, dqr, dkr = outputs
+    opts = dict(options or {})
+    opts.setdefault("workspace_budget", STATIC_SCRATCH_BYTES)
+    _ws, p = plan(query, key, value, sparse_indices, dout, out, softmax_max, softmax_sum, dq, dk, dv, dq_rope=dqr,
+                  dk_rope=dkr, seqlens_q=seqlens_q, seqlens_kv=seqlens_kv, query_rope=query_rope, key_rope=key_rope,
+                  scale=scale, block_size=block_size, layout=layout, sparse_mode=sparse_mode,
+                  deterministic=deterministic, options=opts)
+    s = stream if stream is not None else torch.cuda.current_stream(query.device)
+    rc = lib().sfag_backward_static(p, ctypes.c_void_p(s.cuda_stream))
     if rc != OK:
         _raise(rc)
     return dq, dk, dv, dqr, dkr

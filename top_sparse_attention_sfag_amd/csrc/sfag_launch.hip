@@ -209,7 +209,69 @@ extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* 
   return check_launch("forward kernels");
 }
 
+namespace {
+
+// The backward pass on `workspace`.  library_stream: whether the call may use
+// (and on first use make) the library's second stream.
+int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream, bool library_stream);
+
+constexpr uint64_t kScratchBytes = SFAG_STATIC_SCRATCH_BYTES;
+
+}  // namespace
+
+// Scratch array of sfag_backward_static, one per device.  In host code the
+// name `scratch` stands for a host-side handle, not a device address: host
+// code reaches the array only through the address hipGetSymbolAddress gives
+// for the current device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current); NULL if the lookup fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) return it->second;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch[dev] = p;
+  return p;
+}
+
+}  // namespace
+
 extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream) {
+  return run_backward(workspace, workspaceSize, plan, stream, true);
+}
+
+extern "C" int sfag_backward_static(sfag_plan* plan, void* stream) {
+  set_error("");
+  if (!plan) return fail(SFAG_ERR_NULLPTR, "plan is NULL");
+  if (plan->ws.total > kScratchBytes) {
+    const uint64_t need = plan->ws.total;
+    delete plan;
+    return fail(SFAG_ERR_PARAM_INVALID, "the plan needs a workspace of " + std::to_string(need) +
+                                            " bytes, more than the " + std::to_string(kScratchBytes) +
+                                            "-byte scratch array: re-plan with sfag_plan_configure and "
+                                            "workspaceBudget <= SFAG_STATIC_SCRATCH_BYTES");
+  }
+  void* ws = scratch_address();
+  if (!ws) {
+    delete plan;
+    return fail(SFAG_ERR_RUNTIME, "the scratch array's device address could not be found");
+  }
+  return run_backward(ws, kScratchBytes, plan, stream, false);
+}
+
+namespace {
+
+int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream, bool library_stream) {
   set_error("");
   std::unique_ptr<sfag_plan> own(plan);
   if (!plan) return fail(SFAG_ERR_NULLPTR, "plan is NULL");
@@ -351,7 +413,7 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
       own_side.ev[i] = own_events.e[i];
     }
     side = &own_side;
-  } else if (concurrent) {
+  } else if (concurrent && library_stream) {
     side = side_stream();
     if (side) side_lock.lock();
   }
@@ -485,6 +547,8 @@ extern "C" int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan*
   }
   return check_launch("cast");
 }
+
+}  // namespace
 
 namespace {
 

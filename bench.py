@@ -503,6 +503,8 @@ def main(argv=None):
                          "sfag_band_indices: key positions d-PRE..d+NEXT of the bottom-right diagonal d")
     ap.add_argument("--concurrent", choices=("auto", "off", "on"), default="auto",
                     help="sfag_options.concurrent for the timed calls (default: the library's choice)")
+    ap.add_argument("--token-path", choices=("auto", "fused", "split"), default="auto",
+                    help="sfag_options.tokenPath for the timed calls (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -555,7 +557,12 @@ def main(argv=None):
     seed = si.seed_for(headline)
     print(f"[bench] generating {case.name} on {dev}", file=sys.stderr, flush=True)
     inp, n_pairs = _prepare(case, seed, dev, sfag, band, args.value_is_key)
-    opts = None if args.concurrent == "auto" else dict(concurrent=args.concurrent)
+    opts = {}
+    if args.concurrent != "auto":
+        opts["concurrent"] = args.concurrent
+    if args.token_path != "auto":
+        opts["token_path"] = args.token_path
+    opts = opts or None
     head = _measure(case, inp, n_pairs, det, args.steps, args.warmup, sfag, args.which, args.value_is_key, opts)
 
     line = {

@@ -312,7 +312,7 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
   bool use_row = d.Gp < 32;
   if (o.tokenPath == SFAG_TOKEN_FUSED) use_row = true;
   if (o.tokenPath == SFAG_TOKEN_SPLIT && d.Gp >= 32) use_row = false;
-  if (use_row) {   // k_row reads Delta; k_sdp forms it from dO and O itself
+  if (use_row && d.Gp > 16) {   // k_row reads Delta; k_row16 and k_sdp form it from dO and O themselves
     TimedScope ts("delta", s);
     launch_delta(plan->dtype, plan->dout, plan->out, delta, d.T1 * d.G, s);
   }

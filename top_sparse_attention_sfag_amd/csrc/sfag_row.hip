@@ -315,6 +315,310 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_row16: the fused token kernel for up to 16 heads (one head block of 16),
+// with the work of a tile spread over all four waves and two tiles of
+// gathered rows in flight.
+//
+//   * Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ of a 32-position tile: wave 0 / 1 form Sᵀ of
+//     positions 0..15 / 16..31 (Q in registers), wave 2 / 3 dPᵀ of the same
+//     halves (dO in registers); dPᵀ goes to the S waves through LDS.
+//   * P = exp(scale·S − max)/sum and dS = P ∘ (dP − Delta) in the S waves;
+//     dS is staged in LDS as (head, position) rows, the A operand of
+//   * dQ += dS·K_tile: wave w owns every fourth block of 16 dQ|dQrope
+//     columns (K read transposed from LDS), fp32 accumulators in registers.
+//   * Delta = rowsum(dO ∘ O) (功能说明 stage 2) is formed once per token in
+//     the prologue by wave 2, which holds dO, and handed over through LDS.
+//   * Waves 0..2 issue the tile copies (global_load_lds) and no other
+//     vector-memory work inside the loop, so a wait on their copy counter
+//     can leave the next tile's copies in flight: the copies of tile i + 2 go
+//     out as soon as every wave is done with tile i, while tile i + 1's are
+//     still landing.  Wave 3 issues no copies; it stores the P and dS rows
+//     (staged in LDS, double buffered) and loads the row indices of the tile
+//     after next into LDS, so the copying waves never wait on a load of
+//     their own.
+// ---------------------------------------------------------------------------
+template <typename TT, int DR, bool VK>
+__global__ void __launch_bounds__(256, 1) k_row16(RowArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int KS_QK = DQK / 32;          // 16x16x32 k-steps of S (rope last)
+  constexpr int KS_V = 512 / 32;
+  constexpr int NB_Q = DQK / 16;           // 16-column blocks of dQ|dQrope
+  constexpr int NBW = NB_Q / 4;            // per wave
+  constexpr int KM_BYTES = kTile * 1024;
+  constexpr int KR_BYTES = kTile * DR * 2;
+  constexpr int V_BYTES = VK ? 0 : kTile * 1024;
+  constexpr int BUF = KM_BYTES + KR_BYTES + V_BYTES;
+  constexpr int XSTR = 36;                 // floats per head row of the dPᵀ exchange
+  constexpr int DSTR = 40;                 // 16-bit elements per head row of the dS staging
+  // copy instructions per tile of copying wave w (rows w, w+3, ...; rope
+  // groups of 8 rows w, w+3)
+  constexpr int kRowOps = VK ? 1 : 2;
+  typedef typename TT::vec8 V8;
+
+  __shared__ __attribute__((aligned(16))) unsigned char tbuf[2][BUF];
+  __shared__ __attribute__((aligned(16))) float xdp[16 * XSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dsT[16 * DSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t stg[2][2][kTile * 16];   // [buffer][P, dS][position][head]
+  __shared__ int32_t keys_s[kTile];
+  __shared__ float delta_s[16];
+
+  // ---- work unit: token (and share of its positions), XCD-aware order ------
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, u = b / kXcds;
+  const int sp = u % a.n_split;
+  const int tq = u / a.n_split;
+  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const bool hv = n < a.G;                 // head n
+  const bool s_wave = wave < 2, copier = wave < 3;
+  const int mb = wave & 1;                 // position half of the Sᵀ / dPᵀ waves
+
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+  int cb = 0, ce = nv;
+  if (a.n_split > 1) {
+    const int per = (((nv + a.n_split - 1) / a.n_split) + kTile - 1) / kTile * kTile;
+    cb = min(nv, sp * per);
+    ce = min(nv, cb + per);
+  }
+
+  // ---- prologue: operands, statistics, Delta ----------------------------
+  V8 Bf[KS_QK > KS_V ? KS_QK : KS_V];      // Q (S waves) or dO (dP waves) of head n
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hv) {
+      if (s_wave) {
+        if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + n) * 512 + d0);
+        else v = *(const uint4*)(a.qr + (t * a.G + n) * DR + (d0 - 512));
+      } else if (ks < KS_V) {
+        v = *(const uint4*)(a.dO + (t * a.G + n) * 512 + d0);
+      }
+    }
+    Bf[ks] = as_vec8<V8>(v);
+  }
+  float mlog = 0.f, inv_l = 0.f;
+  bool live = false;
+  if (s_wave && hv) {
+    const float m = a.smax[t * a.G + n], l = a.ssum[t * a.G + n];
+    live = l > 0.f;
+    inv_l = live ? 1.f / l : 0.f;
+    mlog = m * kLog2e;
+  }
+  if (wave == 2) {
+    float dsum = 0.f;
+    if (hv) {
+#pragma unroll
+      for (int ks = 0; ks < KS_V; ++ks) {
+        const uint4 ov = *(const uint4*)(a.o + (t * a.G + n) * 512 + 32 * ks + 8 * g);
+        const uint4 dv = __builtin_bit_cast(uint4, Bf[ks]);
+        const uint16_t* po = (const uint16_t*)&ov;
+        const uint16_t* pd = (const uint16_t*)&dv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dsum = fmaf(TT::to_f(pd[j]), TT::to_f(po[j]), dsum);
+      }
+    }
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    if (g == 0) delta_s[n] = dsum;
+  }
+  // row indices of the first two tiles (a position past the share's end
+  // repeats its first valid position; its P and dS are 0)
+  int32_t key0 = 0, key1 = 0;
+  if (copier && cb < ce) {
+    const int c_0 = cb + (lane & 31), c_1 = cb + kTile + (lane & 31);
+    key0 = rt[c_0 < ce ? c_0 : cb];
+    key1 = rt[c_1 < ce ? c_1 : cb];
+  }
+  // every prologue load has landed before the first copy goes out, so the
+  // copy counter waits below count copies only
+  __builtin_amdgcn_s_waitcnt(0);
+  f32x4 acc[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- tile copies -------------------------------------------------------
+  // Copying wave w fetches K (and V) rows w, w + 3, ... of the tile and the
+  // rope rows of groups w, w + 3 (8 rows per instruction); chunk c of row r
+  // lands at chunk (c & ~7) | ((c & 7) ^ (r & 7)).
+  auto issue = [&](int32_t keyv, int buf) {
+    unsigned char* base = tbuf[buf];
+#pragma unroll
+    for (int r0 = 0; r0 < kTile; r0 += 3) {
+      const int r = r0 + wave;
+      if (r < kTile) {
+        const int64_t key = __builtin_amdgcn_readlane(keyv, r);
+        const int gc = lane ^ (r & 7);
+        lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
+        if (!VK) lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+      }
+    }
+    if (DR > 0) {
+#pragma unroll
+      for (int gi0 = 0; gi0 < kTile / 8; gi0 += 3) {
+        const int gi = gi0 + wave;
+        if (gi < kTile / 8) {
+          const int r = gi * 8 + (lane >> 3);
+          const int64_t key = __shfl(keyv, r);
+          const int gc = (lane & 7) ^ (r & 7);
+          lds_load16(a.kr + key * DR + gc * 8, base + KM_BYTES + gi * 8 * (DR * 2));
+        }
+      }
+    }
+  };
+  // wait until at most this wave's copies of one tile are outstanding
+  // (s_waitcnt with only the vector-memory count bounded; gfx9 encoding:
+  // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+  auto wait_one_tile = [&]() {
+    constexpr int nr0 = (kTile + 2) / 3, nr1 = (kTile + 1) / 3, nr2 = kTile / 3;
+    constexpr int g0 = DR > 0 ? 2 : 0, g12 = DR > 0 ? 1 : 0;
+    constexpr int n0 = nr0 * kRowOps + g0, n1 = nr1 * kRowOps + g12, n2 = nr2 * kRowOps + g12;
+    static_assert(n0 < 64 && n1 < 64 && n2 < 64, "copy counts must fit the 6-bit vmcnt field");
+    if (wave == 0) __builtin_amdgcn_s_waitcnt((n0 & 15) | ((n0 >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (wave == 1) __builtin_amdgcn_s_waitcnt((n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((n2 & 15) | ((n2 >> 4) << 14) | (7 << 4) | (15 << 8));
+  };
+
+  // Per-lane LDS offsets (see k_row): Sᵀ / dPᵀ A operand rows 16 mb + n.
+  const int x = n & 7;
+  const int oA_even = n * 1024 + 16 * (g ^ x);
+  const int oA_odd = n * 1024 + 16 * ((4 + g) ^ x);
+  const int oR_even = n * (DR * 2) + 16 * (g ^ x);
+  const int oR_odd = n * (DR * 2) + 16 * ((4 + g) ^ x);
+  const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;
+  const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
+  int oT[4], oTr[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    oT[w] = r1 * 1024 + 16 * ((2 * w + half) ^ x1) + hoff;
+    oTr[w] = r1 * (DR * 2) + 16 * ((2 * w + half) ^ x1) + hoff;
+  }
+
+  if (copier && cb < ce) {
+    issue(key0, 0);
+    if (cb + kTile < ce) issue(key1, 1);
+  }
+  int cur = 0, it = 0;
+  for (int c0 = cb; c0 < ce; c0 += kTile, cur ^= 1, ++it) {
+    const bool more = c0 + kTile < ce;
+    if (copier) {
+      if (more) wait_one_tile();
+      else __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
+    }
+    __syncthreads();
+    const unsigned char* Km = tbuf[cur];
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
+    // wave 3: row indices of the tile after next, into LDS for the copiers
+    if (wave == 3 && c0 + 2 * kTile < ce && lane < kTile) {
+      const int c = c0 + 2 * kTile + lane;
+      keys_s[lane] = rt[c < ce ? c : cb];
+    }
+    // ---- Sᵀ (waves 0, 1) or dPᵀ (waves 2, 3) of positions 16 mb .. +15
+    f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s_wave) {
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const unsigned char* p = Km + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1) + mb * 16384;
+        r = TT::mfma(as_vec8<V8>(*(const uint4*)p), Bf[ks], r);
+      }
+      if (DR > 0) {
+        r = TT::mfma(as_vec8<V8>(*(const uint4*)(Kr + oR_even + mb * 16 * (DR * 2))), Bf[KS_QK - 2], r);
+        r = TT::mfma(as_vec8<V8>(*(const uint4*)(Kr + oR_odd + mb * 16 * (DR * 2))), Bf[KS_QK - 1], r);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS_V; ++ks) {
+        const unsigned char* p = Vm + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1) + mb * 16384;
+        r = TT::mfma(as_vec8<V8>(*(const uint4*)p), Bf[ks], r);
+      }
+      // dPᵀ of head n, positions 16 mb + 4g .. +3
+      *(f32x4*)(xdp + n * XSTR + 16 * mb + 4 * g) = r;
+    }
+    __syncthreads();
+    // ---- P and dS (waves 0, 1)
+    if (s_wave) {
+      const f32x4 dp = *(const f32x4*)(xdp + n * XSTR + 16 * mb + 4 * g);
+      const float dl = delta_s[n];
+      uint16_t pv[4], dsv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * mb + 4 * g + i;   // position within the tile
+        const bool ok = live && (c0 + j < nv);
+        const float p = ok ? exp2f(r[i] * a.scale_log2 - mlog) * inv_l : 0.f;
+        pv[i] = TT::from_f(p);
+        dsv[i] = TT::from_f(p * (dp[i] - dl) * a.ds_scale);
+        stg[it & 1][0][j * 16 + n] = pv[i];
+        stg[it & 1][1][j * 16 + n] = dsv[i];
+      }
+      *(uint2*)(dsT + n * DSTR + 16 * mb + 4 * g) =
+          make_uint2(dsv[0] | ((uint32_t)dsv[1] << 16), dsv[2] | ((uint32_t)dsv[3] << 16));
+    }
+    __syncthreads();
+    // ---- P and dS rows of the tile to memory (wave 3)
+    if (wave == 3) {
+      const int which = lane >> 5, j = lane & 31;
+      if (c0 + j < nv) {
+        const uint4* src = (const uint4*)(stg[it & 1][which] + j * 16);
+        uint16_t* out = (which ? a.ds_out : a.p_out) + (tl * a.E + c0 + j) * 16;
+        ((uint4*)out)[0] = src[0];
+        ((uint4*)out)[1] = src[1];
+      }
+    }
+    // ---- dQ += dS·K over the tile's 32 positions, this wave's column blocks
+    {
+      const uint2 lo = *(const uint2*)(dsT + n * DSTR + 4 * g);
+      const uint2 hi = *(const uint2*)(dsT + n * DSTR + 16 + 4 * g);
+      const V8 A8 = as_vec8<V8>(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      auto kread = [&](int nb) -> V8 {
+        const unsigned char* p1 = nb < 32 ? Km + oT[nb & 3] + 128 * (nb >> 2) : Kr + oTr[nb & 3];
+        const unsigned char* p2 = p1 + (nb < 32 ? 16 * 1024 : 16 * (DR * 2));
+        return join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)p2));
+      };
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) acc[j] = TT::mfma(A8, kread(wave + 4 * j), acc[j]);
+    }
+    __syncthreads();
+    // every wave is done with this buffer: the copies of the tile after next
+    if (copier && c0 + 2 * kTile < ce) {
+      const int32_t keyv = keys_s[lane & 31];
+      issue(keyv, cur);
+    }
+  }
+
+  // ---- dQ | dQrope: column blocks wave, wave + 4, ... -----------------------
+  if (a.n_split > 1) {
+    if (cb >= ce) return;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int col = 16 * (wave + 4 * j) + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = 4 * g + i;
+        if (hh < a.G) atomicAdd(a.dq_acc + (tl * a.G + hh) * DQK + col, acc[j][i]);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int col = 16 * (wave + 4 * j) + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * g + i;
+      if (hh < a.G) {
+        const uint16_t v = TT::from_f(acc[j][i] * a.dq_mul);
+        if (col < 512) a.dq[(t * a.G + hh) * 512 + col] = v;
+        else a.dqr[(t * a.G + hh) * DR + (col - 512)] = v;
+      }
+    }
+  }
+}
+
 void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s) {
   if (a.ntok == 0) return;
   const int64_t per = (int64_t)kXcds * kRun;
@@ -322,6 +626,18 @@ void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(padded * a.n_hb * a.n_split)), block(256);
   // value passed as the key tensor itself: gather each row once
   const bool vk = a.v == a.k;
+  if (a.Gp == 16) {   // up to 16 heads: all four waves share a token's tiles
+    const dim3 grid16((unsigned)(padded * a.n_split));
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid16, block, 0, s, a); };
+    if (dtype == SFAG_BF16) {
+      if (rope) vk ? go(k_row16<BF16, 64, true>) : go(k_row16<BF16, 64, false>);
+      else vk ? go(k_row16<BF16, 0, true>) : go(k_row16<BF16, 0, false>);
+    } else {
+      if (rope) vk ? go(k_row16<FP16, 64, true>) : go(k_row16<FP16, 64, false>);
+      else vk ? go(k_row16<FP16, 0, true>) : go(k_row16<FP16, 0, false>);
+    }
+    return;
+  }
   if (dtype == SFAG_BF16) {
     if (rope) {
       if (vk) hipLaunchKernelGGL((k_row<BF16, 64, true>), grid, block, 0, s, a);

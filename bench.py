@@ -113,7 +113,7 @@ def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
 # Kernel groups of the timing API and the kernels (by demangled name) each
 # one stands for.
 _GROUPS = {
-    "sdp": r"k_sdp<", "dq": r"k_dq<", "row": r"k_row<", "keyblock": r"k_keyblock<", "transpose": r"k_transpose",
+    "sdp": r"k_sdp<", "dq": r"k_dq<", "row": r"k_row(16)?<", "keyblock": r"k_keyblock<", "transpose": r"k_transpose",
     "col": r"k_col<", "fwd": r"k_fwd<", "kb_reduce": r"k_kb_reduce", "cast": r"k_cast<", "decode": r"k_decode",
     "delta": r"k_delta<",
 }
@@ -186,7 +186,8 @@ def _summarize_profiles(d, config, calib_mb):
     os.makedirs(out_dir, exist_ok=True)
 
     def dispatches(kind):
-        """{dispatch id: (kernel name, {counter: value})} of one counter run."""
+        """{dispatch id: (kernel name, {counter: value})} of one counter run,
+        each counter summed over the rows (instances) rocprofv3 reports."""
         out = {}
         for r in _read_csvs(os.path.join(d, kind), "counter_collection.csv"):
             i = int(r["Dispatch_Id"])
@@ -203,14 +204,17 @@ def _summarize_profiles(d, config, calib_mb):
     rd_bytes = lambda c: 32 * c["TCC_EA0_RDREQ_32B"] + 64 * c["TCC_EA0_RDREQ_64B"] + 128 * c["TCC_EA0_RDREQ_128B"]
     wr_bytes = lambda c: 64 * c["TCC_EA0_WRREQ_64B"] + 32 * (c["TCC_EA0_WRREQ"] - c["TCC_EA0_WRREQ_64B"])
 
-    # MFMA busy per kernel group
+    # MFMA busy per kernel group: busy cycles summed over the 1024 SIMDs over
+    # 1024 x the dispatch's active cycles (rocprofv3's MfmaUtil); the one
+    # GRBM_GUI_ACTIVE value rocprofv3 reports adds up the active cycles of
+    # the 8 XCDs' graphics blocks, so one XCD's share is an eighth of it
     mfma = {}
     md, nm = window(dispatches("mfma"))
     for g, pat in _GROUPS.items():
         rows = [c for k, c in md.values() if re.search(pat, k)]
         if rows and all("GRBM_GUI_ACTIVE" in c for c in rows):
             busy = sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for c in rows)
-            act = sum(c["GRBM_GUI_ACTIVE"] for c in rows)
+            act = sum(c["GRBM_GUI_ACTIVE"] for c in rows) / 8
             mfma[g] = busy / (act * 1024) if act else None
 
     stats = _read_csvs(os.path.join(d, "trace"), "kernel_stats.csv")
@@ -231,14 +235,29 @@ def _summarize_profiles(d, config, calib_mb):
     rd_all, wr_all = dispatches("rd"), dispatches("wr")
     traffic = {"workload": case.name, "commands": cmds, "sources_sha256": _sources_sha256(), "calibration": None,
                "kernels": {}, "step": None, "mfma_busy": mfma or None}
+    rf = wf = 1.0
     if calib_mb:
+        # the counters see a fixed share of the TCC-to-memory requests: the
+        # copy of known size gives the factor for reads and for writes, the
+        # read-only sum a second reading of the read factor
+        # (launched before any kernel of the library; a tensor above 2 GiB
+        # runs as several dispatches of one kernel, so their counts add up)
         want = calib_mb * 1048576.0
-        cp_r = [rd_bytes(c) for k, c in rd_all.values() if "CUDAFunctorOnSelf_add<int>" in k]
-        cp_w = [wr_bytes(c) for k, c in wr_all.values() if "CUDAFunctorOnSelf_add<int>" in k]
-        sm_r = [rd_bytes(c) for k, c in rd_all.values() if "reduce_kernel" in k]
-        traffic["calibration"] = dict(bytes=want, copy_read=max(cp_r) if cp_r else None,
-                                      copy_write=max(cp_w) if cp_w else None,
-                                      sum_read=max(sm_r) if sm_r else None)
+
+        def before_lib(disp, pat):
+            first = min((i for i, (k, _c) in disp.items() if "sfag" in k), default=None)
+            return [c for i, (k, c) in disp.items() if pat in k and (first is None or i < first)]
+        cp_r = sum(rd_bytes(c) for c in before_lib(rd_all, "CUDAFunctorOnSelf_add<"))
+        cp_w = sum(wr_bytes(c) for c in before_lib(wr_all, "CUDAFunctorOnSelf_add<"))
+        sm_r = sum(rd_bytes(c) for c in before_lib(rd_all, "reduce_kernel"))
+        cal = dict(bytes=want, copy_read=cp_r, copy_write=cp_w, sum_read=sm_r)
+        if cp_r and cp_w:
+            rf, wf = want / cp_r, want / cp_w
+            cal.update(read_factor=rf, write_factor=wf, sum_read_factor=want / sm_r if sm_r else None)
+        traffic["calibration"] = cal
+    rd_bytes_raw, wr_bytes_raw = rd_bytes, wr_bytes
+    rd_bytes = lambda c: rf * rd_bytes_raw(c)
+    wr_bytes = lambda c: wf * wr_bytes_raw(c)
     rw, nr = window(rd_all)
     ww, nw = window(wr_all)
     for g, pat in _GROUPS.items():
@@ -475,12 +494,16 @@ def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", val
                mfma_frac=tflops / MFMA_PEAK_TFLOPS, valid_pairs=n_pairs,
                alg_model_GBs=alg_bytes / (ms * 1e-3) / 1e9,
                kernels_ms={k: v[0] / v[1] for k, v in prof.items()}, roofline=roof)
+    # counter-measured bytes of the step's L2 misses (TCC requests to the
+    # memory fabric, served by the last-level cache or HBM: an upper bound on
+    # the HBM bytes), from the committed summary of this workload when it was
+    # taken from the current sources
     if rec and rec.get("step"):
         gbs = rec["step"]["bytes"] / (ms * 1e-3) / 1e9
-        out.update(hbm_counter_GB_per_step=rec["step"]["bytes"] / 1e9, hbm_counter_GBs=gbs,
-                   hbm_frac=gbs / HBM_PEAK_GBS)
+        out.update(l2_miss_GB_per_step=rec["step"]["bytes"] / 1e9, l2_miss_GBs=gbs,
+                   l2_miss_frac_of_hbm_peak=gbs / HBM_PEAK_GBS)
     else:
-        out.update(hbm_counter_GB_per_step=None, hbm_counter_GBs=None, hbm_frac=None)
+        out.update(l2_miss_GB_per_step=None, l2_miss_GBs=None, l2_miss_frac_of_hbm_peak=None)
     return out
 
 
@@ -529,12 +552,12 @@ def main(argv=None):
     if args.calib_copy_mb:
         # one elementwise kernel that reads and writes calib_copy_mb MiB each,
         # and one reduction that only reads them
-        src = torch.ones((args.calib_copy_mb << 20) // 4, dtype=torch.int32, device=dev)
+        src = torch.ones((args.calib_copy_mb << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
-        total = src.sum()
+        total = src.sum()   # float32: reduced as it is, no widened copy first
         torch.cuda.synchronize()
         del src, dst, total
 
@@ -585,8 +608,8 @@ def main(argv=None):
                    "value_is_key": bool(args.value_is_key)},
         "mfma_frac": head["mfma_frac"],
         "alg_model_GBs": head["alg_model_GBs"],
-        "hbm_counter_GBs": head["hbm_counter_GBs"],
-        "hbm_frac": head["hbm_frac"],
+        "l2_miss_GBs": head["l2_miss_GBs"],
+        "l2_miss_frac_of_hbm_peak": head["l2_miss_frac_of_hbm_peak"],
         "kernels_ms": head["kernels_ms"],
         "roofline": head["roofline"],
     }

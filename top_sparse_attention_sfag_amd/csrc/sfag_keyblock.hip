@@ -75,6 +75,14 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t l) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(l) : "memory");
 }
 
+// Chunk swizzle of the 64-byte stage rows (4 chunks of 16 bytes): chunk q of
+// row r sits at position q ^ swz(r).  Any 8 consecutive rows then hit 8
+// different 16-byte bank groups of a 128-byte bank line, and any 16
+// consecutive rows 16 different groups of a 256-byte line, so the MFMA
+// operand reads (16 rows at one chunk, 8 or 16 lanes a cycle) meet no bank
+// conflict.  It depends on bits 1..3 of r only.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int64_t v) {
   int64_t lo = 0, hi = n;
   while (lo < hi) {
@@ -194,7 +202,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // ---- stage copies -------------------------------------------------------
   // A of stage (visit, ks): 256 rows x 4 chunks (heads 32ks + 8q .. +8), 16
   // instructions, wave w issuing w, w+4, w+8, w+12; the lane writing position
-  // p of row r fetches chunk p ^ ((r >> 2) & 3).  Rows not selected (and
+  // p of row r fetches chunk p ^ swz(r).  Rows not selected (and
   // chunks past the heads) take an offset outside the resource: they fetch
   // nothing and their slots receive zeros, which the MFMAs read as such.
   // B: the block's columns x 4 chunks likewise, NB per wave.
@@ -226,7 +234,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   auto issue_a = [&](const StageCopy& sc, int k) {
     const int i = wave + 4 * k;
     const int row = 16 * i + (lane >> 2);
-    const int q = (lane & 3) ^ ((row >> 2) & 3);
+    const int q = (lane & 3) ^ swz(row);
     const int hq = 32 * sc.ks + 8 * q;
     const uint32_t off = (sc.pr[k] >= 0 && hq < Gp) ? (uint32_t)(((sc.pr[k] - sc.p0) * Gp + hq) * 2) : kOutside;
     bdma16(sc.ars, off, sc.st + i * 1024);
@@ -234,7 +242,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   auto issue_b = [&](const StageCopy& sc, int k) {
     const int i = wave + 4 * k;
     const int col = 16 * i + (lane >> 2);
-    const int q = (lane & 3) ^ ((col >> 2) & 3);
+    const int q = (lane & 3) ^ swz(col);
     const int hq = 32 * sc.ks + 8 * q;
     const uint32_t off = hq < Gp ? (uint32_t)((col * Gp + hq) * 2) : kOutside;
     bdma16(sc.brs, off, sc.st + kStageA + i * 1024);
@@ -266,7 +274,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     for (int k = 0; k < 4; ++k) {
       const int i = wave + 4 * k;
       const int row = 16 * i + (lane >> 2);
-      const int q = (lane & 3) ^ ((row >> 2) & 3);
+      const int q = (lane & 3) ^ swz(row);
       const int hq = 32 * ks + 8 * q;
       const uint32_t off = (pr[k] >= 0 && hq < Gp) ? (uint32_t)(((pr[k] - p0) * Gp + hq) * 2) : kOutside;
       bdma16(ars, off, st + i * 1024);
@@ -276,7 +284,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     for (int k = 0; k < NB; ++k) {
       const int i = wave + 4 * k;
       const int col = 16 * i + (lane >> 2);
-      const int q = (lane & 3) ^ ((col >> 2) & 3);
+      const int q = (lane & 3) ^ swz(col);
       const int hq = 32 * ks + 8 * q;
       const uint32_t off = hq < Gp ? (uint32_t)((col * Gp + hq) * 2) : kOutside;
       bdma16(brs, off, st + kStageA + i * 1024);
@@ -300,12 +308,12 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // the stage (their copies fetch nothing and land zeros), so every row is
   // read as it is.
   auto compute = [&](const unsigned char* st, const StageCopy& sc) {
-    const int po = (g ^ (n >> 2)) << 4;          // rows mb*16 + n: (r >> 2) & 3 = n >> 2
+    const int po = (g ^ swz(n)) << 4;            // rows mb*16 + n: swz(r) = swz(n)
     V8 Bf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = bcol + 16 * nb;
-      Bf[nb] = as_vec8<V8>(*(const uint4*)(st + kStageA + col * 64 + ((g ^ ((col >> 2) & 3)) << 4)));
+      Bf[nb] = as_vec8<V8>(*(const uint4*)(st + kStageA + col * 64 + ((g ^ swz(col)) << 4)));
     }
     uint4 av[2][4];
     auto rd = [&](int h, uint4 (&dst)[4]) {
@@ -335,12 +343,12 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   auto compute16 = [&](const unsigned char* st, const StageCopy& sc) {
     typedef typename TT::vec4 V4;
     const int ch = g >> 1, hoff = (g & 1) << 3;
-    const int po = ((ch ^ (n >> 2)) << 4) + hoff;
+    const int po = ((ch ^ swz(n)) << 4) + hoff;
     V4 Bf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = bcol + 16 * nb;
-      Bf[nb] = __builtin_bit_cast(V4, *(const uint2*)(st + kStageA + col * 64 + ((ch ^ ((col >> 2) & 3)) << 4) + hoff));
+      Bf[nb] = __builtin_bit_cast(V4, *(const uint2*)(st + kStageA + col * 64 + ((ch ^ swz(col)) << 4) + hoff));
     }
     uint2 av[2][4];
     auto rd = [&](int h, uint2 (&dst)[4]) {

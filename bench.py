@@ -113,7 +113,7 @@ def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
 # Kernel groups of the timing API and the kernels (by demangled name) each
 # one stands for.
 _GROUPS = {
-    "sdp": r"k_sdp<", "dq": r"k_dq<", "row": r"k_row(16)?<", "keyblock": r"k_keyblock<", "transpose": r"k_transpose",
+    "sdp": r"k_sdp<", "dq": r"k_dq<", "row": r"k_row(16)?<", "keyblock": r"k_keyblock<",
     "col": r"k_col<", "fwd": r"k_fwd<", "kb_reduce": r"k_kb_reduce", "cast": r"k_cast<", "decode": r"k_decode",
     "delta": r"k_delta<",
 }
@@ -472,7 +472,7 @@ def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", val
     # alone; its duration from the timed region unless it shares the GPU with
     # the second stream's kernels there
     dom = max(rprof, key=lambda k: rprof[k][0])
-    overlapped = concurrent and dom in ("dq", "keyblock", "transpose", "kb_sort")
+    overlapped = concurrent and dom in ("dq", "keyblock", "kb_sort")
     src = rprof if overlapped or dom not in prof else prof
     dom_ms = src[dom][0] / src[dom][1]
     launches_per_step = src[dom][1] / (nsteps_r if src is rprof else steps)

@@ -130,14 +130,17 @@ def test_token_paths_agree(name):
         _run(case, seed=21, inp=inp, options=dict(token_path=path))
 
 
-def test_duplicated_indices():
-    case = si.Case("dup", S1=4, S2=64, G=16, K=40)
+@pytest.mark.parametrize("G,options", [(16, None), (128, dict(scatter="keyblock")), (112, dict(scatter="keyblock"))],
+                         ids=["g16", "g128_keyblock", "g112_keyblock"])
+def test_duplicated_indices(G, options):
+    case = si.Case("dup", S1=4, S2=300 if G > 16 else 64, G=G, K=40)
     inp = si.make_inputs(case, 3)
     idx = inp["sparse_indices"].reshape(4, 40)
     idx[0, 10:20] = idx[0, 0]          # one key ten times
     idx[2, :] = idx[2, 5]              # a whole row of one key
+    idx[3, 1] = idx[3, 0]              # one key twice
     inp = add_oracle_stats(case, inp)
-    _run(case, 3, inp=inp)
+    _run(case, 3, inp=inp, options=options)
 
 
 def test_masked_rows_never_read():
@@ -207,6 +210,20 @@ def test_deterministic_independent_of_chunking(path):
         torch.cuda.synchronize()
         for a, b in zip(base, chunked):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), opts
+
+
+# The key-block contraction at head counts that pad to 128 (the two-waves-per-
+# SIMD kernel, heads past N1 in its last 32-head stage) and to 64.
+KEYBLOCK_HEADS = [
+    si.Case("kb_g112_causal", S1=48, S2=300, G=112, K=96, mode=3, index_rule="causal_mix"),
+    si.Case("kb_g100_fp16_norope", S1=20, S2=280, G=100, Dr=0, K=80, dtype="fp16"),
+    si.Case("kb_g40_rope", S1=30, S2=270, G=40, K=70),
+]
+
+
+@pytest.mark.parametrize("case", KEYBLOCK_HEADS, ids=[c.name for c in KEYBLOCK_HEADS])
+def test_keyblock_head_counts(case):
+    _run(case, seed=11, options=dict(scatter="keyblock"))
 
 
 @pytest.mark.parametrize("path", ["keyblock", "atomic", "partials"])

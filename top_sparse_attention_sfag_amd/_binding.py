@@ -144,7 +144,7 @@ def lib():
     return _lib
 
 
-KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "sdp", "dq", "col", "csr", "key_reduce", "transpose", "kb_sort",
+KERNEL_GROUPS = ("seq_offsets", "delta", "fill", "decode", "row", "sdp", "dq", "col", "csr", "key_reduce", "kb_sort",
                  "keyblock", "kb_reduce", "cast", "fwd")
 
 

@@ -63,8 +63,6 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter, bool validate) {
     carve(c, w.sort_vals[0], n * 4);
     carve(c, w.sort_vals[1], n * 4);
     carve(c, w.sort_hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
-    carve(c, w.qT, ch * (uint64_t)(d.D + d.Dr) * d.Gp * 2);
-    carve(c, w.oT, ch * (uint64_t)d.D * d.Gp * 2);
     carve(c, w.kb_part, (uint64_t)d.nTR * d.T2 * d.AW * 4);
     carve(c, w.kb_nonempty, (uint64_t)d.nTR * d.nKB * 4);
     carve(c, w.vis_flags, n * 4);
@@ -411,10 +409,10 @@ int plan_launch(sfag_plan* p) {
   }
   // Chunk-sized bytes per token: index rows, dS and P (and for the partials
   // scatter the per-pair rows and the sort buffers; for the key-block path
-  // the sort and visit buffers and the transposed Q|Qr and dO copies).
+  // the sort and visit buffers).
   uint64_t per_tok = 4 + (uint64_t)d.E * 4 + 2 * (uint64_t)d.E * d.Gp * 2;
   if (partials) per_tok += (uint64_t)d.E * d.AW * 4 + 4 * (uint64_t)d.E * 4 + 64;
-  if (keyblock) per_tok += 8 * (uint64_t)d.E * 4 + 64 + (uint64_t)(2 * d.D + d.Dr) * d.Gp * 2;
+  if (keyblock) per_tok += 8 * (uint64_t)d.E * 4 + 64;
   const uint64_t fixed = fixed_bytes(partials);
   // the key-block sort key (key block * chunk + token) stays below 2^31
   const int64_t cap = keyblock ? std::min<int64_t>(pair_cap, 0x7ffffffeLL / std::max<int64_t>(1, d.nKB)) : pair_cap;

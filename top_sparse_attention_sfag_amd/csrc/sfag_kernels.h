@@ -29,21 +29,21 @@ constexpr int kMaxColBlocks = 6;
 
 // A block of output columns of the key-centric kernel: `src` 0 contracts dS
 // with [Q|Qr] (dK, dKrope), 1 contracts P with dO (dV); `tcol0` is the first
-// column in the transposed source, `ocol0` the first accumulator column.
+// column in the source rows, `ocol0` the first accumulator column.
 struct ColBlock {
   int32_t src, tcol0, ocol0, width;
 };
 
 struct KbArgs {
-  const uint16_t *qT, *oT;     // (ntok, 512+Dr, Gp) and (ntok, 512, Gp) transposed Q|Qr and dO
+  const uint16_t *q, *qr, *dO; // (T1, N1, 512), (T1, N1, Dr), (T1, N1, 512) as given
   const uint16_t *ds, *p;      // (ntok, E, Gp)
   const int32_t* svals;        // pair ids sorted by (key block, token)
   const int32_t* er;           // key row within its block of each sorted pair
   const int32_t *vis_start, *vis_key, *n_vis;  // visits: first sorted pair, composite key; count
   int32_t* nonempty;           // (nTR, nKB) flags
   float* part;                 // (nTR, T2, AW) partial sums per token range
-  int64_t ntok, E, Gp, T2, AW, TR, Dq;
-  int32_t nKB, nTR, nCB;
+  int64_t t0, ntok, E, G, Gp, T2, AW, TR;
+  int32_t Dr, nKB, nTR, nCB;
   ColBlock cbs[kMaxColBlocks];
 };
 
@@ -91,8 +91,6 @@ void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
 // N1 >= 32: the S/P/dP/dS kernel, then the dQ kernel (together they replace launch_row)
 void launch_sdp(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
 void launch_dq(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
-void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO, int64_t t0, int64_t ntok, int64_t G,
-                      int64_t Gp, int32_t Dr, uint16_t* qT, uint16_t* oT, hipStream_t s);
 void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s);
 void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows, int64_t n, int64_t ntok,
                    int32_t nkb, int32_t* flags, int32_t* scan_tmp, int32_t* vis_start, int32_t* vis_key, int32_t* er,

@@ -11,8 +11,9 @@
 //     C[key][col] += Σ_h A[key][h] · B[h][col]
 // with v_mfma_f32_16x16x32, where A holds the token's dS (or P) rows placed
 // at their key rows (rows the token does not select read a zero row) and B is
-// the token's Q|Qrope (or dO) from a per-token transposed copy, so that 8
-// consecutive heads of one column are 16 contiguous bytes.
+// the token's Q|Qrope (or dO) rows as they lie in memory (head-major): the
+// operand's column-of-heads fragments come out of LDS through the transposing
+// read ds_read_b64_tr_b16, so no transposed copy of the token side is made.
 //
 // A visit runs in four stages, one per 32-head step.  Both operands of a
 // stage reach LDS through global_load_lds, three stages ahead of their use
@@ -37,7 +38,6 @@ namespace sfag {
 namespace {
 
 constexpr int kKB = kKeyBlock;             // key rows per block (256)
-constexpr int kThreads = 256;              // 4 waves, one per SIMD
 constexpr int kStageA = kKB * 64;          // 256 rows x 32 heads, 16-bit
 constexpr int kStageB = 256 * 64;          // up to 256 columns x 32 heads
 constexpr int kStageBytes = kStageA + kStageB;
@@ -74,14 +74,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ void dma4(const void* g, uint32_t l) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(l) : "memory");
 }
+__device__ __forceinline__ void dma16(const void* g, uint32_t l) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(l) : "memory");
+}
+
+// 16 zero bytes: the source of B-stage slots of heads past N1.
+__device__ __attribute__((aligned(16))) uint4 g_zero16;
+
+// B stage: 32 head rows (the stage's heads) of NB * 64 columns, NB * 128
+// bytes each, in 16-byte chunks; chunk j of head row r sits at position
+// j ^ (2 * bswz<NB>(r)), which moves 32-byte chunk pairs within an aligned
+// group of 8 (NB = 3: 384-byte rows) or 16 (NB = 4) chunks.  The transposing
+// reads take one chunk pair from each of 4 consecutive head rows per 16
+// lanes (rows 8g + 0..3 or 8g + 4..7 with 32 heads, 4g + 0..3 with 16); the
+// swizzle puts the 4 rows of any 16 lanes on distinct 32-byte bank groups of
+// a 128-byte line, and the 8 rows of any 32 lanes on distinct groups of a
+// 256-byte line (for 384-byte rows counting the 128-byte shift of odd rows).
+template <int NB>
+__device__ __forceinline__ int bswz(int r) {
+  if constexpr (NB == 4) return (r & 7) ^ (((r >> 3) & 1) << 2);
+  else return (r & 3) ^ (((r >> 2) ^ (r >> 3)) & 1);
+}
 
 // Chunk swizzle of the 64-byte stage rows (4 chunks of 16 bytes): chunk q of
-// row r sits at position q ^ swz(r).  Any 8 consecutive rows then hit 8
-// different 16-byte bank groups of a 128-byte bank line, and any 16
-// consecutive rows 16 different groups of a 256-byte line, so the MFMA
-// operand reads (16 rows at one chunk, 8 or 16 lanes a cycle) meet no bank
-// conflict.  It depends on bits 1..3 of r only.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// row r sits at position q ^ swz(r).  The A-operand reads take chunk g of 16
+// consecutive rows per 16 lanes; of the row-dependent swizzles measured with
+// that access, (r >> 1) & 3 is one that runs it at the full ds_read_b128 rate
+// (about 200 bytes per clock per CU with 8 waves, against 128 for r & 3,
+// (r >> 2) & 3 or none).  It depends on bits 1..2 of r only.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
 __device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int64_t v) {
   int64_t lo = 0, hi = n;
@@ -110,6 +131,21 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// The same for a wave-uniform count (the values the key-block pipeline
+// uses; any other waits for everything, which is never too early).
+__device__ __forceinline__ void wait_copies(int n) {
+  switch (n) {
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 14: wait_vm<14>(); break;
+    case 16: wait_vm<16>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
 
 struct KbShared {
   int32_t cnt[3][kKB];       // per key row: how often the visit's token lists it
@@ -119,11 +155,14 @@ struct KbShared {
   int32_t vkey[kWin + 2];    // their composite keys
 };
 
-// One column block: NB 16-column MFMA blocks per wave (4 for 256 columns,
-// 3 for 192).  Wave w: all 256 key rows (16 MFMA row blocks), columns
-// w * 16 * NB .. of the block.  GP is the padded head count when it is 128
-// (all strides compile-time), else 0 (taken from the args).
-template <typename TT, int NB, int GP>
+// One column block of NB * 64 columns (NB = 4 for 256 columns, 3 for 192),
+// W waves (4 or 8).  Wave w takes the column quarter w % 4 (NB 16-column MFMA
+// blocks) and, with 4 waves, all 256 key rows (16 MFMA row blocks), with 8
+// waves the half w / 4 of them (8 row blocks): two waves per SIMD, each with
+// half the accumulators, so that one wave's waits are covered by the other's
+// MFMAs.  GP is the padded head count when it is 128 (all strides
+// compile-time), else 0 (taken from the args).
+template <typename TT, int NB, int GP, int W>
 __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int tr, int kb, int64_t vlo,
                                          int64_t vhi, unsigned char* __restrict__ st0,
                                          unsigned char* __restrict__ st1, unsigned char* __restrict__ st2,
@@ -136,16 +175,25 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
   const int Gp = GP ? GP : (int)a.Gp, nks = (Gp + 31) >> 5;
-  const uint16_t* Bsrc = c.src == 0 ? a.qT : a.oT;
-  const int64_t Bcols = c.src == 0 ? a.Dq : 512;
+  const uint16_t* Bmain = c.src == 0 ? a.q : a.dO;
   const uint16_t* Asrc = c.src == 0 ? a.ds : a.p;
   const int64_t kbase = (int64_t)kb * a.ntok;
-  constexpr int K = 4 + NB;   // copy instructions per wave and stage (A, B)
+  constexpr int NT = 64 * W;        // threads
+  constexpr int RB = 64 / W;        // MFMA row blocks per wave
+  constexpr int KA = 16 / W;        // A copy instructions per wave and stage
+  // B copy instructions per stage: 4 NB for 32 head rows, 2 NB with 16 heads
+  // (GP = 16: rows 16 .. 31 of the stage are never read)
+  constexpr int NBI = GP == 16 ? 2 * NB : 4 * NB;
+  constexpr int KBM = (NBI + W - 1) / W;
+  const int KB = (NBI - wave + W - 1) / W;      // B copy instructions of this wave and stage
+  const int K = KA + KB;                        // copy instructions per wave and stage
+  const int mb0 = (wave >> 2) * RB;             // first row block of the wave
+  const int cq = wave & 3;                      // column quarter of the wave
 
   // ---- visit metadata, staged in LDS for a window of visits from wb ------
   int64_t wb = vlo;
   auto load_window = [&]() {
-    for (int j = tid; j < kWin + 3; j += kThreads) {
+    for (int j = tid; j < kWin + 3; j += NT) {
       const int64_t x = wb + j;
       sh.vstart[j] = x <= vhi ? a.vis_start[x] : 0;
       if (j < kWin + 2) sh.vkey[j] = x < vhi ? a.vis_key[x] : 0;
@@ -155,16 +203,18 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   auto v_count = [&](int64_t v) -> int { return sh.vstart[v + 1 - wb] - sh.vstart[v - wb]; };
   auto v_token = [&](int64_t v) -> int64_t { return (int64_t)sh.vkey[v - wb] - kbase; };
 
-  f32x4 C[16][NB];
+  f32x4 C[RB][NB];
 #pragma unroll
-  for (int mb = 0; mb < 16; ++mb)
+  for (int mb = 0; mb < RB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) C[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- slot maps ----------------------------------------------------------
   auto reset = [&](int b) {
-    sh.cnt[b][tid] = 0;
-    sh.prim[b][tid] = -1;
+    if (tid < kKB) {
+      sh.cnt[b][tid] = 0;
+      sh.prim[b][tid] = -1;
+    }
     if (tid == 0) sh.rounds[b] = 1;
   };
   auto add_entry = [&](int b, int32_t pair, int row) {
@@ -179,18 +229,18 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     const int cnt = v_count(v);
     if (tid < cnt && tid < kEnt) add_entry(b, e_pair[eh * kEnt + tid], e_row[eh * kEnt + tid]);
     const int64_t s0 = v_start(v);
-    for (int j = tid + kEnt; j < cnt; j += kThreads) add_entry(b, a.svals[s0 + j], a.er[s0 + j]);
+    for (int j = tid + kEnt; j < cnt; j += NT) add_entry(b, a.svals[s0 + j], a.er[s0 + j]);
   };
   const uint32_t l_pair = lds_addr(e_pair), l_row = lds_addr(e_row);
   // copy of visit v's first kEnt pairs (ids and key rows) into LDS: 8
-  // dword-copy instructions, two per wave; lanes past the visit re-read
+  // dword-copy instructions, 8 / W per wave; lanes past the visit re-read
   // its first pair
   auto issue_entries = [&](int64_t v, int eh) {
     const int64_t s0 = v_start(v);
     const int cnt = v_count(v);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int ins = wave * 2 + k;          // 0..3 pair ids, 4..7 key rows
+    for (int k = 0; k < 8 / W; ++k) {
+      const int ins = wave * (8 / W) + k;    // 0..3 pair ids, 4..7 key rows
       const int part = ins & 3;
       const int e = part * 64 + lane;
       const int64_t src = s0 + (e < cnt ? e : 0);
@@ -201,38 +251,72 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 
   // ---- stage copies -------------------------------------------------------
   // A of stage (visit, ks): 256 rows x 4 chunks (heads 32ks + 8q .. +8), 16
-  // instructions, wave w issuing w, w+4, w+8, w+12; the lane writing position
+  // instructions, wave w issuing w, w + W, ...; the lane writing position
   // p of row r fetches chunk p ^ swz(r).  Rows not selected (and
   // chunks past the heads) take an offset outside the resource: they fetch
   // nothing and their slots receive zeros, which the MFMAs read as such.
-  // B: the block's columns x 4 chunks likewise, NB per wave.
-  // The copies of one stage, prepared once (slot-map entries read, buffer
-  // resources made) and then issued one A and one B instruction at a time
-  // between the MFMAs of the stage being computed: a burst of copies at the
-  // top of a stage stalls the issuing wave until the address unit takes them.
+  // B: the 32 head rows of the block's columns (bswz layout), 4 * NB
+  // instructions (2 * NB, rows 0 .. 15, with 16 heads), wave w issuing w,
+  // w + W, ...; the lane writing position e of the stage fetches the chunk
+  // of head row e / (8 NB) that belongs there, from Q or Qrope (a block may
+  // straddle the two) or dO; heads past N1 read 16 zero bytes.
+  // The copies of one stage, prepared once (slot-map entries read, sources
+  // made) and then issued one A and one B instruction at a time between the
+  // MFMAs of the stage being computed: a burst of copies at the top of a
+  // stage stalls the issuing wave until the address unit takes them.
+  const int G = (int)a.G;
+  const int Dr = a.Dr;
+  // Address of the zero chunk, made opaque so that it stays in registers: left
+  // to the compiler it is reloaded through a scalar load inside the copy
+  // code, and the wait for that load also waits for every LDS read in flight.
+  uint32_t z_lo = (uint32_t)(uintptr_t)&g_zero16, z_hi = (uint32_t)((uint64_t)(uintptr_t)&g_zero16 >> 32);
+  asm volatile("" : "+v"(z_lo), "+v"(z_hi));
+  // Per B instruction k, this lane's chunk: element offset from the stage's
+  // first head row in Q|dO or Qrope (bits 0..14), head row within the stage
+  // (bits 16..20), and whether it is a Qrope chunk (bit 21).
+  uint32_t b_chunk[KBM];
+#pragma unroll
+  for (int k = 0; k < KBM; ++k) {
+    const int e = 64 * (wave + W * k) + lane;
+    const int hr = e / (8 * NB), pos = e - hr * (8 * NB);
+    const int col = c.tcol0 + 8 * (pos ^ (2 * bswz<NB>(hr)));
+    const bool rope = c.src == 0 && col >= 512;
+    const uint32_t off = rope ? (uint32_t)(hr * Dr + (col - 512)) : (uint32_t)(hr * 512 + col);
+    b_chunk[k] = off | ((uint32_t)hr << 16) | ((uint32_t)rope << 21);
+  }
   struct StageCopy {
-    __amdgpu_buffer_rsrc_t ars, brs;
-    int32_t pr[4];
+    __amdgpu_buffer_rsrc_t ars;
+    const uint16_t *bm, *br;   // rows of head 32ks of the token in Q|dO and Qrope
+    int32_t pr[KA];
     int32_t p0;
     int ks;
     uint32_t st;
     bool on;
   };
+  auto b_rows = [&](StageCopy& sc, int64_t tl, int ks) {
+    const int64_t hrow = (a.t0 + tl) * a.G + 32 * ks;
+    sc.bm = Bmain + hrow * 512;
+    sc.br = a.qr + hrow * Dr;
+  };
+  auto b_src = [&](const StageCopy& sc, int k) -> const void* {
+    const uint32_t x = b_chunk[k];
+    if (32 * sc.ks + (int)((x >> 16) & 31) >= G) return (const void*)(((uint64_t)z_hi << 32) | z_lo);
+    return ((x >> 21) ? sc.br : sc.bm) + (x & 0x7fff);
+  };
   auto prep_stage = [&](StageCopy& sc, bool on, int b, int64_t tl, int ks, uint32_t st) {
     sc.on = on;
     if (!on) return;
-    // A rows of token tl: pairs tl*E .. tl*E + E - 1; B: the block's
-    // columns of the token's transposed copy
+    // A rows of token tl: pairs tl*E .. tl*E + E - 1
     sc.ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
-    sc.brs = make_rsrc(Bsrc + (tl * Bcols + c.tcol0) * Gp, (int)(NB * 64 * Gp * 2));
+    b_rows(sc, tl, ks);
     sc.p0 = (int32_t)(tl * a.E);
     sc.ks = ks;
     sc.st = st;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sc.pr[k] = sh.prim[b][16 * (wave + 4 * k) + (lane >> 2)];
+    for (int k = 0; k < KA; ++k) sc.pr[k] = sh.prim[b][16 * (wave + W * k) + (lane >> 2)];
   };
   auto issue_a = [&](const StageCopy& sc, int k) {
-    const int i = wave + 4 * k;
+    const int i = wave + W * k;
     const int row = 16 * i + (lane >> 2);
     const int q = (lane & 3) ^ swz(row);
     const int hq = 32 * sc.ks + 8 * q;
@@ -240,24 +324,20 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     bdma16(sc.ars, off, sc.st + i * 1024);
   };
   auto issue_b = [&](const StageCopy& sc, int k) {
-    const int i = wave + 4 * k;
-    const int col = 16 * i + (lane >> 2);
-    const int q = (lane & 3) ^ swz(col);
-    const int hq = 32 * sc.ks + 8 * q;
-    const uint32_t off = hq < Gp ? (uint32_t)((col * Gp + hq) * 2) : kOutside;
-    bdma16(sc.brs, off, sc.st + kStageA + i * 1024);
+    dma16(b_src(sc, k), sc.st + kStageA + (wave + W * k) * 1024);
   };
   auto issue_part = [&](const StageCopy& sc, int k) {
     if (!sc.on) return;
-    issue_a(sc, k);
-    if (k < NB) issue_b(sc, k);
+    if (k < KA) issue_a(sc, k);
+    if (k < KBM && k < KB) issue_b(sc, k);
   };
   auto issue_all = [&](StageCopy& sc) {
     if (sc.on) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) issue_a(sc, k);
+      for (int k = 0; k < KA; ++k) issue_a(sc, k);
 #pragma unroll
-      for (int k = 0; k < NB; ++k) issue_b(sc, k);
+      for (int k = 0; k < KBM; ++k)
+        if (k < KB) issue_b(sc, k);
     }
     sc.on = false;
   };
@@ -265,30 +345,9 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // (Gp != 128) waits for every copy at each stage, so spreading its copies
   // over the MFMAs would leave the last ones no time before that wait.
   auto issue_stage = [&](int b, int64_t tl, int ks, uint32_t st) {
-    const __amdgpu_buffer_rsrc_t ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
-    const int32_t p0 = (int32_t)(tl * a.E);
-    int32_t pr[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pr[k] = sh.prim[b][16 * (wave + 4 * k) + (lane >> 2)];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = wave + 4 * k;
-      const int row = 16 * i + (lane >> 2);
-      const int q = (lane & 3) ^ swz(row);
-      const int hq = 32 * ks + 8 * q;
-      const uint32_t off = (pr[k] >= 0 && hq < Gp) ? (uint32_t)(((pr[k] - p0) * Gp + hq) * 2) : kOutside;
-      bdma16(ars, off, st + i * 1024);
-    }
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bsrc + (tl * Bcols + c.tcol0) * Gp, (int)(NB * 64 * Gp * 2));
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int i = wave + 4 * k;
-      const int col = 16 * i + (lane >> 2);
-      const int q = (lane & 3) ^ swz(col);
-      const int hq = 32 * ks + 8 * q;
-      const uint32_t off = hq < Gp ? (uint32_t)((col * Gp + hq) * 2) : kOutside;
-      bdma16(brs, off, st + kStageA + i * 1024);
-    }
+    StageCopy sc;
+    prep_stage(sc, true, b, tl, ks, st);
+    issue_all(sc);
   };
   // Round r of a stage (r >= 1, keys listed more than once by the token):
   // the rows listed exactly r times leave the sum, so their stage rows are
@@ -296,40 +355,62 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // round).
   auto drop_rows = [&](unsigned char* st, int b, int r) {
     bar();
-    if (sh.cnt[b][tid] == r) {
+    if (tid < kKB && sh.cnt[b][tid] == r) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) *(uint4*)(st + tid * 64 + j * 16) = make_uint4(0, 0, 0, 0);
     }
     bar();
   };
   // C += A · B over the 32 heads of one stage
-  const int bcol = wave * 16 * NB + n;
+  // B fragments: lane (g, n) of column block nb takes column
+  // 16 (NB cq + nb) + n of the block; a transposing read from head row r
+  // (lanes 4m .. 4m + 3 of each 16 addressing row r0 + m, columns 4 apart)
+  // gives it heads r0 .. r0 + 3.  Byte offset in the B stage of the 8 bytes
+  // this lane addresses in head row r:
+  auto boff = [&](int r, int nb) -> int {
+    return r * (NB * 128) + ((2 * ((NB * cq + nb) ^ bswz<NB>(r)) + ((n & 3) >> 1)) << 4) + 8 * (n & 1);
+  };
   // Rows the token does not select, and head chunks past Gp, hold zeros in
   // the stage (their copies fetch nothing and land zeros), so every row is
   // read as it is.
   auto compute = [&](const unsigned char* st, const StageCopy& sc) {
     const int po = (g ^ swz(n)) << 4;            // rows mb*16 + n: swz(r) = swz(n)
+    // heads 8g .. 8g + 7: head rows 8g + n / 4 and 4 further
+    const int r0 = 8 * g + (n >> 2);
     V8 Bf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = bcol + 16 * nb;
-      Bf[nb] = as_vec8<V8>(*(const uint4*)(st + kStageA + col * 64 + ((g ^ swz(col)) << 4)));
+      const unsigned char* bs = st + kStageA;
+      Bf[nb] = join_tr<V8>(lds_read_tr((const uint16_t*)(bs + boff(r0, nb))),
+                           lds_read_tr((const uint16_t*)(bs + boff(r0 + 4, nb))));
     }
     uint4 av[2][4];
     auto rd = [&](int h, uint4 (&dst)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int mb = 4 * h + j;
+        const int mb = mb0 + 4 * h + j;
         dst[j] = *(const uint4*)(st + (mb * 16 + n) * 64 + po);
       }
     };
+    // The reads of row group h + 1 go out ahead of the MFMAs of group h (the
+    // scheduler would otherwise sink them below most of those MFMAs, leaving
+    // the LDS latency exposed at the next group), and the stage copies
+    // between the two halves of the group's MFMAs.
     rd(0, av[0]);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      if (h + 1 < 4) rd(h + 1, av[(h + 1) & 1]);
-      issue_part(sc, h);   // nothing unless the caller prepared copies
+    for (int h = 0; h < RB / 4; ++h) {
+      if (h + 1 < RB / 4) rd(h + 1, av[(h + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          C[4 * h + j][nb] = TT::mfma(as_vec8<V8>(av[h & 1][j]), Bf[nb], C[4 * h + j][nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_part(sc, h);   // nothing unless the caller prepared copies
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 2; j < 4; ++j)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           C[4 * h + j][nb] = TT::mfma(as_vec8<V8>(av[h & 1][j]), Bf[nb], C[4 * h + j][nb]);
@@ -338,33 +419,40 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 
   // The same for 16 heads (Gp = 16: the upper half of every stage row is
   // zero): v_mfma_f32_16x16x16 over the 16 live heads, half the MFMA work
-  // and half the operand reads.  Lane group g takes heads 4g .. 4g + 3, the
-  // 8-byte half g & 1 of 16-byte chunk g >> 1.
+  // and half the operand reads.  Lane group g takes heads 4g .. 4g + 3: the
+  // 8-byte half g & 1 of 16-byte chunk g >> 1 of an A row, head rows
+  // 4g .. 4g + 3 of the B stage.
   auto compute16 = [&](const unsigned char* st, const StageCopy& sc) {
     typedef typename TT::vec4 V4;
     const int ch = g >> 1, hoff = (g & 1) << 3;
     const int po = ((ch ^ swz(n)) << 4) + hoff;
     V4 Bf[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = bcol + 16 * nb;
-      Bf[nb] = __builtin_bit_cast(V4, *(const uint2*)(st + kStageA + col * 64 + ((ch ^ swz(col)) << 4) + hoff));
-    }
+    for (int nb = 0; nb < NB; ++nb)
+      Bf[nb] = __builtin_bit_cast(V4, lds_read_tr((const uint16_t*)(st + kStageA + boff(4 * g + (n >> 2), nb))));
     uint2 av[2][4];
     auto rd = [&](int h, uint2 (&dst)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int mb = 4 * h + j;
+        const int mb = mb0 + 4 * h + j;
         dst[j] = *(const uint2*)(st + (mb * 16 + n) * 64 + po);
       }
     };
     rd(0, av[0]);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      if (h + 1 < 4) rd(h + 1, av[(h + 1) & 1]);
-      issue_part(sc, h);
+    for (int h = 0; h < RB / 4; ++h) {
+      if (h + 1 < RB / 4) rd(h + 1, av[(h + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          C[4 * h + j][nb] = TT::mfma16(__builtin_bit_cast(V4, av[h & 1][j]), Bf[nb], C[4 * h + j][nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_part(sc, h);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 2; j < 4; ++j)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           C[4 * h + j][nb] = TT::mfma16(__builtin_bit_cast(V4, av[h & 1][j]), Bf[nb], C[4 * h + j][nb]);
@@ -376,9 +464,8 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // copies of the (up to) two following stages and pair copies
   auto wait_stage = [&](int64_t s) {
     const int later = (s + 1 < nst ? 1 : 0) + (s + 2 < nst ? 1 : 0);
-    if (GP != 128 || later == 0) wait_vm<0>();
-    else if (later == 2) wait_vm<2 * K>();
-    else wait_vm<K>();
+    if (GP != 128) wait_vm<0>();
+    else wait_copies(later * K);
   };
   auto stage_buf = [&](int ks) -> unsigned char* { return ks == 0 ? st0 : ks == 1 ? st1 : ks == 2 ? st2 : st3; };
   const uint32_t L0 = lds_addr(st0), L1 = lds_addr(st1), L2 = lds_addr(st2), L3 = lds_addr(st3);
@@ -393,7 +480,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     if (v < vhi) {
       const int64_t s0 = v_start(v);
       const int cnt = v_count(v);
-      for (int j = tid; j < cnt; j += kThreads) add_entry(x, a.svals[s0 + j], a.er[s0 + j]);
+      for (int j = tid; j < cnt; j += NT) add_entry(x, a.svals[s0 + j], a.er[s0 + j]);
     }
   }
   __syncthreads();
@@ -423,7 +510,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       }
       // stage(v) and pairs(v + 2) have landed once at most stage(v + 1),
       // issued after them, is outstanding
-      if (v + 1 < vhi) wait_vm<K>();
+      if (v + 1 < vhi) wait_copies(K);
       else wait_vm<0>();
       bar();
       const int R = sh.rounds[u];
@@ -563,12 +650,12 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 
   // ---- partial of this token range ----------------------------------------
   float* out = a.part + (int64_t)tr * a.T2 * a.AW;
-  const int ocol = c.ocol0 + wave * 16 * NB + n;
+  const int ocol = c.ocol0 + cq * 16 * NB + n;
 #pragma unroll
-  for (int mb = 0; mb < 16; ++mb) {
+  for (int mb = 0; mb < RB; ++mb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = (int64_t)kb * kKB + mb * 16 + 4 * g + i;
+      const int64_t row = (int64_t)kb * kKB + (mb0 + mb) * 16 + 4 * g + i;
       if (row < a.T2) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) out[row * a.AW + ocol + 16 * nb] = C[mb][nb][i];
@@ -579,11 +666,11 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 
 }  // namespace
 
-// GPK = 16: the 16-head variant only (its own kernel, so that its operand
-// registers do not weigh on the other variants' allocation); 0: Gp = 128 or
-// the generic path, chosen from the arguments.
+// GPK = 16 or 128: the variant for that padded head count only (each its own
+// kernel, so that no variant's registers weigh on another's allocation); 0:
+// the generic path.
 template <typename TT, int GPK>
-__global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
+__global__ void __launch_bounds__(GPK == 128 ? 512 : 256, 1) k_keyblock(KbArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char st1[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char st2[kStageBytes];
@@ -613,14 +700,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_keyblock(KbArgs a) {
   if (threadIdx.x == 0 && cb == 0) a.nonempty[(int64_t)tr * a.nKB + kb] = vhi > vlo ? 1 : 0;
   if (vhi <= vlo) return;
   if constexpr (GPK == 16) {
-    if (c.width == 256) kb_block<TT, 4, 16>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
-    else kb_block<TT, 3, 16>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
-  } else if (a.Gp == 128) {
-    if (c.width == 256) kb_block<TT, 4, 128>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
-    else kb_block<TT, 3, 128>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    if (c.width == 256) kb_block<TT, 4, 16, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 16, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+  } else if constexpr (GPK == 128) {
+    if (c.width == 256) kb_block<TT, 4, 128, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 128, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   } else {
-    if (c.width == 256) kb_block<TT, 4, 0>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
-    else kb_block<TT, 3, 0>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    if (c.width == 256) kb_block<TT, 4, 0, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 0, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   }
 }
 
@@ -688,57 +775,16 @@ __global__ void __launch_bounds__(256) k_kb_reduce(const float* __restrict__ par
   }
 }
 
-// Per-token transposed copies: qT[tl][c][h] = [Q|Qr][t][h][c] and
-// oT[tl][c][h] = dO[t][h][c], heads padded with zeros to Gp.  One block per
-// (token, 64-column slice).
-__global__ void __launch_bounds__(256) k_transpose(const uint16_t* __restrict__ q, const uint16_t* __restrict__ qr,
-                                                   const uint16_t* __restrict__ dO, int64_t t0, int64_t G, int64_t Gp,
-                                                   int32_t Dr, uint16_t* __restrict__ qT, uint16_t* __restrict__ oT) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][128 + 8];
-  const int64_t Dq = 512 + Dr;
-  const int nsl_q = (int)(Dq / 64), nsl = nsl_q + 8;
-  const int64_t tl = blockIdx.x / nsl;
-  const int sl = blockIdx.x % nsl;
-  const int64_t t = t0 + tl;
-  const bool isq = sl < nsl_q;
-  const int c0 = isq ? sl * 64 : (sl - nsl_q) * 64;
-  // load [G][64] as 16-byte chunks: thread -> (head, chunk)
-  for (int x = threadIdx.x; x < Gp * 8; x += 256) {
-    const int hh = x >> 3, ch = x & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (hh < G) {
-      const int c = c0 + ch * 8;
-      if (!isq) v = *(const uint4*)(dO + (t * G + hh) * 512 + c);
-      else if (c < 512) v = *(const uint4*)(q + (t * G + hh) * 512 + c);
-      else v = *(const uint4*)(qr + (t * G + hh) * Dr + (c - 512));
-    }
-    const uint16_t* pv = (const uint16_t*)&v;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) tile[ch * 8 + k][hh] = pv[k];
-  }
-  __syncthreads();
-  uint16_t* dst = isq ? qT + (tl * Dq + c0) * Gp : oT + (tl * 512 + c0) * Gp;
-  const int CH = (int)(Gp / 8);
-  for (int x = threadIdx.x; x < 64 * CH; x += 256) {
-    const int c = x / CH, ch = x - c * CH;
-    *(uint4*)(dst + c * Gp + ch * 8) = *(const uint4*)&tile[c][ch * 8];
-  }
-}
-
-void launch_transpose(const uint16_t* q, const uint16_t* qr, const uint16_t* dO, int64_t t0, int64_t ntok, int64_t G,
-                      int64_t Gp, int32_t Dr, uint16_t* qT, uint16_t* oT, hipStream_t s) {
-  if (ntok == 0) return;
-  const int nsl = (512 + Dr) / 64 + 8;
-  hipLaunchKernelGGL(k_transpose, dim3((unsigned)(ntok * nsl)), dim3(256), 0, s, q, qr, dO, t0, G, Gp, Dr, qT, oT);
-}
-
 void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s) {
   // token ranges per XCD: two per group of 16 (see the unit order above)
   const int64_t per_xcd = 2 * (((int64_t)a.nTR + 15) / 16);
-  const dim3 grid((unsigned)(kXcds * per_xcd * a.nKB * a.nCB)), block(kThreads);
+  const dim3 grid((unsigned)(kXcds * per_xcd * a.nKB * a.nCB)), block(a.Gp == 128 ? 512 : 256);
   if (a.Gp == 16) {
     if (dtype == SFAG_BF16) hipLaunchKernelGGL((k_keyblock<BF16, 16>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_keyblock<FP16, 16>), grid, block, 0, s, a);
+  } else if (a.Gp == 128) {
+    if (dtype == SFAG_BF16) hipLaunchKernelGGL((k_keyblock<BF16, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_keyblock<FP16, 128>), grid, block, 0, s, a);
   } else {
     if (dtype == SFAG_BF16) hipLaunchKernelGGL((k_keyblock<BF16, 0>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_keyblock<FP16, 0>), grid, block, 0, s, a);

@@ -386,7 +386,7 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
   // k_dq runs beside the key-block kernels (64 heads, 8192 varlen tokens,
   // top-2048 causal: 9.4 -> 8.4 ms; with 128 heads no gain at 4096 tokens
   // and +3% at 32768, so off there by default).  Running the key-block
-  // pre-work (transposes, sort, visits) beside k_sdp instead measured no gain
+  // pre-work (then transposes, sort, visits) beside k_sdp instead measured no gain
   // (128 heads, 4096 tokens: 7.67 -> 7.89 ms), so it stays on `stream`.  The
   // caller's auxiliary stream if it gave one (with events of the call's own),
   // else the library's, whose events this call holds for its whole enqueue
@@ -422,16 +422,10 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
   auto order = [&](hipStream_t a, hipStream_t b, SideEvent e) {
     return hipEventRecord(side->ev[e], a) == hipSuccess && hipStreamWaitEvent(b, side->ev[e], 0) == hipSuccess;
   };
-  uint16_t* qT = keyblock ? at<uint16_t>(workspace, w.qT) : nullptr;
-  uint16_t* oT = keyblock ? at<uint16_t>(workspace, w.oT) : nullptr;
   int32_t* skeys = nullptr;
   int32_t* svals = nullptr;
-  // transposed copies, sort by key block, visits of one chunk on stream `st`
-  auto pre_work = [&](int64_t t0, int64_t ntok, hipStream_t st) {
-    {
-      TimedScope ts("transpose", st);
-      launch_transpose(ra.q, ra.qr, ra.dO, t0, ntok, d.G, d.Gp, (int32_t)d.Dr, qT, oT, st);
-    }
+  // sort by key block and visits of one chunk on stream `st`
+  auto pre_work = [&](int64_t ntok, hipStream_t st) {
     const int64_t n = ntok * d.E;
     TimedScope ts("kb_sort", st);
     launch_csr(n, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals, at<int32_t>(workspace, w.sort_hist),
@@ -479,11 +473,12 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
       launch_row(plan->dtype, rope, ra, s);
     }
     if (kb_work) {
-      pre_work(t0, ntok, s);
+      pre_work(ntok, s);
       {
         KbArgs ka;
-        ka.qT = qT;
-        ka.oT = oT;
+        ka.q = ra.q;
+        ka.qr = ra.qr;
+        ka.dO = ra.dO;
         ka.ds = ds;
         ka.p = pb;
         ka.svals = svals;
@@ -493,13 +488,15 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
         ka.n_vis = at<int32_t>(workspace, w.vis_n);
         ka.nonempty = at<int32_t>(workspace, w.kb_nonempty);
         ka.part = at<float>(workspace, w.kb_part);
+        ka.t0 = t0;
         ka.ntok = ntok;
         ka.E = d.E;
+        ka.G = d.G;
         ka.Gp = d.Gp;
         ka.T2 = d.T2;
         ka.AW = d.AW;
         ka.TR = d.TR;
-        ka.Dq = d.D + d.Dr;
+        ka.Dr = (int32_t)d.Dr;
         ka.nKB = (int32_t)d.nKB;
         ka.nTR = (int32_t)((ntok + d.TR - 1) / d.TR);
         // column blocks: dK|dKrope (three of 192 with rope, two of 256

@@ -32,8 +32,6 @@ struct WorkspaceLayout {
   uint64_t sort_vals[2] = {0, 0};
   uint64_t sort_hist = 0;  // int32 (256, nblocks)
   uint64_t csr_off = 0;    // int32 (T2 + 1)
-  uint64_t qT = 0;         // 16-bit (chunk, 512 + Dr, Gp): per-token transposed Q|Qr
-  uint64_t oT = 0;         // 16-bit (chunk, 512, Gp): per-token transposed dO
   uint64_t kb_part = 0;    // fp32 (nTR, T2, AW): per token-range partial sums
   uint64_t kb_nonempty = 0;  // int32 (nTR, nKB)
   uint64_t vis_flags = 0;  // int32 (chunk*E): visit starts, scanned in place

@@ -25,8 +25,9 @@
 // by one token has k identical dS/P rows (same token, same key), so each
 // stage of that visit runs k rounds over the row.
 //
-// C stays in registers (AGPRs; one wave per SIMD) for the whole token range
-// and is written once as an fp32 partial of that range; a second kernel adds
+// C stays in registers (8 waves, two per SIMD, each with a 128-key half of
+// the rows and a quarter of the columns) for the whole token range and is
+// written once as an fp32 partial of that range; a second kernel adds
 // the partials of the ranges in ascending order.  Every sum runs in a fixed
 // order, so the result is bitwise reproducible.
 #include "sfag_device.h"
@@ -135,6 +136,7 @@ __device__ __forceinline__ void wait_vm() {
 // uses; any other waits for everything, which is never too early).
 __device__ __forceinline__ void wait_copies(int n) {
   switch (n) {
+    case 2: wait_vm<2>(); break;
     case 3: wait_vm<3>(); break;
     case 4: wait_vm<4>(); break;
     case 5: wait_vm<5>(); break;
@@ -670,7 +672,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
 // kernel, so that no variant's registers weigh on another's allocation); 0:
 // the generic path.
 template <typename TT, int GPK>
-__global__ void __launch_bounds__(GPK == 128 ? 512 : 256, 1) k_keyblock(KbArgs a) {
+__global__ void __launch_bounds__(512, 1) k_keyblock(KbArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char st0[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char st1[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char st2[kStageBytes];
@@ -700,14 +702,14 @@ __global__ void __launch_bounds__(GPK == 128 ? 512 : 256, 1) k_keyblock(KbArgs a
   if (threadIdx.x == 0 && cb == 0) a.nonempty[(int64_t)tr * a.nKB + kb] = vhi > vlo ? 1 : 0;
   if (vhi <= vlo) return;
   if constexpr (GPK == 16) {
-    if (c.width == 256) kb_block<TT, 4, 16, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
-    else kb_block<TT, 3, 16, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    if (c.width == 256) kb_block<TT, 4, 16, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 16, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   } else if constexpr (GPK == 128) {
     if (c.width == 256) kb_block<TT, 4, 128, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
     else kb_block<TT, 3, 128, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   } else {
-    if (c.width == 256) kb_block<TT, 4, 0, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
-    else kb_block<TT, 3, 0, 4>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    if (c.width == 256) kb_block<TT, 4, 0, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
+    else kb_block<TT, 3, 0, 8>(a, c, tr, kb, vlo, vhi, st0, st1, st2, st3, &sh, e_pair, e_row);
   }
 }
 
@@ -778,7 +780,7 @@ __global__ void __launch_bounds__(256) k_kb_reduce(const float* __restrict__ par
 void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s) {
   // token ranges per XCD: two per group of 16 (see the unit order above)
   const int64_t per_xcd = 2 * (((int64_t)a.nTR + 15) / 16);
-  const dim3 grid((unsigned)(kXcds * per_xcd * a.nKB * a.nCB)), block(a.Gp == 128 ? 512 : 256);
+  const dim3 grid((unsigned)(kXcds * per_xcd * a.nKB * a.nCB)), block(512);
   if (a.Gp == 16) {
     if (dtype == SFAG_BF16) hipLaunchKernelGGL((k_keyblock<BF16, 16>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_keyblock<FP16, 16>), grid, block, 0, s, a);

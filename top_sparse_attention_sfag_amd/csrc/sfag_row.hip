@@ -317,8 +317,8 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
 
 // ---------------------------------------------------------------------------
 // k_row16: the fused token kernel for up to 16 heads (one head block of 16),
-// with the work of a tile spread over all four waves and two tiles of
-// gathered rows in flight.
+// with the work of a tile spread over all four waves and two workgroups per
+// CU (one or two tile buffers each, see kSingle).
 //
 //   * Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ of a 32-position tile: wave 0 / 1 form Sᵀ of
 //     positions 0..15 / 16..31 (Q in registers), wave 2 / 3 dPᵀ of the same
@@ -331,15 +331,16 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
 //     the prologue by wave 2, which holds dO, and handed over through LDS.
 //   * Waves 0..2 issue the tile copies (global_load_lds) and no other
 //     vector-memory work inside the loop, so a wait on their copy counter
-//     can leave the next tile's copies in flight: the copies of tile i + 2 go
-//     out as soon as every wave is done with tile i, while tile i + 1's are
-//     still landing.  Wave 3 issues no copies; it stores the P and dS rows
-//     (staged in LDS, double buffered) and loads the row indices of the tile
-//     after next into LDS, so the copying waves never wait on a load of
-//     their own.
+//     counts copies only.  With two buffers that wait leaves the next tile's
+//     copies in flight: the copies of tile i + 2 go out as soon as every
+//     wave is done with tile i, while tile i + 1's are still landing; with
+//     one, tile i + 1's go out then and are waited for in full.  Wave 3
+//     issues no copies; it stores the P and dS rows (staged in LDS, double
+//     buffered) and loads the row indices of the tile whose copies go out
+//     next into LDS, so the copying waves never wait on a load of their own.
 // ---------------------------------------------------------------------------
 template <typename TT, int DR, bool VK>
-__global__ void __launch_bounds__(256, 1) k_row16(RowArgs a) {
+__global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int KS_QK = DQK / 32;          // 16x16x32 k-steps of S (rope last)
   constexpr int KS_V = 512 / 32;
@@ -356,7 +357,15 @@ __global__ void __launch_bounds__(256, 1) k_row16(RowArgs a) {
   constexpr int kRowOps = VK ? 1 : 2;
   typedef typename TT::vec8 V8;
 
-  __shared__ __attribute__((aligned(16))) unsigned char tbuf[2][BUF];
+  // Two workgroups share a CU, each one's phases (and its copies' latency)
+  // overlapping the other's: with separate K and V rows (64 KB a tile) or
+  // rope rows each workgroup has one tile buffer, with value = key and no
+  // rope two (the next tile landing during this one).  Config-4 shape (16
+  // heads, 8192 positions, separate V): 74.9 -> 66.5 ms against one
+  // double-buffered workgroup per CU; 4 heads with rope: 0.056 -> 0.043 ms.
+  constexpr bool kSingle = !VK || DR > 0;
+  constexpr int kAhead = kSingle ? kTile : 2 * kTile;   // positions between a tile and its copies' issue
+  __shared__ __attribute__((aligned(16))) unsigned char tbuf[kSingle ? 1 : 2][BUF];
   __shared__ __attribute__((aligned(16))) float xdp[16 * XSTR];
   __shared__ __attribute__((aligned(16))) uint16_t dsT[16 * DSTR];
   __shared__ __attribute__((aligned(16))) uint16_t stg[2][2][kTile * 16];   // [buffer][P, dS][position][head]
@@ -500,22 +509,24 @@ __global__ void __launch_bounds__(256, 1) k_row16(RowArgs a) {
 
   if (copier && cb < ce) {
     issue(key0, 0);
-    if (cb + kTile < ce) issue(key1, 1);
+    if (!kSingle && cb + kTile < ce) issue(key1, 1);
   }
   int cur = 0, it = 0;
-  for (int c0 = cb; c0 < ce; c0 += kTile, cur ^= 1, ++it) {
+  for (int c0 = cb; c0 < ce; c0 += kTile, cur ^= (kSingle ? 0 : 1), ++it) {
     const bool more = c0 + kTile < ce;
     if (copier) {
-      if (more) wait_one_tile();
+      if (more && !kSingle) wait_one_tile();
       else __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
     }
     __syncthreads();
     const unsigned char* Km = tbuf[cur];
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
-    // wave 3: row indices of the tile after next, into LDS for the copiers
-    if (wave == 3 && c0 + 2 * kTile < ce && lane < kTile) {
-      const int c = c0 + 2 * kTile + lane;
+    // wave 3: row indices of the tile whose copies go out at the end of this
+    // one (the next with one buffer, the one after with two), into LDS for
+    // the copiers
+    if (wave == 3 && c0 + kAhead < ce && lane < kTile) {
+      const int c = c0 + kAhead + lane;
       keys_s[lane] = rt[c < ce ? c : cb];
     }
     // ---- Sᵀ (waves 0, 1) or dPᵀ (waves 2, 3) of positions 16 mb .. +15
@@ -583,8 +594,9 @@ __global__ void __launch_bounds__(256, 1) k_row16(RowArgs a) {
       for (int j = 0; j < NBW; ++j) acc[j] = TT::mfma(A8, kread(wave + 4 * j), acc[j]);
     }
     __syncthreads();
-    // every wave is done with this buffer: the copies of the tile after next
-    if (copier && c0 + 2 * kTile < ce) {
+    // every wave is done with this buffer: the copies of the next tile (one
+    // buffer) or the one after (two)
+    if (copier && c0 + kAhead < ce) {
       const int32_t keyv = keys_s[lane & 31];
       issue(keyv, cur);
     }

@@ -428,6 +428,230 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_sdp8: the same for a block of 128 heads as 8 waves of 16 heads, two waves
+// per SIMD.  With 16 heads a wave holds its Q and dO rows in 136 registers
+// (32 heads need 272, which leaves one wave per SIMD), so each SIMD has a
+// second wave whose MFMAs run while the first waits.  S and dP of a tile
+// come from v_mfma_f32_16x16x32 (16 heads x 16 positions, two position
+// blocks); lane (g, n) then holds heads 4g .. 4g + 3 of the wave at position
+// n of each block.  Every wave reads the whole tile from LDS, twice the LDS
+// traffic of 32-head waves.
+// ---------------------------------------------------------------------------
+template <typename TT, int DR, bool VK>
+__global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int KS_QK = DQK / 32;   // k-steps of 32 along D+Dr (rope last)
+  constexpr int KS_V = 512 / 32;
+  constexpr int KM_BYTES = kTile * 1024;
+  constexpr int KR_BYTES = kTile * DR * 2;
+  constexpr int BUF = KM_BYTES + KR_BYTES + (VK ? 0 : kTile * 1024);
+  typedef typename TT::vec8 V8;
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
+  // P and dS of a tile as (tensor, position) rows of 128 heads (256 bytes);
+  // 16-byte chunk j of row r sits at chunk j ^ (r & 15)
+  __shared__ __attribute__((aligned(16))) unsigned char stg[2 * kTile * 256];
+
+  int hb;
+  const int64_t tl = unit_token(blockIdx.x, 1, hb, a.ntok, a.reverse);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int h0 = 16 * wave;
+  const int h = h0 + n;
+  const bool hv = h < a.G;
+
+  // Delta of head h: lane (g, n) sums columns 128g .. 128g + 127 of dO ∘ O,
+  // the four lanes of head n then add up (功能说明 stage 2)
+  float dsum = 0.f;
+  if (hv) {
+    const uint16_t* orow = a.o + (t * a.G + h) * 512 + 128 * g;
+    const uint16_t* drow = a.dO + (t * a.G + h) * 512 + 128 * g;
+#pragma unroll 4
+    for (int c = 0; c < 16; ++c) {
+      const uint4 ov = *(const uint4*)(orow + 8 * c);
+      const uint4 dv = *(const uint4*)(drow + 8 * c);
+      const uint16_t* po = (const uint16_t*)&ov;
+      const uint16_t* pd = (const uint16_t*)&dv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsum = fmaf(TT::to_f(pd[j]), TT::to_f(po[j]), dsum);
+    }
+  }
+  dsum += __shfl_xor(dsum, 16);
+  dsum += __shfl_xor(dsum, 32);
+  // A operands: Q|Qrope and dO of head h, columns 32ks + 8g .. +8
+  V8 Qf[KS_QK], dOf[KS_V];
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hv) {
+      if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
+      else v = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
+    }
+    Qf[ks] = as_vec8<V8>(v);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS_V; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hv) v = *(const uint4*)(a.dO + (t * a.G + h) * 512 + 32 * ks + 8 * g);
+    dOf[ks] = as_vec8<V8>(v);
+  }
+  // output heads of this lane: h0 + 4g + i
+  float mb[4], dl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = h0 + 4 * g + i;
+    mb[i] = __builtin_inff();
+    dl[i] = __shfl(dsum, 4 * g + i);
+    if (hh < a.G) {
+      const float m = a.smax[t * a.G + hh], l = a.ssum[t * a.G + hh];
+      if (l > 0.f) mb[i] = m * kLog2e + __log2f(l);
+    } else {
+      dl[i] = 0.f;
+    }
+  }
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+  int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
+
+  // The gather of a tile as a fixed list of copy instructions per wave: K
+  // (and V) rows wave + 8j, then rope group `wave` (waves 0..3, 8 rows each).
+  constexpr int kPerRow = VK ? 1 : 2;
+  constexpr int kRowOps = kPerRow * (kTile / 8);
+  constexpr int kOps = kRowOps + (DR > 0 ? 1 : 0);
+  auto issue_op = [&](int i, int32_t keyv, uint32_t base) {
+    if (i < kRowOps) {
+      const int r = wave + 8 * (i / kPerRow);
+      const int64_t key = __builtin_amdgcn_readlane(keyv, r);
+      const int gc = lane ^ (r & 15);
+      if (!VK && (i & 1)) lds_load16_at(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+      else lds_load16_at(a.k + key * 512 + gc * 8, base + r * 1024);
+    } else if (wave < kTile / 8) {
+      const int r = wave * 8 + (lane >> 3);
+      const int64_t key = __shfl(keyv, r);
+      const int gc = (lane & 7) ^ ((r >> 1) & 7);
+      lds_load16_at(a.kr + key * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
+    }
+  };
+  // staged rows stored by this wave: tensor wave / 4, rows
+  // 8 (wave % 4) + 4 q + lane / 16 (q = 0, 1), chunk lane % 16
+  int stg_c0 = -1;
+  const int srow0 = 8 * (wave & 3) + (lane >> 4), sj = lane & 15, sten = wave >> 2;
+  auto stage_out = [&]() {
+    const uint4 v0 = *(const uint4*)(stg + (sten * kTile + srow0) * 256 + ((sj ^ (srow0 & 15)) << 4));
+    const uint4 v1 = *(const uint4*)(stg + (sten * kTile + srow0 + 4) * 256 + ((sj ^ ((srow0 + 4) & 15)) << 4));
+    uint16_t* out = (sten ? a.ds_out : a.p_out) + (tl * a.E + stg_c0 + srow0) * a.Gp + sj * 8;
+    if (stg_c0 + srow0 < nv) *(uint4*)out = v0;
+    if (stg_c0 + srow0 + 4 < nv) *(uint4*)(out + 4 * a.Gp) = v1;
+  };
+  // LDS offsets of this lane's B-operand reads: row 16 nb + n, chunk
+  // 4 ks + g (K|V rows, swizzle r & 15) or 4 ks' + g (rope rows, (r >> 1) & 7)
+  auto kofs = [&](int nb, int ks) -> int {
+    const int r = 16 * nb + n;
+    return r * 1024 + (((4 * ks + g) ^ (r & 15)) << 4);
+  };
+  auto rofs = [&](int nb, int ks) -> int {
+    const int r = 16 * nb + n;
+    return r * (DR * 2) + (((4 * ks + g) ^ ((r >> 1) & 7)) << 4);
+  };
+
+  auto tile = [&](int c0, const unsigned char* Km, unsigned char* nxt) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // the previous tile's P and dS rows: read back and stored at once, so
+    // that they hold no registers through the MFMA loop
+    if (stg_c0 >= 0) stage_out();
+    const bool more = c0 + kTile < nv;
+    const uint32_t nxt_l = lds_off(nxt);
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Vm = VK ? Km : Kr + KR_BYTES;
+    f32x4 S[2], P[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) S[nb] = P[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // operand reads one k-step ahead with value = key; with separate V rows
+    // (twice the operand registers) in the k-step itself, the other wave of
+    // the SIMD covering their latency
+    constexpr int LA = VK ? 1 : 0;
+    uint4 kv[LA + 1][2], vv[LA + 1][2];
+    auto rd = [&](int ks, int slot) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        kv[slot][nb] = *(const uint4*)(Km + kofs(nb, ks));
+        vv[slot][nb] = VK ? kv[slot][nb] : *(const uint4*)(Vm + kofs(nb, ks));
+      }
+    };
+    if (LA) rd(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS_V; ++ks) {
+      if (!LA) rd(ks, 0);
+      else if (ks + 1 < KS_V) rd(ks + 1, (ks + 1) & LA);
+      // the next tile's copies over the first 8 k-steps
+      if (more && ks < 8)
+#pragma unroll
+        for (int i = ks * kOps / 8; i < (ks + 1) * kOps / 8; ++i) issue_op(i, keys, nxt_l);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        S[nb] = TT::mfma(Qf[ks], as_vec8<V8>(kv[ks & LA][nb]), S[nb]);
+        P[nb] = TT::mfma(dOf[ks], as_vec8<V8>(vv[ks & LA][nb]), P[nb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
+    if constexpr (DR > 0) {
+      uint4 bv[KS_QK - KS_V][2];
+#pragma unroll
+      for (int ks = 0; ks < KS_QK - KS_V; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) bv[ks][nb] = *(const uint4*)(Kr + rofs(nb, ks));
+#pragma unroll
+      for (int ks = 0; ks < KS_QK - KS_V; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) S[nb] = TT::mfma(Qf[KS_V + ks], as_vec8<V8>(bv[ks][nb]), S[nb]);
+    }
+    // P and dS of positions c0 + 16 nb + n, heads h0 + 4g .. +3
+    uint2 wp[2], wd[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const bool valid = c0 + 16 * nb + n < nv;
+      float pv[4], dv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(S[nb][i] * a.scale_log2 - mb[i]);
+        p = valid ? p : 0.f;
+        pv[i] = p;
+        dv[i] = p * (P[nb][i] - dl[i]) * a.ds_scale;
+      }
+      wp[nb] = make_uint2(pack2<TT>(pv[0], pv[1]), pack2<TT>(pv[2], pv[3]));
+      wd[nb] = make_uint2(pack2<TT>(dv[0], dv[1]), pack2<TT>(dv[2], dv[3]));
+    }
+    bar();   // every wave has read the previous staged tile back
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = 16 * nb + n;
+      const int o = r * 256 + (((2 * wave + (g >> 1)) ^ (r & 15)) << 4) + ((g & 1) << 3);
+      *(uint2*)(stg + o) = wp[nb];
+      *(uint2*)(stg + kTile * 256 + o) = wd[nb];
+    }
+    stg_c0 = c0;
+  };
+
+  if (nv > 0) {
+    const uint32_t b0 = lds_off(buf0);
+#pragma unroll
+    for (int i = 0; i < kOps; ++i) issue_op(i, keys, b0);
+  }
+  keys = tile_keys(rt, nv, kTile, lane);
+  for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
+    tile(c0, buf0, buf1);
+    if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+  }
+  __syncthreads();
+  if (stg_c0 >= 0) stage_out();
+}
+
+// ---------------------------------------------------------------------------
 // k_dq: 512 threads; head block of 128 heads; wave w takes heads
 // 64 (w / 4) .. +64 of the block and the 16-column blocks w % 4, w % 4 + 4,
 // ... of dQ|dQrope (blocks 32..35 are the rope columns).
@@ -575,6 +799,20 @@ void launch_sdp(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a_in.ntok + per - 1) / per * per;
   RowArgs a = a_in;
+  // 128 heads: k_sdp8 (8 waves of 16 heads)
+  if (a.Gp == 128) {
+    a.n_hb = 1;
+    const bool vk8 = a.v == a.k;
+    auto go8 = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)padded), dim3(512), 0, s, a); };
+    if (dtype == SFAG_BF16) {
+      if (rope) vk8 ? go8(k_sdp8<BF16, 64, true>) : go8(k_sdp8<BF16, 64, false>);
+      else vk8 ? go8(k_sdp8<BF16, 0, true>) : go8(k_sdp8<BF16, 0, false>);
+    } else {
+      if (rope) vk8 ? go8(k_sdp8<FP16, 64, true>) : go8(k_sdp8<FP16, 64, false>);
+      else vk8 ? go8(k_sdp8<FP16, 0, true>) : go8(k_sdp8<FP16, 0, false>);
+    }
+    return;
+  }
   // k_sdp: up to 128 heads per block, 32 per wave
   const int nw = (int)std::min<int64_t>(4, a.Gp / 32);
   a.n_hb = (int32_t)((a.Gp + 32 * nw - 1) / (32 * nw));

@@ -113,7 +113,7 @@ def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
 # Kernel groups of the timing API and the kernels (by demangled name) each
 # one stands for.
 _GROUPS = {
-    "sdp": r"k_sdp<", "dq": r"k_dq<", "row": r"k_row(16)?<", "keyblock": r"k_keyblock<",
+    "sdp": r"k_sdp8?<", "dq": r"k_dq<", "row": r"k_row(16)?<", "keyblock": r"k_keyblock<",
     "col": r"k_col<", "fwd": r"k_fwd<", "kb_reduce": r"k_kb_reduce", "cast": r"k_cast<", "decode": r"k_decode",
     "delta": r"k_delta<",
 }
@@ -244,12 +244,29 @@ def _summarize_profiles(d, config, calib_mb):
         # runs as several dispatches of one kernel, so their counts add up)
         want = calib_mb * 1048576.0
 
-        def before_lib(disp, pat):
-            first = min((i for i, (k, _c) in disp.items() if "sfag" in k), default=None)
-            return [c for i, (k, c) in disp.items() if pat in k and (first is None or i < first)]
-        cp_r = sum(rd_bytes(c) for c in before_lib(rd_all, "CUDAFunctorOnSelf_add<"))
-        cp_w = sum(wr_bytes(c) for c in before_lib(wr_all, "CUDAFunctorOnSelf_add<"))
-        sm_r = sum(rd_bytes(c) for c in before_lib(rd_all, "reduce_kernel"))
+        # the calibration runs first: its copy is every add dispatch before
+        # the first reduction, its sum every reduction from there up to the
+        # next add or library dispatch (the input generator's own adds and
+        # reductions come later)
+        def calib(disp):
+            ids = sorted(disp)
+            red = [i for i in ids if "reduce_kernel" in disp[i][0]]
+            if not red:
+                return [], []
+            copy = [disp[i][1] for i in ids if i < red[0] and "CUDAFunctorOnSelf_add<" in disp[i][0]]
+            run = []
+            for i in ids[ids.index(red[0]):]:
+                k = disp[i][0]
+                if "CUDAFunctorOnSelf_add<" in k or "sfag" in k:
+                    break
+                if "reduce_kernel" in k:
+                    run.append(disp[i][1])
+            return copy, run
+        cr, sr_ = calib(rd_all)
+        cw, _ = calib(wr_all)
+        cp_r = sum(rd_bytes(c) for c in cr)
+        cp_w = sum(wr_bytes(c) for c in cw)
+        sm_r = sum(rd_bytes(c) for c in sr_)
         cal = dict(bytes=want, copy_read=cp_r, copy_write=cp_w, sum_read=sm_r)
         if cp_r and cp_w:
             rf, wf = want / cp_r, want / cp_w

@@ -61,10 +61,16 @@ def _run(case, seed, value_is_key=False):
     assert np.all(np.isneginf(gm[empty])) and np.all(gl[empty] == 0) and np.all(go[empty] == 0)
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gm[live])) and np.all(np.isfinite(gl))
     err = rel_l2(go, O)
-    print(case.name, f"out rel-L2 {err:.2e}", flush=True)
+    dm = np.max(np.abs(gm[live] - M[live]) / (1.0 + np.abs(M[live]))) if live.any() else 0.0
+    dl = np.max(np.abs(gl[live] - L[live]) / L[live]) if live.any() else 0.0
+    print(case.name, f"out rel-L2 {err:.2e}, max dev {dm:.2e}, sum rel dev {dl:.2e}", flush=True)
+    # out is rounded to 16 bits (relative step 2^-8 for bf16, so a rel-L2 of
+    # ~1e-3 from rounding alone); max and sum are fp32 results of fp32 dot
+    # products over at most 576 bf16 terms and sums of at most K*block fp32
+    # exponentials, whose rounding stays near 1e-6 relative
     assert err <= 5e-3, err
     np.testing.assert_allclose(gm[live], M[live], rtol=1e-4, atol=1e-4)
-    np.testing.assert_allclose(gl[live], L[live], rtol=1e-3, atol=0)
+    np.testing.assert_allclose(gl[live], L[live], rtol=1e-4, atol=0)
     return go, gm, gl
 
 
@@ -114,6 +120,12 @@ def test_forward_then_backward_matches_oracle_pair():
     torch.cuda.synchronize()
     T1, T2, G = case.T1, case.T2, case.G
     f = lambda x, shape: x.float().cpu().numpy().astype(np.float64).reshape(shape)
-    assert rel_l2(f(dq, (T1, G, case.D)), ref["dq"]) <= 1e-2
-    assert rel_l2(f(dk, (T2, case.D)), ref["dk"]) <= 2e-2
-    assert rel_l2(f(dv, (T2, case.D)), ref["dv"]) <= 2e-2
+    # the backward's own tolerances: the library's fp32 statistics and its
+    # bf16-rounded out differ from the oracle's by far less than the 16-bit
+    # rounding of dS and the gradients that those tolerances already absorb
+    errs = dict(dq=rel_l2(f(dq, (T1, G, case.D)), ref["dq"]), dk=rel_l2(f(dk, (T2, case.D)), ref["dk"]),
+                dv=rel_l2(f(dv, (T2, case.D)), ref["dv"]), dqr=rel_l2(f(dqr, (T1, G, case.Dr)), ref["dqr"]),
+                dkr=rel_l2(f(dkr, (T2, case.Dr)), ref["dkr"]))
+    print("forward-fed backward", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, tol in dict(dq=5e-3, dqr=5e-3, dk=1e-2, dv=1e-2, dkr=1e-2).items():
+        assert errs[n] <= tol, (n, errs[n])

@@ -50,6 +50,11 @@ __device__ __forceinline__ V as_vec8(uint4 u) { return __builtin_bit_cast(V, u);
 template <typename V>
 __device__ __forceinline__ V zero_vec8() { return __builtin_bit_cast(V, make_uint4(0, 0, 0, 0)); }
 
+// Index of the calling wave in its workgroup as a wave-uniform value: through
+// readfirstlane the compiler keeps it, and what is derived from it, in scalar
+// registers and branches on it with scalar instructions.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane L supplies the address of 4 consecutive 16-bit elements; calling
 // that 16x4 block M[L][e], lane j of the group receives M[4i + j/4][j%4] for

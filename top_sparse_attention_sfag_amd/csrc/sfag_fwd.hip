@@ -37,10 +37,13 @@ constexpr int kRun = 16;    // consecutive tokens per XCD run
 // without alias information it then waits for every outstanding copy before
 // the next LDS read, so the next tile's gather would not overlap the current
 // tile's MFMAs.  Reads of copied data follow the explicit s_waitcnt and the
-// barrier at the top of each tile.
+// barrier at the top of each tile.  The copy starts with one wait state
+// (s_nop 0): on this chip family an LDS DMA that reads M0 right after a scalar
+// write of M0 needs one, and the compiler inserts it only for DMA
+// instructions it emits itself.
 __device__ __forceinline__ void lds_load16(const void* g, void* l) {
   const uint32_t la = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
 }
 
 }  // namespace
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(256, 1) k_fwd(FwdArgs a) {
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int h0 = hb * 64 + wave * 16;
   const bool wave_on = h0 < a.Gp;
   const int h = h0 + n;

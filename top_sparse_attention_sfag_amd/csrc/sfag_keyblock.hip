@@ -15,15 +15,18 @@
 // operand's column-of-heads fragments come out of LDS through the transposing
 // read ds_read_b64_tr_b16, so no transposed copy of the token side is made.
 //
-// A visit runs in four stages, one per 32-head step.  Both operands of a
-// stage reach LDS through global_load_lds, three stages ahead of their use
-// (four stage buffers), so the only waits on memory are explicit ones on
-// copies issued about three stages earlier.  The key-row slot map of a visit
-// (which rows its token selects, how often, and which pair supplies each
-// row) is built two visits ahead with LDS atomics from the visit's pairs,
-// which are themselves copied into LDS a visit ahead.  A key listed k times
-// by one token has k identical dS/P rows (same token, same key), so each
-// stage of that visit runs k rounds over the row.
+// A visit runs in stages, one per 32-head step (four at 128 heads).  Both
+// operands of a stage reach LDS through global_load_lds, about three stages
+// ahead of their use (four stage buffers), so the only waits on memory are
+// explicit ones on copies issued about three stages earlier.  At 128 heads
+// each stage's barrier sits between its two row groups, so that the reads of
+// the next stage's operands overlap MFMAs, and a visit's copy sources are
+// formed once per visit.  The key-row slot map of a visit (which rows its
+// token selects, how often, and which pair supplies each row) is built two
+// visits ahead with LDS atomics from the visit's pairs, which are themselves
+// copied into LDS ahead of that.  A key listed k times by one token has k
+// identical dS/P rows (same token, same key), so each stage of that visit
+// runs k rounds over the row.
 //
 // C stays in registers (8 waves, two per SIMD, each with a 128-key half of
 // the rows and a quarter of the columns) for the whole token range and is
@@ -51,6 +54,9 @@ constexpr int kXcds = 8;                   // XCDs of the chip (workgroup b runs
 // on purpose: the compiler then does not track them, so it inserts no waits
 // of its own for them before unrelated LDS reads; every read of copied data
 // is preceded by an explicit wait on the copy (wait_vm) and a barrier.
+// Each copy starts with one wait state (s_nop 0): on this chip family an LDS
+// DMA that reads M0 right after a scalar write of M0 needs one, and the
+// compiler inserts it only for DMA instructions it emits itself.
 __device__ __forceinline__ uint32_t lds_addr(const void* l) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
 }
@@ -62,7 +68,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* l) {
 // the LDS slot it writes receives zeros: rows that are never used cost no
 // memory traffic.
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t l) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(l) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(l) : "memory");
 }
 constexpr uint32_t kOutside = 0x80000000u;   // offset past any resource size used here
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -73,10 +79,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t l) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(l) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(l) : "memory");
 }
 __device__ __forceinline__ void dma16(const void* g, uint32_t l) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(l) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(l) : "memory");
 }
 
 // 16 zero bytes: the source of B-stage slots of heads past N1.
@@ -132,21 +138,16 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// The same for a wave-uniform count (the values the key-block pipeline
-// uses; any other waits for everything, which is never too early).
-__device__ __forceinline__ void wait_copies(int n) {
-  switch (n) {
-    case 2: wait_vm<2>(); break;
-    case 3: wait_vm<3>(); break;
-    case 4: wait_vm<4>(); break;
-    case 5: wait_vm<5>(); break;
-    case 6: wait_vm<6>(); break;
-    case 7: wait_vm<7>(); break;
-    case 8: wait_vm<8>(); break;
-    case 14: wait_vm<14>(); break;
-    case 16: wait_vm<16>(); break;
-    default: wait_vm<0>(); break;
-  }
+// Wait until at most M stages' copies of this wave are outstanding: KA A
+// copies and KB B copies per stage, where the NBI B-copy instructions of a
+// stage go to waves w, w + W, ..., so KB is ceil(NBI / W) for waves below
+// NBI % W (all of them when W divides NBI) and floor(NBI / W) for the rest.
+// (The count has to be an immediate, hence the two forms.)
+template <int M, int KA, int NBI, int W>
+__device__ __forceinline__ void wait_stages(int wave) {
+  constexpr int KH = KA + (NBI + W - 1) / W, KL = KA + NBI / W;
+  if (NBI % W == 0 || wave < NBI % W) wait_vm<M * KH>();
+  else wait_vm<M * KL>();
 }
 
 struct KbShared {
@@ -165,8 +166,8 @@ struct KbShared {
 // MFMAs.  GP is the padded head count when it is 128 (all strides
 // compile-time), else 0 (taken from the args).
 template <typename TT, int NB, int GP, int W>
-__device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int tr, int kb, int64_t vlo,
-                                         int64_t vhi, unsigned char* __restrict__ st0,
+__device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int tr, int kb, int vlo,
+                                         int vhi, unsigned char* __restrict__ st0,
                                          unsigned char* __restrict__ st1, unsigned char* __restrict__ st2,
                                          unsigned char* __restrict__ st3, KbShared* __restrict__ shp,
                                          int32_t* __restrict__ e_pair, int32_t* __restrict__ e_row) {
@@ -174,12 +175,12 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // buffer from the reads of another, so that those reads need no wait)
   KbShared& sh = *shp;
   typedef typename TT::vec8 V8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, n = lane & 15;
   const int Gp = GP ? GP : (int)a.Gp, nks = (Gp + 31) >> 5;
   const uint16_t* Bmain = c.src == 0 ? a.q : a.dO;
   const uint16_t* Asrc = c.src == 0 ? a.ds : a.p;
-  const int64_t kbase = (int64_t)kb * a.ntok;
+  const int kbase = kb * (int)a.ntok;   // composite keys are int32 by construction
   constexpr int NT = 64 * W;        // threads
   constexpr int RB = 64 / W;        // MFMA row blocks per wave
   constexpr int KA = 16 / W;        // A copy instructions per wave and stage
@@ -188,22 +189,21 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   constexpr int NBI = GP == 16 ? 2 * NB : 4 * NB;
   constexpr int KBM = (NBI + W - 1) / W;
   const int KB = (NBI - wave + W - 1) / W;      // B copy instructions of this wave and stage
-  const int K = KA + KB;                        // copy instructions per wave and stage
   const int mb0 = (wave >> 2) * RB;             // first row block of the wave
   const int cq = wave & 3;                      // column quarter of the wave
 
   // ---- visit metadata, staged in LDS for a window of visits from wb ------
-  int64_t wb = vlo;
+  int wb = vlo;
   auto load_window = [&]() {
     for (int j = tid; j < kWin + 3; j += NT) {
-      const int64_t x = wb + j;
+      const int x = wb + j;
       sh.vstart[j] = x <= vhi ? a.vis_start[x] : 0;
       if (j < kWin + 2) sh.vkey[j] = x < vhi ? a.vis_key[x] : 0;
     }
   };
-  auto v_start = [&](int64_t v) -> int64_t { return (int64_t)sh.vstart[v - wb]; };
-  auto v_count = [&](int64_t v) -> int { return sh.vstart[v + 1 - wb] - sh.vstart[v - wb]; };
-  auto v_token = [&](int64_t v) -> int64_t { return (int64_t)sh.vkey[v - wb] - kbase; };
+  auto v_start = [&](int v) -> int { return sh.vstart[v - wb]; };
+  auto v_count = [&](int v) -> int { return sh.vstart[v + 1 - wb] - sh.vstart[v - wb]; };
+  auto v_token = [&](int v) -> int { return sh.vkey[v - wb] - kbase; };
 
   f32x4 C[RB][NB];
 #pragma unroll
@@ -227,25 +227,25 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // map of visit v from its pairs: the first kEnt from the LDS copy, the
   // rest (only with duplicated keys) straight from memory
   // (eh: which of the two entry buffers holds the visit's pairs)
-  auto build = [&](int b, int64_t v, int eh) {
+  auto build = [&](int b, int v, int eh) {
     const int cnt = v_count(v);
     if (tid < cnt && tid < kEnt) add_entry(b, e_pair[eh * kEnt + tid], e_row[eh * kEnt + tid]);
-    const int64_t s0 = v_start(v);
+    const int s0 = v_start(v);
     for (int j = tid + kEnt; j < cnt; j += NT) add_entry(b, a.svals[s0 + j], a.er[s0 + j]);
   };
   const uint32_t l_pair = lds_addr(e_pair), l_row = lds_addr(e_row);
   // copy of visit v's first kEnt pairs (ids and key rows) into LDS: 8
   // dword-copy instructions, 8 / W per wave; lanes past the visit re-read
   // its first pair
-  auto issue_entries = [&](int64_t v, int eh) {
-    const int64_t s0 = v_start(v);
+  auto issue_entries = [&](int v, int eh) {
+    const int s0 = v_start(v);
     const int cnt = v_count(v);
 #pragma unroll
     for (int k = 0; k < 8 / W; ++k) {
       const int ins = wave * (8 / W) + k;    // 0..3 pair ids, 4..7 key rows
       const int part = ins & 3;
       const int e = part * 64 + lane;
-      const int64_t src = s0 + (e < cnt ? e : 0);
+      const int src = s0 + (e < cnt ? e : 0);
       if (ins < 4) dma4(a.svals + src, l_pair + eh * kEnt * 4 + part * 256);
       else dma4(a.er + src, l_row + eh * kEnt * 4 + part * 256);
     }
@@ -295,7 +295,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     uint32_t st;
     bool on;
   };
-  auto b_rows = [&](StageCopy& sc, int64_t tl, int ks) {
+  auto b_rows = [&](StageCopy& sc, int tl, int ks) {
     const int64_t hrow = (a.t0 + tl) * a.G + 32 * ks;
     sc.bm = Bmain + hrow * 512;
     sc.br = a.qr + hrow * Dr;
@@ -305,17 +305,27 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     if (32 * sc.ks + (int)((x >> 16) & 31) >= G) return (const void*)(((uint64_t)z_hi << 32) | z_lo);
     return ((x >> 21) ? sc.br : sc.bm) + (x & 0x7fff);
   };
-  auto prep_stage = [&](StageCopy& sc, bool on, int b, int64_t tl, int ks, uint32_t st) {
+  // the slot-map entries (staged pair of each key row) of this lane's A copies
+  auto prim_of = [&](int b, int32_t (&pr)[KA]) {
+#pragma unroll
+    for (int k = 0; k < KA; ++k) pr[k] = sh.prim[b][16 * (wave + W * k) + (lane >> 2)];
+  };
+  auto prep_with = [&](StageCopy& sc, bool on, const int32_t (&pr)[KA], int tl, int ks, uint32_t st) {
     sc.on = on;
     if (!on) return;
     // A rows of token tl: pairs tl*E .. tl*E + E - 1
-    sc.ars = make_rsrc(Asrc + tl * a.E * Gp, (int)(a.E * Gp * 2));
+    sc.ars = make_rsrc(Asrc + (int64_t)tl * a.E * Gp, (int)(a.E * Gp * 2));
     b_rows(sc, tl, ks);
-    sc.p0 = (int32_t)(tl * a.E);
+    sc.p0 = tl * (int)a.E;
     sc.ks = ks;
     sc.st = st;
 #pragma unroll
-    for (int k = 0; k < KA; ++k) sc.pr[k] = sh.prim[b][16 * (wave + W * k) + (lane >> 2)];
+    for (int k = 0; k < KA; ++k) sc.pr[k] = pr[k];
+  };
+  auto prep_stage = [&](StageCopy& sc, bool on, int b, int tl, int ks, uint32_t st) {
+    int32_t pr[KA];
+    if (on) prim_of(b, pr);
+    prep_with(sc, on, pr, tl, ks, st);
   };
   auto issue_a = [&](const StageCopy& sc, int k) {
     const int i = wave + W * k;
@@ -346,7 +356,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   // All copies of a stage at once, at the top of the stage: the generic path
   // (Gp != 128) waits for every copy at each stage, so spreading its copies
   // over the MFMAs would leave the last ones no time before that wait.
-  auto issue_stage = [&](int b, int64_t tl, int ks, uint32_t st) {
+  auto issue_stage = [&](int b, int tl, int ks, uint32_t st) {
     StageCopy sc;
     prep_stage(sc, true, b, tl, ks, st);
     issue_all(sc);
@@ -461,14 +471,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     }
   };
 
-  const int64_t nst = 4 * (vhi - vlo);   // stages
-  // before stage s: wait for its copies; everything issued after them is the
-  // copies of the (up to) two following stages and pair copies
-  auto wait_stage = [&](int64_t s) {
-    const int later = (s + 1 < nst ? 1 : 0) + (s + 2 < nst ? 1 : 0);
-    if (GP != 128) wait_vm<0>();
-    else wait_copies(later * K);
-  };
+  const int nst = 4 * (vhi - vlo);   // stages (four 32-head stages per visit)
   auto stage_buf = [&](int ks) -> unsigned char* { return ks == 0 ? st0 : ks == 1 ? st1 : ks == 2 ? st2 : st3; };
   const uint32_t L0 = lds_addr(st0), L1 = lds_addr(st1), L2 = lds_addr(st2), L3 = lds_addr(st3);
   auto stage_lds = [&](int ks) -> uint32_t { return ks == 0 ? L0 : ks == 1 ? L1 : ks == 2 ? L2 : L3; };
@@ -478,31 +481,235 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   load_window();
   __syncthreads();
   for (int x = 0; x < 2; ++x) {
-    const int64_t v = vlo + x;
+    const int v = vlo + x;
     if (v < vhi) {
-      const int64_t s0 = v_start(v);
+      const int s0 = v_start(v);
       const int cnt = v_count(v);
       for (int j = tid; j < cnt; j += NT) add_entry(x, a.svals[s0 + j], a.er[s0 + j]);
     }
   }
   __syncthreads();
 
-  if (GP != 128 && nks == 1) {
+  if constexpr (GP == 128) {
+    // 128 heads: four 32-head stages per visit, numbered x = 4 w + ks over
+    // the visits w = v - vlo of the range; stage x uses buffer ks.  Each
+    // stage's barrier sits between its two row groups: a wave computes row
+    // group 0 of stage x, waits for the copies of stage x + 1 and meets the
+    // others, and then reads the operands of stage x + 1 while the MFMAs of
+    // row group 1 run: row group 0 of A at once, and B one column block at a
+    // time, each into the registers of the column block whose row-group-1
+    // MFMAs were just issued.  Stage x + 4 is copied into buffer ks (which
+    // every wave has finished reading at the barrier) between those MFMAs.
+    // So the operand reads that follow a barrier overlap MFMAs, and copies
+    // are issued three and a half stages before their use.  Bookkeeping
+    // after the barrier of stage 4 w + ks: ks = 0: the map slot of visit
+    // w + 2 (last used by visit w - 1) is cleared and the pairs of visit
+    // w + 2 are copied; ks = 2: its map is built (those copies are older
+    // than the copies this barrier waited for); ks = 3: the round count of
+    // visit w + 1 is read.
+    typedef typename TT::vec8 V8b;
+    const int po = (g ^ swz(n)) << 4;   // A row chunk of this lane (rows 16 mb + n)
+    const int r0 = 8 * g + (n >> 2);    // B head rows r0 and r0 + 4
+    // (operand reads address a stage through an LDS pointer made opaque per
+    // stage, so that the per-lane offsets are shared by the four buffers
+    // instead of being kept, precomputed, once per buffer)
+    typedef __attribute__((address_space(3))) const unsigned char* lds_p;
+    auto lds_base = [&](const unsigned char* st) -> lds_p {
+      lds_p b = (lds_p)st;
+      asm volatile("" : "+v"(b));
+      return b;
+    };
+    auto rdA = [&](lds_p st, int h, uint4 (&dst)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 x = *(__attribute__((address_space(3))) const u32x4*)(st + ((mb0 + 4 * h + j) * 16 + n) * 64 + po);
+        dst[j] = __builtin_bit_cast(uint4, x);
+      }
+    };
+    auto rdB1 = [&](lds_p st, int nb) -> V8b {
+      lds_p bs = st + kStageA;
+      return join_tr<V8b>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(bs + boff(r0, nb))),
+                          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(bs + boff(r0 + 4, nb))));
+    };
+    auto rdB = [&](lds_p st, V8b (&dst)[NB]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) dst[nb] = rdB1(st, nb);
+    };
+    // MFMAs of row group h with column block nb
+    auto mma = [&](const uint4 (&av)[4], const V8b& B, int h, int nb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) C[4 * h + j][nb] = TT::mfma(as_vec8<V8b>(av[j]), B, C[4 * h + j][nb]);
+    };
+    // Copy sources of one visit, made once per visit and offset per stage:
+    // stage ks of the visit reads A at byte offset aoff[k] + 64 ks (rows not
+    // selected keep an offset outside the resource for every ks) and B from
+    // the token's head rows 32 ks .. 32 ks + 31 in Q|dO (bm) or Qrope (br).
+    struct VisitCopy {
+      __amdgpu_buffer_rsrc_t ars;
+      const unsigned char *bm, *br;
+      uint32_t aoff[KA];
+      bool on;
+    };
+    const uint32_t aq0 = (uint32_t)((((lane & 3) ^ swz(16 * wave + (lane >> 2))) * 8) * 2);
+    auto make_copy = [&](VisitCopy& vc, bool on, int tl, const int32_t (&pr)[KA]) {
+      vc.on = on;
+      if (!on) return;
+      vc.ars = make_rsrc(Asrc + (int64_t)tl * a.E * 128, (int)(a.E * 128 * 2));
+      const int p0 = tl * (int)a.E;
+#pragma unroll
+      for (int k = 0; k < KA; ++k) {
+        // row 16 (wave + W k) + lane / 4: its swizzle equals that of row
+        // 16 wave + lane / 4 (16 W k is a multiple of 8)
+        vc.aoff[k] = pr[k] >= 0 ? (uint32_t)((pr[k] - p0) * 256) + aq0 : kOutside;
+      }
+      const int64_t hrow = (a.t0 + tl) * a.G;
+      vc.bm = (const unsigned char*)(Bmain + hrow * 512);
+      vc.br = (const unsigned char*)(a.qr + hrow * Dr);
+    };
+    const void* zero16 = (const void*)(((uint64_t)z_hi << 32) | z_lo);
+    // copy part k (A instruction k and B instruction k) of stage ks (the
+    // stage's offsets enter as opaque scalars, so that no per-stage copy of a
+    // lane's addresses is kept; the offset field of an LDS-bound buffer load
+    // would move the LDS destination as well)
+    auto issue_copy = [&](const VisitCopy& vc, int ks, int k) {
+      if (!vc.on) return;
+      const uint32_t st = stage_lds(ks);
+      if (k < KA) {
+        uint32_t ko = 64u * ks;
+        asm volatile("" : "+s"(ko));
+        bdma16(vc.ars, vc.aoff[k] + ko, st + (wave + W * k) * 1024);
+      }
+      if (k < KBM && k < KB) {
+        const uint32_t x = b_chunk[k];
+        const unsigned char* bm = vc.bm + ks * (32 * 512 * 2);
+        const unsigned char* br = vc.br + ks * (32 * 2 * Dr);
+        asm volatile("" : "+s"(bm), "+s"(br));
+        const bool live = 32 * ks + (int)((x >> 16) & 31) < G;
+        const void* src = live ? (const void*)((((x >> 21) & 1) ? br : bm) + 2 * (x & 0x7fff)) : zero16;
+        dma16(src, st + kStageA + (wave + W * k) * 1024);
+      }
+    };
+    const int nw = vhi - vlo;
+    // prologue: the four stages of the first visit (map slot 0)
+    {
+      int32_t p0r[KA];
+      prim_of(0, p0r);
+      VisitCopy vc;
+      make_copy(vc, true, v_token(vlo), p0r);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        issue_copy(vc, ks, 0);
+        issue_copy(vc, ks, 1);
+      }
+    }
+    // stage 0's copies were issued first: 3 later stages' copies may be
+    // outstanding
+    wait_stages<3, KA, NBI, W>(wave);
+    bar();
+    V8b Bc[NB];
+    uint4 a0[4], a1[4];
+    rdB(lds_base(st0), Bc);
+    rdA(lds_base(st0), 0, a0);
+    int R = sh.rounds[0];
+    int su = 0;   // map slot of visit w: w % 3
+    for (int w = 0; w < nw; ++w, su = su == 2 ? 0 : su + 1) {
+      const int s1 = su == 2 ? 0 : su + 1, s2 = su == 0 ? 2 : su - 1;   // slots of visits w + 1, w + 2
+      const bool next = w + 1 < nw;
+      // copies of visit w + 1, issued during visit w (its map was built a
+      // visit ago and stays unchanged through visit w)
+      VisitCopy vc;
+      {
+        int32_t pn[KA];
+        prim_of(s1, pn);
+        make_copy(vc, next, next ? v_token(vlo + w + 1) : 0, pn);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        unsigned char* buf = stage_buf(ks);
+        const lds_p lb = lds_base(buf);
+        // earlier rounds of a visit whose token lists some key more than once
+        for (int r = 0; r + 1 < R; ++r) {
+          if (r) {
+            drop_rows(buf, su, r);
+            rdB(lb, Bc);
+            rdA(lb, 0, a0);
+          }
+          rdA(lb, 1, a1);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) mma(a0, Bc[nb], 0, nb);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) mma(a1, Bc[nb], 1, nb);
+        }
+        if (R > 1) {
+          drop_rows(buf, su, R - 1);
+          rdB(lb, Bc);
+          rdA(lb, 0, a0);
+        }
+        // last round, with the barrier between the row groups
+        rdA(lb, 1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mma(a0, Bc[nb], 0, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        // stage x + 1 exists unless this is the range's last stage; the
+        // copies issued after those of stage x + 1 are those of the stages
+        // x + 2 and x + 3 that exist
+        if (next || ks < 3) {
+          if (next || ks == 0) wait_stages<2, KA, NBI, W>(wave);
+          else if (ks == 1) wait_stages<1, KA, NBI, W>(wave);
+          else wait_vm<0>();
+          bar();
+          if (ks == 0) {
+            if (vlo + w + 2 - wb + 1 > kWin) {   // visit w + 2 leaves the window
+              wb = vlo + w;
+              load_window();
+              __syncthreads();
+            }
+            reset(s2);
+            if (w + 2 < nw) issue_entries(vlo + w + 2, w & 1);
+          } else if (ks == 2) {
+            if (w + 2 < nw) build(s2, vlo + w + 2, w & 1);
+          } else if (ks == 3) {
+            R = sh.rounds[s1];
+          }
+        }
+        // The reads of the next stage's operands run on the last stage as
+        // well (of a buffer in LDS, results unused), so that both paths leave
+        // the same reads in flight here and the compiler's waits before the
+        // MFMAs below stay on the operands those MFMAs use.
+        const lds_p nbuf = lds_base(stage_buf((ks + 1) & 3));
+        rdA(nbuf, 0, a0);
+        // row group 1, one column block at a time; B of stage x + 1 replaces
+        // each block's operand once its MFMAs are issued, and the copies of
+        // stage x + 4 (visit w + 1, stage ks: none on the last visit) go out
+        // between the blocks
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          __builtin_amdgcn_sched_barrier(0);
+          mma(a1, Bc[nb], 1, nb);
+          __builtin_amdgcn_sched_barrier(0);
+          Bc[nb] = rdB1(nbuf, nb);
+          if (nb < 2) issue_copy(vc, ks, nb);
+        }
+      }
+    }
+  } else if (nks == 1) {
     // Up to 32 heads (one stage per visit): the four stage buffers rotate over
     // visits and stage copies run two visits ahead.  At the top of visit v
     // the map of visit v + 2 is built (its pairs were copied a visit ago) and
     // its stage is copied between the MFMAs of visit v; the pairs of visit
     // v + 3 are copied at the same time.  Each visit waits once, for copies
     // issued one and two visits earlier.
-    auto rbuf = [&](int64_t v) -> unsigned char* { return stage_buf((int)((v - vlo) & 3)); };
-    auto rlds = [&](int64_t v) -> uint32_t { return stage_lds((int)((v - vlo) & 3)); };
-    auto ehalf = [&](int64_t v) -> int { return (int)((v - vlo) & 1); };
+    auto rbuf = [&](int v) -> unsigned char* { return stage_buf((v - vlo) & 3); };
+    auto rlds = [&](int v) -> uint32_t { return stage_lds((v - vlo) & 3); };
+    auto ehalf = [&](int v) -> int { return (v - vlo) & 1; };
     // issue order: stage(vlo), pairs(vlo + 2), stage(vlo + 1)
     issue_stage(0, v_token(vlo), 0, rlds(vlo));
     if (vlo + 2 < vhi) issue_entries(vlo + 2, ehalf(vlo + 2));
     if (vlo + 1 < vhi) issue_stage(1, v_token(vlo + 1), 0, rlds(vlo + 1));
-    for (int64_t v = vlo; v < vhi; ++v) {
-      const int u = (int)((v - vlo) % 3);
+    for (int v = vlo; v < vhi; ++v) {
+      const int u = (v - vlo) % 3;
       const int u2 = u == 0 ? 2 : u - 1;   // map slot of visit v + 2
       if (v - wb + 3 > kWin) {   // visits v .. v + 3 leave the window
         __syncthreads();
@@ -512,7 +719,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       }
       // stage(v) and pairs(v + 2) have landed once at most stage(v + 1),
       // issued after them, is outstanding
-      if (v + 1 < vhi) wait_copies(K);
+      if (v + 1 < vhi) wait_stages<1, KA, NBI, W>(wave);
       else wait_vm<0>();
       bar();
       const int R = sh.rounds[u];
@@ -529,26 +736,26 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       }
       reset(u);   // this visit's map slot, for visit v + 3
     }
-  } else if (GP != 128 && nks <= 2) {
+  } else if (nks <= 2) {
     // Up to 64 heads (one or two 32-head stages per visit): visits alternate
     // between the buffer pairs st0|st1 and st2|st3; the stages of visit v + 1
     // are copied while visit v is computed (its slot map was built a visit
     // earlier), so each visit waits once, for copies issued a visit ago.
-    auto vbuf = [&](int64_t v, int ks) -> unsigned char* { return stage_buf((int)(((v - vlo) & 1) << 1) + ks); };
-    auto vlds = [&](int64_t v, int ks) -> uint32_t { return stage_lds((int)(((v - vlo) & 1) << 1) + ks); };
-    auto issue_visit = [&](int b, int64_t v) {
-      const int64_t tl = v_token(v);
+    auto vbuf = [&](int v, int ks) -> unsigned char* { return stage_buf((((v - vlo) & 1) << 1) + ks); };
+    auto vlds = [&](int v, int ks) -> uint32_t { return stage_lds((((v - vlo) & 1) << 1) + ks); };
+    auto issue_visit = [&](int b, int v) {
+      const int tl = v_token(v);
       for (int ks = 0; ks < nks; ++ks) issue_stage(b, tl, ks, vlds(v, ks));
     };
     // The pairs of visit v + 3 are copied at the top of visit v (the two
     // entry buffers alternate) and its slot map is built at the end of visit
     // v + 1: the top-of-visit wait covers both kinds of copies, each issued a
     // whole visit earlier.
-    auto ehalf = [&](int64_t v) -> int { return (int)((v - vlo) & 1); };
+    auto ehalf = [&](int v) -> int { return (v - vlo) & 1; };
     if (vlo + 2 < vhi) issue_entries(vlo + 2, ehalf(vlo + 2));
     issue_visit(0, vlo);
-    for (int64_t v = vlo; v < vhi; ++v) {
-      const int u = (int)((v - vlo) % 3);
+    for (int v = vlo; v < vhi; ++v) {
+      const int u = (v - vlo) % 3;
       const int u1 = u == 2 ? 0 : u + 1, u2 = u == 0 ? 2 : u - 1;
       if (v - wb + 3 > kWin) {   // visits v .. v + 3 leave the window
         __syncthreads();
@@ -564,7 +771,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
       // stage ks of visit v + 1 is copied between the MFMAs of stage ks of
       // visit v (a burst of copies stalls the issuing wave)
       const bool nxt = v + 1 < vhi;
-      const int64_t tl1 = nxt ? v_token(v + 1) : 0;
+      const int tl1 = nxt ? v_token(v + 1) : 0;
       for (int ks = 0; ks < nks; ++ks) {
         StageCopy sc;
         prep_stage(sc, nxt, u1, tl1, ks, vlds(v + 1, ks));
@@ -581,7 +788,7 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     }
   } else {
   {
-    const int64_t tl = v_token(vlo);
+    const int tl = v_token(vlo);
     StageCopy sc;
     prep_stage(sc, true, 0, tl, 0, L0);
     issue_all(sc);
@@ -592,32 +799,27 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
   }
 
   // ---- one visit per iteration, four stages ---------------------------------
-  for (int64_t v = vlo; v < vhi; ++v) {
-    const int u = (int)((v - vlo) % 3);
+  int u = 0;   // map slot of visit v: (v - vlo) % 3
+  for (int v = vlo; v < vhi; ++v, u = u == 2 ? 0 : u + 1) {
     const int u1 = u == 2 ? 0 : u + 1, u2 = u == 0 ? 2 : u - 1;
-    const int64_t s = 4 * (v - vlo);
     if (v - wb + 2 > kWin) {   // visits v .. v + 2 leave the window
       __syncthreads();
       wb = v;
       load_window();
       __syncthreads();
     }
-    const int64_t tl = v_token(v);
+    const int tl = v_token(v);
     const bool more = v + 1 < vhi;
-    const int64_t tl1 = more ? v_token(v + 1) : 0;
-    // stage 0
-    wait_stage(s);
+    const int tl1 = more ? v_token(v + 1) : 0;
+    // stage 0 (this path waits for every copy at each stage)
+    wait_vm<0>();
     bar();
     const int R = sh.rounds[u];
     reset(u2);
     if (v + 2 < vhi) issue_entries(v + 2, 0);
     StageCopy sc;
-    if (GP != 128) {
-      sc.on = false;
-      if (nks > 3) issue_stage(u, tl, 3, L3);
-    } else {
-      prep_stage(sc, nks > 3, u, tl, 3, L3);
-    }
+    sc.on = false;
+    if (nks > 3) issue_stage(u, tl, 3, L3);
     for (int r = 0; r < R; ++r) {
       if (r) drop_rows(st0, u, r);
       compute(st0, sc);
@@ -626,17 +828,12 @@ __device__ __forceinline__ void kb_block(const KbArgs& a, const ColBlock c, int 
     // stages 1 .. 3: each issues the copy of the next visit's stage ks - 1
 #pragma unroll
     for (int ks = 1; ks < 4; ++ks) {
-      if (ks < nks || GP != 128) {
-        wait_stage(s + ks);
+      {
+        wait_vm<0>();
         bar();
-        // map of visit v + 2: its pairs were copied during stage 0, before
-        // the copies waited for above
+        // map of visit v + 2: its pairs were copied during stage 0
         if (ks == 3 && v + 2 < vhi) build(u2, v + 2, 0);
-        if (GP != 128) {
-          if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
-        } else {
-          prep_stage(sc, more, u1, tl1, ks - 1, stage_lds(ks - 1));
-        }
+        if (more) issue_stage(u1, tl1, ks - 1, stage_lds(ks - 1));
         if (ks < nks) {
           for (int r = 0; r < R; ++r) {
             if (r) drop_rows(stage_buf(ks), u, r);
@@ -697,8 +894,8 @@ __global__ void __launch_bounds__(512, 1) k_keyblock(KbArgs a) {
   const ColBlock c = a.cbs[cb];
   const int64_t t_lo = (int64_t)tr * a.TR, t_hi = min<int64_t>(t_lo + a.TR, a.ntok);
   const int64_t nvis = *a.n_vis;
-  const int64_t vlo = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_lo));
-  const int64_t vhi = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_hi));
+  const int vlo = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_lo));
+  const int vhi = __builtin_amdgcn_readfirstlane((int)lower_bound_i32(a.vis_key, nvis, (int64_t)kb * a.ntok + t_hi));
   if (threadIdx.x == 0 && cb == 0) a.nonempty[(int64_t)tr * a.nKB + kb] = vhi > vlo ? 1 : 0;
   if (vhi <= vlo) return;
   if constexpr (GPK == 16) {

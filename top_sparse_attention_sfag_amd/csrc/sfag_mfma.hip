@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256, 1) k_col(ColArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * BSTR];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int64_t tl = blockIdx.x;
   const int64_t t = a.t0 + tl;
   const int G = (int)a.G;

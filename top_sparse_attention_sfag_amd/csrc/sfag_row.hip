@@ -40,10 +40,13 @@ constexpr int kRun = 16;           // consecutive tokens per XCD run
 // without alias information it then waits for every outstanding copy before
 // the next LDS read, so the next tile's gather would not overlap the current
 // tile's MFMAs.  Reads of copied data follow the explicit s_waitcnt and the
-// barrier at the top of each tile.
+// barrier at the top of each tile.  The copy starts with one wait state
+// (s_nop 0): on this chip family an LDS DMA that reads M0 right after a scalar
+// write of M0 needs one, and the compiler inserts it only for DMA
+// instructions it emits itself.
 __device__ __forceinline__ void lds_load16(const void* g, void* l) {
   const uint32_t la = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
 }
 
 }  // namespace
@@ -78,7 +81,7 @@ __global__ void __launch_bounds__(256, 1) k_row(RowArgs a) {
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int h0 = hb * 64 + wave * 16;
   const bool wave_on = h0 < a.Gp;
   const int h = h0 + n;
@@ -380,7 +383,7 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
   const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const bool hv = n < a.G;                 // head n
   const bool s_wave = wave < 2, copier = wave < 3;
   const int mb = wave & 1;                 // position half of the Sᵀ / dPᵀ waves

@@ -38,15 +38,17 @@ constexpr int kRun = 16;
 // wave-uniform LDS address l_base + 16 l).  Inline asm on purpose: the
 // compiler does not track it, so it adds no waits of its own before LDS reads
 // of the other buffer; reads of copied data follow an explicit s_waitcnt and
-// a barrier.
+// a barrier.  The copy starts with one wait state (s_nop 0): on this chip
+// family an LDS DMA that reads M0 right after a scalar write of M0 needs one,
+// and the compiler inserts it only for DMA instructions it emits itself.
 __device__ __forceinline__ void lds_load16(const void* g, const void* l) {
   const uint32_t la = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
 }
 
 // Same, with the LDS address given as a 32-bit offset.
 __device__ __forceinline__ void lds_load16_at(const void* g, uint32_t la) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_off(const void* l) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)l);
@@ -160,7 +162,7 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
   const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb, a.ntok, a.reverse);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int hi = lane & 31, kg = lane >> 5;   // row of the A operand, k-group
   const int h0 = hb * HB + wave * 32;
   const int h = h0 + hi;
@@ -456,7 +458,7 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
   const int64_t tl = unit_token(blockIdx.x, 1, hb, a.ntok, a.reverse);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int h0 = 16 * wave;
   const int h = h0 + n;
   const bool hv = h < a.G;
@@ -673,7 +675,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
   const int64_t tl = unit_token(blockIdx.x, a.n_hb, hb, a.ntok, a.reverse);
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int hw = wave >> 2, wq = wave & 3;    // head half, column group
   const int hmax = (int)(a.Gp - hb * 128);    // heads of this block present in the dS rows
   const int nv = a.nvalid[tl];

@@ -213,11 +213,15 @@ def test_deterministic_independent_of_chunking(path):
 
 
 # The key-block contraction at head counts that pad to 128 (the two-waves-per-
-# SIMD kernel, heads past N1 in its last 32-head stage) and to 64.
+# SIMD kernel, heads past N1 in its last 32-head stage) and to 64; the last
+# two cases have more key blocks than twice the positions per token, where the
+# pairs are grouped by the global radix sort instead of per-token counting.
 KEYBLOCK_HEADS = [
     si.Case("kb_g112_causal", S1=48, S2=300, G=112, K=96, mode=3, index_rule="causal_mix"),
     si.Case("kb_g100_fp16_norope", S1=20, S2=280, G=100, Dr=0, K=80, dtype="fp16"),
     si.Case("kb_g40_rope", S1=30, S2=270, G=40, K=70),
+    si.Case("kb_g128_radix_grouping", S1=40, S2=4096, G=128, K=4),
+    si.Case("kb_g16_radix_grouping", S1=24, S2=3000, G=16, K=5),
 ]
 
 

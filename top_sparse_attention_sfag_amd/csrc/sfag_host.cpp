@@ -57,15 +57,23 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter, bool validate) {
   if (d.row_split > 1) carve(c, w.dq_acc, ch * (uint64_t)d.G * (d.D + d.Dr) * 4);
   if (keyblock) {
     const uint64_t n = ch * E;
-    const uint64_t nblk = (n + kSortBlock - 1) / kSortBlock;
-    carve(c, w.sort_keys[0], n * 4);
-    carve(c, w.sort_keys[1], n * 4);
-    carve(c, w.sort_vals[0], n * 4);
-    carve(c, w.sort_vals[1], n * 4);
-    carve(c, w.sort_hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
+    if (kb_use_bins(d)) {
+      // per-token counting: sorted pair ids, their key rows, the grid
+      const uint64_t cells = (uint64_t)d.nKB * ch;
+      carve(c, w.sort_vals[0], n * 4);
+      carve(c, w.kb_grid, 2 * cells * 4);
+      carve(c, w.kb_grid_tmp, ((cells + 4095) / 4096 + 2) * 4);
+    } else {
+      const uint64_t nblk = (n + kSortBlock - 1) / kSortBlock;
+      carve(c, w.sort_keys[0], n * 4);
+      carve(c, w.sort_keys[1], n * 4);
+      carve(c, w.sort_vals[0], n * 4);
+      carve(c, w.sort_vals[1], n * 4);
+      carve(c, w.sort_hist, (256 * nblk + 256 * nblk / 4096 + 2) * 4);
+      carve(c, w.vis_flags, n * 4);
+    }
     carve(c, w.kb_part, (uint64_t)d.nTR * d.T2 * d.AW * 4);
     carve(c, w.kb_nonempty, (uint64_t)d.nTR * d.nKB * 4);
-    carve(c, w.vis_flags, n * 4);
     carve(c, w.vis_start, (n + 1) * 4);
     carve(c, w.vis_key, n * 4);
     carve(c, w.vis_er, n * 4);

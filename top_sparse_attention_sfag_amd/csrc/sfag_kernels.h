@@ -96,6 +96,11 @@ void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows,
                    int32_t nkb, int32_t* flags, int32_t* scan_tmp, int32_t* vis_start, int32_t* vis_key, int32_t* er,
                    int32_t* n_vis, hipStream_t s);
 void launch_scan_i32(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s);
+// Pairs of a chunk grouped by (key block, token) through per-token counting
+// (key blocks up to kMaxBinBlocks); fills svals, er and the visit lists.
+void launch_kb_bins(const int32_t* rows, const int32_t* nvalid, int64_t E, int32_t nkb, int64_t ntok, int32_t* cnt,
+                    int32_t* flg, int32_t* scan_tmp, int32_t* svals, int32_t* er, int32_t* vis_start, int32_t* vis_key,
+                    int32_t* n_vis, hipStream_t s);
 void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
                       float* acc, hipStream_t s);
 void launch_col(int32_t dtype, bool rope, bool partial, const ColArgs& a, hipStream_t s);

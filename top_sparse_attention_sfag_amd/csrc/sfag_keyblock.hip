@@ -953,6 +953,90 @@ __global__ void __launch_bounds__(256) k_vis_write(const int32_t* __restrict__ c
   }
 }
 
+// Pairs of a chunk grouped by (key block, token) without a global sort: a
+// counting sort whose counters sit in the (key block, token) grid, key block
+// major.  k_bin_count histograms each token's valid positions over the key
+// blocks (LDS atomics) into cnt and flg (count, count > 0); exclusive scans
+// of both give every (key block, token) cell its first slot among the sorted
+// pairs and its visit number; k_bin_scatter then writes each token's visits
+// and places its pairs (pair id tl * E + j, key row within the block) at
+// their cells' slots.  Within one cell the pairs land in no fixed order: a
+// visit's slot map places each pair's row by key row, and pairs that share a
+// key row (one token listing a key twice) hold identical rows, so the sums
+// do not depend on that order.  The result matches the stable sort by key
+// block (visits in (key block, token) order, vis_start[v + 1] - vis_start[v]
+// pairs each).
+__global__ void __launch_bounds__(256) k_bin_count(const int32_t* __restrict__ rows,
+                                                   const int32_t* __restrict__ nvalid, int64_t E, int32_t nkb,
+                                                   int64_t ntok, int32_t* __restrict__ cnt,
+                                                   int32_t* __restrict__ flg) {
+  extern __shared__ int32_t hist[];   // nkb
+  const int64_t tl = blockIdx.x;
+  for (int i = threadIdx.x; i < nkb; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int nv = nvalid[tl];
+  const int32_t* r = rows + tl * E;
+  for (int j = threadIdx.x; j < nv; j += 256) atomicAdd(&hist[r[j] / kKB], 1);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nkb; i += 256) {
+    const int32_t c = hist[i];
+    cnt[(int64_t)i * ntok + tl] = c;
+    flg[(int64_t)i * ntok + tl] = c > 0 ? 1 : 0;
+  }
+}
+
+// goff, vidx: the exclusive scans of cnt and flg.
+__global__ void __launch_bounds__(256) k_bin_scatter(const int32_t* __restrict__ rows,
+                                                     const int32_t* __restrict__ nvalid, int64_t E, int32_t nkb,
+                                                     int64_t ntok, const int32_t* __restrict__ goff,
+                                                     const int32_t* __restrict__ vidx, int32_t* __restrict__ svals,
+                                                     int32_t* __restrict__ er, int32_t* __restrict__ vis_start,
+                                                     int32_t* __restrict__ vis_key, int32_t* __restrict__ n_vis) {
+  extern __shared__ int32_t sh[];     // hist[nkb], cursor[nkb]
+  int32_t* hist = sh;
+  int32_t* cursor = sh + nkb;
+  const int64_t tl = blockIdx.x;
+  for (int i = threadIdx.x; i < nkb; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int nv = nvalid[tl];
+  const int32_t* r = rows + tl * E;
+  for (int j = threadIdx.x; j < nv; j += 256) atomicAdd(&hist[r[j] / kKB], 1);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nkb; i += 256) {
+    const int64_t cell = (int64_t)i * ntok + tl;
+    cursor[i] = goff[cell];
+    if (hist[i] > 0) {
+      const int32_t v = vidx[cell];
+      vis_start[v] = goff[cell];
+      vis_key[v] = (int32_t)cell;
+    }
+    if (cell == (int64_t)nkb * ntok - 1) {   // the grid's last cell closes the lists
+      const int32_t nvis = vidx[cell] + (hist[i] > 0 ? 1 : 0);
+      vis_start[nvis] = goff[cell] + hist[i];
+      *n_vis = nvis;
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nv; j += 256) {
+    const int32_t row = r[j], kb = row / kKB;
+    const int32_t pos = atomicAdd(&cursor[kb], 1);
+    svals[pos] = (int32_t)(tl * E + j);
+    er[pos] = row - kb * kKB;
+  }
+}
+
+void launch_kb_bins(const int32_t* rows, const int32_t* nvalid, int64_t E, int32_t nkb, int64_t ntok, int32_t* cnt,
+                    int32_t* flg, int32_t* scan_tmp, int32_t* svals, int32_t* er, int32_t* vis_start, int32_t* vis_key,
+                    int32_t* n_vis, hipStream_t s) {
+  if (ntok == 0) return;
+  hipLaunchKernelGGL(k_bin_count, dim3((unsigned)ntok), dim3(256), (size_t)nkb * 4, s, rows, nvalid, E, nkb, ntok,
+                     cnt, flg);
+  launch_scan_i32(cnt, (int64_t)nkb * ntok, scan_tmp, s);
+  launch_scan_i32(flg, (int64_t)nkb * ntok, scan_tmp, s);
+  hipLaunchKernelGGL(k_bin_scatter, dim3((unsigned)ntok), dim3(256), (size_t)nkb * 8, s, rows, nvalid, E, nkb, ntok,
+                     cnt, flg, svals, er, vis_start, vis_key, n_vis);
+}
+
 // acc[row] += Σ_tr part[tr][row] over the token ranges whose (range, key
 // block) was non-empty, in ascending range order.
 __global__ void __launch_bounds__(256) k_kb_reduce(const float* __restrict__ part, const int32_t* __restrict__ nonempty,

@@ -428,6 +428,15 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
   auto pre_work = [&](int64_t ntok, hipStream_t st) {
     const int64_t n = ntok * d.E;
     TimedScope ts("kb_sort", st);
+    if (kb_use_bins(d)) {
+      int32_t* grid = at<int32_t>(workspace, w.kb_grid);
+      svals = at<int32_t>(workspace, w.sort_vals[0]);
+      launch_kb_bins(rows, nvalid, d.E, (int32_t)d.nKB, ntok, grid, grid + d.nKB * ntok,
+                     at<int32_t>(workspace, w.kb_grid_tmp), svals, at<int32_t>(workspace, w.vis_er),
+                     at<int32_t>(workspace, w.vis_start), at<int32_t>(workspace, w.vis_key),
+                     at<int32_t>(workspace, w.vis_n), st);
+      return;
+    }
     launch_csr(n, rows, nvalid, d.E, d.T2, d.kb_sort_bits, keys, vals, at<int32_t>(workspace, w.sort_hist),
                nullptr, &svals, st, 1, ntok, &skeys);
     launch_visits(skeys, svals, rows, n, ntok, (int32_t)d.nKB, at<int32_t>(workspace, w.vis_flags),

@@ -39,6 +39,8 @@ struct WorkspaceLayout {
   uint64_t vis_key = 0;    // int32 (chunk*E): composite key of each visit
   uint64_t vis_er = 0;     // int32 (chunk*E): key row within its block of each sorted pair
   uint64_t vis_n = 0;      // int32: number of visits
+  uint64_t kb_grid = 0;    // int32 (2, nKB, chunk): per (key block, token) counts and visit flags, then their scans
+  uint64_t kb_grid_tmp = 0;  // int32: segment sums of the grid scans
   uint64_t dq_acc = 0;     // fp32 (chunk, G, D + Dr): dQ|dQrope sums when a token's positions are split
   uint64_t total = 0;
 };
@@ -73,6 +75,11 @@ constexpr int kDefaultRanges = 16;
 
 // Key rows per block of the key-centric dK/dV contraction.
 constexpr int kKeyBlockRows = 256;
+
+// Key blocks up to which the key-block path groups pairs by per-token
+// counting (counters in LDS) instead of the global radix sort.
+constexpr int64_t kMaxBinBlocks = 8192;
+inline bool kb_use_bins(const Dims& d) { return d.nKB <= kMaxBinBlocks && d.nKB <= 2 * d.E; }
 
 // Radix-sort block geometry shared by host and kernels.
 constexpr int kSortThreads = 256;

@@ -143,6 +143,27 @@ def test_duplicated_indices(G, options):
     _run(case, 3, inp=inp, options=options)
 
 
+@pytest.mark.parametrize("K", [200, 400], ids=["k200", "k400_long_visits"])
+def test_duplicated_indices_key_blocks(K):
+    """128 heads, key-block path, three key blocks and three token ranges of
+    8: keys listed several times by tokens past the first two of a range
+    (slot maps built from pairs copied ahead), and, with K = 400, one key
+    listed 300 times (a visit of more pairs than the 256 copied ahead, the
+    rest read from memory) and another 280 times by the first token of a
+    range (a map built before the pipeline starts)."""
+    case = si.Case("dup_maps", S1=24, S2=600, G=128, K=K)
+    inp = si.make_inputs(case, 4)
+    idx = inp["sparse_indices"].reshape(24, K)
+    idx[3, 20:40] = idx[3, 0]          # twenty times
+    idx[12, :] = idx[12, 7]            # a whole row of one key
+    idx[20, 1] = idx[20, 0]            # twice
+    if K > 255:
+        idx[5, :300] = 17              # 300 times, fifth token of its range
+        idx[8, :280] = 300             # 280 times, first token of its range
+    inp = add_oracle_stats(case, inp)
+    _run(case, 4, inp=inp, options=dict(scatter="keyblock"))
+
+
 def test_masked_rows_never_read():
     """Key rows named only by masked entries (after the causal bound, or past
     the key length) hold NaN: every output must stay finite, match the oracle,

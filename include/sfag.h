@@ -103,8 +103,9 @@ typedef struct sfag_plan sfag_plan;
  *   tokenPath        SFAG_TOKEN_* (FUSED is the default for N1 <= 16).
  *   tokenOrder       SFAG_ORDER_*.
  *   concurrent       SFAG_CONCURRENT_*: run the dQ kernel on a second stream
- *                    beside the key-block kernels (default on for
- *                    32 <= N1 < 128 on the key-block path).
+ *                    beside the key-block kernels (default on the key-block
+ *                    path for 32 <= N1 < 128, and for N1 = 128 with chunks
+ *                    of at most 4096 tokens).
  *   rowSplit         workgroups sharing one token's positions in the fused
  *                    token kernel (0 = chosen; 1..8; never split when
  *                    deterministic, whose sums must keep a fixed order).
@@ -180,7 +181,8 @@ int sfag_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const 
  * enqueued; errors found by the kernels are not reported (indices are bounds
  * checked on the device, so bad indices are masked, never dereferenced).
  * When the plan runs the dQ kernel beside the key-block kernels (by default
- * with 32 <= N1 < 128; sfag_options.concurrent), that kernel goes on a
+ * with 32 <= N1 < 128, or N1 = 128 and chunks of at most 4096 tokens;
+ * sfag_options.concurrent), that kernel goes on a
  * second stream (sfag_options.auxStream, or one of the library's: one per
  * device, default priority, made on first use and kept until the process
  * ends) between an event recorded on `stream` and an event `stream` waits

@@ -384,16 +384,20 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
 
   // A second stream on the key-block path with the split token kernels:
   // k_dq runs beside the key-block kernels (64 heads, 8192 varlen tokens,
-  // top-2048 causal: 9.4 -> 8.4 ms; with 128 heads no gain at 4096 tokens
-  // and +3% at 32768, so off there by default).  Running the key-block
-  // pre-work (then transposes, sort, visits) beside k_sdp instead measured no gain
-  // (128 heads, 4096 tokens: 7.67 -> 7.89 ms), so it stays on `stream`.  The
-  // caller's auxiliary stream if it gave one (with events of the call's own),
-  // else the library's, whose events this call holds for its whole enqueue
-  // sequence.
+  // top-2048 causal: 9.4 -> 8.4 ms).  With 128 heads it pays only where the
+  // key-block launch is short enough that its last round of workgroups
+  // leaves CUs idle for k_dq to fill (4096 tokens, top-2048 causal: 6.66 ->
+  // 6.55 ms), and costs on long ones (32768 tokens, top-8192: 286 -> 293 ms,
+  // in 3 chunks or in one), so by default it is on there for chunks of at
+  // most 4096 tokens.  Running the key-block pre-work beside k_sdp instead
+  // measured no gain (128 heads, 4096 tokens: 7.67 -> 7.89 ms), so it stays
+  // on `stream`.  The caller's auxiliary stream if it gave one (with events
+  // of the call's own), else the library's, whose events this call holds for
+  // its whole enqueue sequence.
   const bool kb_work = keyblock && d.E > 0;
+  const bool side_pays = d.Gp < 128 || d.chunk <= 4096;
   bool concurrent = kb_work && !use_row &&
-                    (o.concurrent == SFAG_CONCURRENT_ON || (o.concurrent == SFAG_CONCURRENT_AUTO && d.Gp < 128));
+                    (o.concurrent == SFAG_CONCURRENT_ON || (o.concurrent == SFAG_CONCURRENT_AUTO && side_pays));
   bool dq_side = concurrent;
   SideStream own_side;
   struct OwnEvents {

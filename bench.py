@@ -446,11 +446,13 @@ def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", val
 
         def step(opts=options):
             sfag.backward(*args_pos, outputs=outs, workspace=ws, stream=stream, options=opts, **kw)
-        # with 32 <= N1 < 128 the dQ kernel runs on a second stream beside the
-        # key-block kernels (see sfag_options.concurrent): the per-kernel
-        # times that pick the roofline kernel then come from a serial pass
+        # unless told to stay serial the library may run the dQ kernel on a
+        # second stream beside the key-block kernels (see
+        # sfag_options.concurrent; by default for 32 <= N1 < 128, and for 128
+        # heads with short chunks): the per-kernel times that pick the
+        # roofline kernel then come from a serial pass
         cc = (options or {}).get("concurrent", "auto")
-        concurrent = cc == "on" or (cc == "auto" and 32 <= case.G < 128)
+        concurrent = cc != "off"
 
     for _ in range(warmup):
         step()
@@ -494,7 +496,7 @@ def _measure(case, inp, n_pairs, det, steps, warmup, sfag, which="backward", val
     dom_ms = src[dom][0] / src[dom][1]
     launches_per_step = src[dom][1] / (nsteps_r if src is rprof else steps)
     timing = ("HIP events on the kernel's stream in a serial pass after the timed region (the default schedule "
-              "overlaps it with the second stream)" if src is rprof and concurrent
+              "may overlap it with the second stream)" if src is rprof and concurrent
               else "HIP events on the kernel's stream in the timed region")
     roof = _roofline(case, dom, dom_ms, launches_per_step, n_pairs)
     rec = _traffic_record(case) if which == "backward" and not value_is_key and options is None else None

@@ -103,9 +103,10 @@ typedef struct sfag_plan sfag_plan;
  *   tokenPath        SFAG_TOKEN_* (FUSED is the default for N1 <= 16).
  *   tokenOrder       SFAG_ORDER_*.
  *   concurrent       SFAG_CONCURRENT_*: run the dQ kernel on a second stream
- *                    beside the key-block kernels (default on the key-block
- *                    path for 32 <= N1 < 128, and for N1 = 128 with chunks
- *                    of at most 4096 tokens).
+ *                    beside the key-block kernels, and the key-block
+ *                    grouping there beside the S/dP kernel (default on the
+ *                    key-block path for 32 <= N1 < 128, and for N1 = 128
+ *                    with chunks of at most 4096 tokens).
  *   rowSplit         workgroups sharing one token's positions in the fused
  *                    token kernel (0 = chosen; 1..8; never split when
  *                    deterministic, whose sums must keep a fixed order).
@@ -182,13 +183,13 @@ int sfag_workspace_size(const sfag_tensor* query, const sfag_tensor* key, const 
  * checked on the device, so bad indices are masked, never dereferenced).
  * When the plan runs the dQ kernel beside the key-block kernels (by default
  * with 32 <= N1 < 128, or N1 = 128 and chunks of at most 4096 tokens;
- * sfag_options.concurrent), that kernel goes on a
+ * sfag_options.concurrent), that kernel and the key-block grouping go on a
  * second stream (sfag_options.auxStream, or one of the library's: one per
  * device, default priority, made on first use and kept until the process
- * ends) between an event recorded on `stream` and an event `stream` waits
- * for, so every output is complete once `stream` reaches that point: the
- * caller synchronizes `stream` only.  Calls that share the library's second
- * stream on one device are ordered on it.
+ * ends) between events recorded on `stream` and events `stream` waits for,
+ * so every output is complete once `stream` reaches the end of the call's
+ * work: the caller synchronizes `stream` only.  Calls that share the
+ * library's second stream on one device are ordered on it.
  */
 int sfag_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void* stream);
 

@@ -966,6 +966,29 @@ __global__ void __launch_bounds__(256) k_vis_write(const int32_t* __restrict__ c
 // do not depend on that order.  The result matches the stable sort by key
 // block (visits in (key block, token) order, vis_start[v + 1] - vis_start[v]
 // pairs each).
+// Runs of equal key blocks among the active lanes of a wave (the active
+// lanes are a prefix: positions j < nvalid): `head` is set on a run's first
+// lane, `len` there is the run's length, and `first` on every active lane is
+// its run's first lane.  Sorted rows give long runs, so one LDS atomic per
+// run replaces one per lane (they would all hit the same counter).
+struct Run {
+  bool head;
+  int len, first;
+};
+__device__ __forceinline__ Run lane_run(int32_t kb, bool act, int lane) {
+  const int32_t prev = __shfl_up(kb, 1);
+  const bool head = act && (lane == 0 || prev != kb);
+  const uint64_t heads = __ballot(head);
+  const int nact = __popcll(__ballot(act));
+  const uint64_t above = heads & ~((2ull << lane) - 1);
+  const uint64_t upto = heads & ((2ull << lane) - 1);
+  Run r;
+  r.head = head;
+  r.len = min(above ? (int)__builtin_ctzll(above) : 64, nact) - lane;
+  r.first = upto ? 63 - (int)__builtin_clzll(upto) : lane;
+  return r;
+}
+
 __global__ void __launch_bounds__(256) k_bin_count(const int32_t* __restrict__ rows,
                                                    const int32_t* __restrict__ nvalid, int64_t E, int32_t nkb,
                                                    int64_t ntok, int32_t* __restrict__ cnt,
@@ -976,7 +999,14 @@ __global__ void __launch_bounds__(256) k_bin_count(const int32_t* __restrict__ r
   __syncthreads();
   const int nv = nvalid[tl];
   const int32_t* r = rows + tl * E;
-  for (int j = threadIdx.x; j < nv; j += 256) atomicAdd(&hist[r[j] / kKB], 1);
+  const int lane = threadIdx.x & 63;
+  for (int j0 = 0; j0 < nv; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    const bool act = j < nv;
+    const int32_t kb = act ? r[j] / kKB : -1;
+    const Run run = lane_run(kb, act, lane);
+    if (run.head) atomicAdd(&hist[kb], run.len);
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < nkb; i += 256) {
     const int32_t c = hist[i];
@@ -1000,7 +1030,14 @@ __global__ void __launch_bounds__(256) k_bin_scatter(const int32_t* __restrict__
   __syncthreads();
   const int nv = nvalid[tl];
   const int32_t* r = rows + tl * E;
-  for (int j = threadIdx.x; j < nv; j += 256) atomicAdd(&hist[r[j] / kKB], 1);
+  const int lane = threadIdx.x & 63;
+  for (int j0 = 0; j0 < nv; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    const bool act = j < nv;
+    const int32_t kb = act ? r[j] / kKB : -1;
+    const Run run = lane_run(kb, act, lane);
+    if (run.head) atomicAdd(&hist[kb], run.len);
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < nkb; i += 256) {
     const int64_t cell = (int64_t)i * ntok + tl;
@@ -1017,11 +1054,19 @@ __global__ void __launch_bounds__(256) k_bin_scatter(const int32_t* __restrict__
     }
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < nv; j += 256) {
-    const int32_t row = r[j], kb = row / kKB;
-    const int32_t pos = atomicAdd(&cursor[kb], 1);
-    svals[pos] = (int32_t)(tl * E + j);
-    er[pos] = row - kb * kKB;
+  for (int j0 = 0; j0 < nv; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    const bool act = j < nv;
+    const int32_t row = act ? r[j] : 0, kb = act ? row / kKB : -1;
+    const Run run = lane_run(kb, act, lane);
+    int32_t base = 0;
+    if (run.head) base = atomicAdd(&cursor[kb], run.len);
+    base = __shfl(base, run.first);
+    if (act) {
+      const int32_t pos = base + (lane - run.first);
+      svals[pos] = (int32_t)(tl * E + j);
+      er[pos] = row - kb * kKB;
+    }
   }
 }
 

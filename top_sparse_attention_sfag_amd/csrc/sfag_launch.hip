@@ -83,10 +83,11 @@ void prof_drain() {
   g_prof_pending.clear();
 }
 
-// A second stream per device (default priority, non-blocking) and two
-// events, made on first use and kept for the life of the process: k_dq runs
-// on it beside the key-block kernels, so that each fills the other's tail.
-enum SideEvent { kEvSdp = 0, kEvDq = 1, kNumSideEvents = 2 };
+// A second stream per device (default priority, non-blocking) and its
+// events, made on first use and kept for the life of the process: the
+// key-block pre-work runs on it beside k_sdp and k_dq beside the key-block
+// kernels, so that each fills the other's tail.
+enum SideEvent { kEvSdp = 0, kEvDq = 1, kEvDecode = 2, kEvPre = 3, kNumSideEvents = 4 };
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t ev[kNumSideEvents] = {};
@@ -199,7 +200,7 @@ extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* 
     const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
     {
       TimedScope ts("decode", s);
-      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s, status);
+      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s, status, true);
     }
     fa.t0 = t0;
     fa.ntok = ntok;
@@ -389,11 +390,13 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
   // leaves CUs idle for k_dq to fill (4096 tokens, top-2048 causal: 6.66 ->
   // 6.55 ms), and costs on long ones (32768 tokens, top-8192: 286 -> 293 ms,
   // in 3 chunks or in one), so by default it is on there for chunks of at
-  // most 4096 tokens.  Running the key-block pre-work beside k_sdp instead
-  // measured no gain (128 heads, 4096 tokens: 7.67 -> 7.89 ms), so it stays
-  // on `stream`.  The caller's auxiliary stream if it gave one (with events
-  // of the call's own), else the library's, whose events this call holds for
-  // its whole enqueue sequence.
+  // most 4096 tokens.  Where the second stream is used, the key-block
+  // pre-work (grouping the pairs by key block) runs on it beside k_sdp, off
+  // the path from k_sdp to the key-block kernel (128 heads, 4096 tokens:
+  // 6.52 -> 6.48 ms; beside k_dq it took 0.33 ms of that path).  The
+  // caller's auxiliary stream if it gave one (with events of the call's
+  // own), else the library's, whose events this call holds for its whole
+  // enqueue sequence.
   const bool kb_work = keyblock && d.E > 0;
   const bool side_pays = d.Gp < 128 || d.chunk <= 4096;
   bool concurrent = kb_work && !use_row &&
@@ -452,10 +455,17 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
     const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
     {
       TimedScope ts("decode", s);
-      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s, status);
+      launch_decode((const int32_t*)plan->idx, t0, ntok, d, q_off, kv_off, rows, nvalid, s, status, true);
     }
     ra.t0 = ca.t0 = t0;
     ra.ntok = ca.ntok = ntok;
+    const bool pre_side = dq_side && kb_work;   // pre-work beside k_sdp
+    if (pre_side) {
+      if (!order(s, side->s, kEvDecode)) return fail(SFAG_ERR_RUNTIME, "fork to the second stream failed");
+      pre_work(ntok, side->s);
+      if (hipEventRecord(side->ev[kEvPre], side->s) != hipSuccess)
+        return fail(SFAG_ERR_RUNTIME, "second stream event failed");
+    }
     if (!use_row) {
       {
         TimedScope ts("sdp", s);
@@ -486,7 +496,9 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
       launch_row(plan->dtype, rope, ra, s);
     }
     if (kb_work) {
-      pre_work(ntok, s);
+      if (!pre_side) pre_work(ntok, s);
+      else if (hipStreamWaitEvent(s, side->ev[kEvPre], 0) != hipSuccess)
+        return fail(SFAG_ERR_RUNTIME, "join of the second stream failed");
       {
         KbArgs ka;
         ka.q = ra.q;

@@ -75,9 +75,10 @@ void launch_seq_offsets(const int32_t* lq, const int32_t* lk, int32_t B, int64_t
                         int32_t* kv_off, uint32_t* status, hipStream_t s);
 void launch_delta(int32_t dtype, const void* dO, const void* O, float* delta, int64_t nrows, hipStream_t s);
 void launch_fill_u32(void* p, uint64_t n, uint32_t v, hipStream_t s);
-// sort_entries: each token's entries in ascending order first (K <= 8192),
-// for the locality of the token kernels' gathers; off where the rows must
-// follow the listing (the index inversion exposed on its own).
+// sort_entries: each token's entries in ascending order first (K <= 16384,
+// sequences of at most 65536 keys, no key listed twice), for the locality of
+// the token kernels' gathers; off where the rows must follow the listing
+// (the index inversion exposed on its own).
 void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, const int32_t* q_off,
                    const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s, uint32_t* status = nullptr,
                    bool sort_entries = false);

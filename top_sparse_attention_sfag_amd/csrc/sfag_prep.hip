@@ -87,113 +87,88 @@ __global__ void __launch_bounds__(256) k_fill_u32(uint32_t* __restrict__ p, uint
 // sparseMode 0 / 3).  Position e = j*block + r of token t is p = idx[t][j] + r,
 // valid iff idx[t][j] >= 0, p < Lk and (mode 3) p <= t_loc + Lk - Lq.  The
 // valid positions are compacted into rows[tl][c] = kv_base + p, and only rows
-// in [0, T2) are ever written.  With a sort the token's in-range entries are
+// in [0, T2) are ever written.  With nw > 0 the token's in-range entries are
 // first put in ascending order, so that the token kernels walk each token's
 // keys in ascending order: tokens that run at the same time on one XCD then
-// gather from nearby key ranges through its L2.  Two sorts, picked by the
-// host for their cost: a counting sort when the sequences are short
-// (kSortCount: sn 32-bit words of LDS hold two 16-bit counters each, one per
-// key, Lk <= 2 sn; the sorted entries follow as 16-bit values), else a
-// bitonic network for few entries (kSortNetwork: sn = the power of two >= K
-// of 32-bit entries).  Entries equal in value are interchangeable (they name
-// the same rows), so the order is fixed by the values alone and the results
-// stay bitwise reproducible; the sums see the terms in a different order
-// than the listing's, which nothing fixes.  With a validation word (status
-// != NULL) entries at or past the key length are counted there.  One block
-// per token of the chunk.
+// gather from nearby key ranges through its L2.  The sort marks each entry
+// in a bitmap of the sequence's keys (nw 32-bit words in LDS, Lk <= 32 nw)
+// and reads the set bits back in order (a popcount scan gives each word its
+// first slot; the sorted entries follow the bitmap as 16-bit values).  A
+// token that lists a key twice keeps the listing's order instead (the
+// bitmap holds one bit a key), so the order depends on the entries alone
+// and the results stay bitwise reproducible; the sums see the terms in a
+// different order than the listing's, which nothing fixes.  With a
+// validation word (status != NULL) entries at or past the key length are
+// counted there.  One block per token of the chunk.
 // ---------------------------------------------------------------------------
-constexpr int32_t kSortNone = 0, kSortCount = 1, kSortNetwork = 2;
-
 __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx, int64_t t0, int64_t K, int32_t block,
                                                 int32_t mode, int32_t layout, int64_t S1, int64_t S2,
                                                 const int32_t* q_off, const int32_t* kv_off, int32_t B, int64_t T2,
                                                 int32_t* __restrict__ rows, int32_t* __restrict__ nvalid,
-                                                uint32_t* status, int32_t sort, int32_t sn) {
+                                                uint32_t* status, int32_t nw) {
   const int64_t tl = blockIdx.x;
   const int64_t t = t0 + tl;
   const int64_t E = K * block;
-  extern __shared__ uint32_t dsh[];   // the sort's LDS (see above)
+  extern __shared__ uint32_t dsh[];   // nw bitmap words, then the sorted entries (16-bit)
   __shared__ int32_t warp_tot[4];
-  __shared__ int32_t base_s, n_in_s;
+  __shared__ int32_t base_s, n_in_s, dup_s;
   const TokenGeo g = token_geo(t, layout, S1, S2, q_off, kv_off, B);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) base_s = 0;
+  if (tid == 0) {
+    base_s = 0;
+    dup_s = 0;
+  }
   int32_t bad = 0;
   // (uniform: one token per block)
-  const bool by_count = sort == kSortCount && g.ok && ((g.Lk + 1) >> 1) <= sn;
-  const bool by_net = sort == kSortNetwork && g.ok;
-  const uint16_t* srt16 = (const uint16_t*)(dsh + sn);
-  const int32_t* srt32 = (const int32_t*)dsh;
+  bool srtd = nw > 0 && g.ok && g.Lk <= 32 * nw;
+  uint16_t* srt = (uint16_t*)(dsh + nw);
   int64_t Ew = E;                        // positions walked below
-  if (by_count) {
+  if (srtd) {
     const int32_t Lk = g.Lk;
-    const int nwt = (Lk + 1) >> 1;
+    const int nwt = (Lk + 31) >> 5;
     for (int i = tid; i < nwt; i += 256) dsh[i] = 0u;
     __syncthreads();
+    bool dup = false;
     for (int j = tid; j < K; j += 256) {
       const int32_t ent = idx[t * K + j];
       if (ent >= Lk) ++bad;
-      if (ent >= 0 && ent < Lk) atomicAdd(&dsh[ent >> 1], 1u << (16 * (ent & 1)));
-    }
-    __syncthreads();
-    // counts -> first slots: thread tid takes words tid*cw .. +cw
-    const int cw = (nwt + 255) / 256;
-    const int w0 = min(nwt, tid * cw), w1 = min(nwt, w0 + cw);
-    uint32_t sum = 0;
-    for (int i = w0; i < w1; ++i) {
-      const uint32_t v = dsh[i];
-      sum += (v & 0xffffu) + (v >> 16);
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) warp_tot[w] = (int32_t)incl;
-    __syncthreads();
-    uint32_t run = incl - sum;
-    for (int i = 0; i < w; ++i) run += (uint32_t)warp_tot[i];
-    if (tid == 255) n_in_s = (int32_t)(run + sum);
-    // (slots stay below K <= 8192: no carry into the upper counter)
-    for (int i = w0; i < w1; ++i) {
-      const uint32_t v = dsh[i], lo = v & 0xffffu;
-      dsh[i] = run | ((run + lo) << 16);
-      run += lo + (v >> 16);
-    }
-    __syncthreads();
-    uint16_t* dst = (uint16_t*)(dsh + sn);
-    for (int j = tid; j < K; j += 256) {
-      const int32_t ent = idx[t * K + j];
       if (ent >= 0 && ent < Lk) {
-        const uint32_t sh = 16u * (uint32_t)(ent & 1);
-        const uint32_t slot = (atomicAdd(&dsh[ent >> 1], 1u << sh) >> sh) & 0xffffu;
-        dst[slot] = (uint16_t)ent;
+        const uint32_t bit = 1u << (ent & 31);
+        if (atomicOr(&dsh[ent >> 5], bit) & bit) dup = true;
       }
     }
+    if (dup) dup_s = 1;
     __syncthreads();
-    Ew = (int64_t)n_in_s * block;
-  } else if (by_net) {
-    constexpr int32_t kLast = 0x7fffffff;   // negative entries and padding sort last
-    int32_t* a = (int32_t*)dsh;
-    for (int j = tid; j < sn; j += 256) {
-      const int32_t ent = j < K ? idx[t * K + j] : -1;
-      if (ent >= g.Lk) ++bad;
-      a[j] = ent >= 0 ? ent : kLast;
-    }
-    __syncthreads();
-    for (int k = 2; k <= sn; k <<= 1) {
-      for (int h = k >> 1; h > 0; h >>= 1) {
-        for (int i = tid; i < (sn >> 1); i += 256) {
-          const int lo = 2 * i - (i & (h - 1)), hi = lo + h;
-          const int32_t x = a[lo], y = a[hi];
-          if ((x > y) == ((lo & k) == 0)) {
-            a[lo] = y;
-            a[hi] = x;
-          }
+    srtd = dup_s == 0;
+    if (srtd) {
+      // first slot of each word: thread tid takes words tid*cw .. +cw
+      const int cw = (nwt + 255) / 256;
+      const int w0 = min(nwt, tid * cw), w1 = min(nwt, w0 + cw);
+      uint32_t sum = 0;
+      for (int i = w0; i < w1; ++i) sum += (uint32_t)__popc(dsh[i]);
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) warp_tot[w] = (int32_t)incl;
+      __syncthreads();
+      uint32_t slot = incl - sum;
+      for (int i = 0; i < w; ++i) slot += (uint32_t)warp_tot[i];
+      if (tid == 255) n_in_s = (int32_t)(slot + sum);
+      for (int i = w0; i < w1; ++i) {
+        uint32_t m = dsh[i];
+        while (m) {
+          const int b = __builtin_ctz(m);
+          m &= m - 1;
+          srt[slot++] = (uint16_t)(32 * i + b);
         }
-        __syncthreads();
       }
+      __syncthreads();
+      Ew = (int64_t)n_in_s * block;
+    } else {
+      bad = 0;   // counted again by the walk over the listing below
     }
   }
   int32_t* out = rows + tl * E;
@@ -203,13 +178,12 @@ __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx,
     int64_t row = 0;
     if (e < Ew && g.ok) {
       const int64_t j = e / block, r = e - j * block;
-      int32_t ent = by_count ? (int32_t)srt16[j] : by_net ? srt32[j] : idx[t * K + j];
-      if (by_net && ent == 0x7fffffff) ent = -1;
+      const int32_t ent = srtd ? (int32_t)srt[j] : idx[t * K + j];
       const int64_t p = (int64_t)ent + r;
       valid = ent >= 0 && p < g.Lk && (mode != 3 || p <= g.bound);
       row = g.kv_base + p;
       valid = valid && row >= 0 && row < T2;
-      if (!by_count && !by_net && r == 0 && ent >= g.Lk) ++bad;
+      if (!srtd && r == 0 && ent >= g.Lk) ++bad;
     }
     const uint64_t bal = __ballot(valid);
     const int rank = __popcll(bal & ((1ull << lane) - 1));
@@ -557,27 +531,14 @@ void launch_decode(const int32_t* idx, int64_t t0, int64_t ntok, const Dims& d, 
                    const int32_t* kv_off, int32_t* rows, int32_t* nvalid, hipStream_t s, uint32_t* status,
                    bool sort_entries) {
   if (ntok == 0) return;
-  // The sort and its LDS: counting over a 16-bit counter per key of the
-  // longest sequence (BSND: S2; TND: at most T2) where that is short (its
-  // cost grows with the key count: 0.02 ms for 4096 tokens of top-2048 over
-  // 4096 keys, 1.2 ms for 65536 tokens of 512 blocks over 32768 keys);
-  // else the network for up to 1024 entries (0.08 ms for the latter); else
-  // none (8192 entries over 32768 keys cost more than the gathers gain).
+  // the sort's LDS: a bit per key of the longest sequence (BSND: S2; TND:
+  // at most T2), keys below 65536 so that 16 bits hold a sorted entry
   const int64_t lk_max = d.layout == 0 ? d.S2 : d.T2;
-  int32_t sort = kSortNone, sn = 0;
-  size_t lds = 0;
-  if (sort_entries && d.K > 1 && d.K <= 8192 && lk_max <= 8192) {
-    sort = kSortCount;
-    sn = (int32_t)std::max<int64_t>(1, (lk_max + 1) / 2);
-    lds = (size_t)sn * 4 + (size_t)(d.K + 1) / 2 * 4;
-  } else if (sort_entries && d.K > 1 && d.K <= 1024) {
-    sort = kSortNetwork;
-    sn = 1;
-    while (sn < d.K) sn *= 2;
-    lds = (size_t)sn * 4;
-  }
+  int32_t nw = 0;
+  if (sort_entries && d.K > 1 && d.K <= 16384 && lk_max <= 65536) nw = (int32_t)std::max<int64_t>(1, (lk_max + 31) / 32);
+  const size_t lds = nw ? (size_t)nw * 4 + (size_t)(d.K + 1) / 2 * 4 : 0;
   hipLaunchKernelGGL(k_decode, dim3((unsigned)ntok), dim3(256), lds, s, idx, t0, d.K, (int32_t)d.block, d.mode,
-                     d.layout, d.S1, d.S2, q_off, kv_off, (int32_t)d.B, d.T2, rows, nvalid, status, sort, sn);
+                     d.layout, d.S1, d.S2, q_off, kv_off, (int32_t)d.B, d.T2, rows, nvalid, status, nw);
 }
 
 void launch_csr(int64_t n, const int32_t* rows, const int32_t* nvalid, int64_t E, int64_t T2, int32_t sort_bits,

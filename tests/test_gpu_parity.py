@@ -393,3 +393,42 @@ def test_auxiliary_stream_of_the_caller():
     torch.cuda.synchronize()
     for a, b in zip(serial, got):
         assert torch.equal(a, b)
+
+
+# Listing-order invariance: each token's entries are walked in ascending key
+# order whatever order the listing gives them (no key listed twice, keys
+# below 65536), so a permuted listing gives the same bits, forward and
+# backward, on the 128-head, N1 <= 16 (blocks) and TND paths.
+ORDER_CASES = [
+    si.Case("order_g128_causal", S1=48, S2=300, G=128, K=96, mode=3, index_rule="causal_mix"),
+    si.Case("order_g16_blocks", S1=20, S2=512, G=16, Dr=0, K=12, block=16, dtype="fp16", std=0.5,
+            index_rule="blocks"),
+    si.Case("order_g64_tnd", layout="TND", B=3, seqlens_q=(20, 0, 31), seqlens_kv=(60, 4, 90), G=64, K=40,
+            mode=3, index_rule="causal_mix"),
+]
+
+
+@pytest.mark.parametrize("case", ORDER_CASES, ids=[c.name for c in ORDER_CASES])
+def test_listing_order_does_not_change_bits(case):
+    import top_sparse_attention_sfag_amd as sfag
+    inp = add_oracle_stats(case, si.make_inputs(case, 8))
+    idx = inp["sparse_indices"].cpu()
+    rows = idx.reshape(-1, idx.shape[-1])
+    g = torch.Generator().manual_seed(11)
+    perm = torch.stack([torch.randperm(rows.shape[1], generator=g) for _ in range(rows.shape[0])])
+    shuffled = torch.gather(rows, 1, perm).reshape(idx.shape).contiguous()
+    assert not torch.equal(shuffled, idx)
+    runs = []
+    for listing in (idx, shuffled):
+        dev = to_device(dict(inp, sparse_indices=listing))
+        print(f"listing order {case.name}", flush=True)
+        outs = [o.clone() for o in call_backward(case, dev, deterministic=True) if o is not None]
+        fwd = sfag.forward(dev["query"], dev["key"], dev["value"], dev["sparse_indices"],
+                           seqlens_q=dev.get("seqlens_q"), seqlens_kv=dev.get("seqlens_kv"),
+                           query_rope=dev.get("query_rope"), key_rope=dev.get("key_rope"), scale=case.scale_value,
+                           block_size=case.block, layout=case.layout, sparse_mode=case.mode)
+        torch.cuda.synchronize()
+        runs.append(outs + [fwd[0].clone(), fwd[1].clone(), fwd[2].clone()])
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int16) if a.element_size() == 2 else a.view(torch.int32),
+                           b.view(torch.int16) if b.element_size() == 2 else b.view(torch.int32))

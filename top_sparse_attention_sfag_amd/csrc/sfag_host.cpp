@@ -55,6 +55,7 @@ WorkspaceLayout layout_for(const Dims& d, int32_t scatter, bool validate) {
     carve(c, w.csr_off, (uint64_t)(d.T2 + 1) * 4);
   }
   if (d.row_split > 1) carve(c, w.dq_acc, ch * (uint64_t)d.G * (d.D + d.Dr) * 4);
+  carve(c, w.phase, 8 * 32 * 4);
   if (keyblock) {
     const uint64_t n = ch * E;
     if (kb_use_bins(d)) {

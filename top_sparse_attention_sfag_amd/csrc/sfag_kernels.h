@@ -22,6 +22,7 @@ struct RowArgs {
   int32_t n_split;   // k_row: workgroups per token (>1: dQ sums go to dq_acc)
   float* dq_acc;     // (ntok, G, 512 + Dr) fp32, zeroed, when n_split > 1
   int32_t reverse;   // k_sdp / k_dq: visit the chunk's tokens last to first
+  int32_t* phase;    // k_row16: per-XCD key-row hint (rotated walks), NULL: walk each token in order
 };
 
 constexpr int kKeyBlock = kKeyBlockRows;

@@ -87,6 +87,8 @@ void prof_drain() {
 // events, made on first use and kept for the life of the process: the
 // key-block pre-work runs on it beside k_sdp and k_dq beside the key-block
 // kernels, so that each fills the other's tail.
+// k_row16 walks start where its XCD's workgroups last were (non-deterministic calls)
+constexpr bool kRowRotate = true;
 enum SideEvent { kEvSdp = 0, kEvDq = 1, kEvDecode = 2, kEvPre = 3, kNumSideEvents = 4 };
 struct SideStream {
   hipStream_t s = nullptr;
@@ -354,6 +356,10 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
   ra.dq_mul = plan->scale / ds_scale;
   ra.n_split = 1;
   ra.dq_acc = nullptr;
+  // Without the deterministic guarantee the N1 <= 16 token kernel starts each
+  // token's walk where the workgroups of its XCD last were (the walk order
+  // only changes the order of dQ's sums).
+  ra.phase = !plan->deterministic && kRowRotate ? at<int32_t>(workspace, w.phase) : nullptr;
   // causal rows grow with the token: longest tokens first
   ra.reverse = d.mode == 3 ? 1 : 0;
   if (o.tokenOrder == SFAG_ORDER_ASCENDING) ra.reverse = 0;

@@ -42,6 +42,7 @@ struct WorkspaceLayout {
   uint64_t kb_grid = 0;    // int32 (2, nKB, chunk): per (key block, token) counts and visit flags, then their scans
   uint64_t kb_grid_tmp = 0;  // int32: segment sums of the grid scans
   uint64_t dq_acc = 0;     // fp32 (chunk, G, D + Dr): dQ|dQrope sums when a token's positions are split
+  uint64_t phase = 0;      // int32 (8 XCDs x 32): key row each XCD's token workgroups last reached (a hint)
   uint64_t total = 0;
 };
 

@@ -374,6 +374,7 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stg[2][2][kTile * 16];   // [buffer][P, dS][position][head]
   __shared__ int32_t keys_s[kTile];
   __shared__ float delta_s[16];
+  __shared__ int rot_s;
 
   // ---- work unit: token (and share of its positions), XCD-aware order ------
   const int b = blockIdx.x;
@@ -396,6 +397,32 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
     cb = min(nv, sp * per);
     ce = min(nv, cb + per);
   }
+  // The share's tiles, walked from tile `rot` on and wrapping.  With a phase
+  // hint (calls without the deterministic guarantee) the walk starts at the
+  // fraction of its tiles that the workgroups of this XCD last announced
+  // reaching: the token's rows ascend (the decode sorts them), so the
+  // workgroups that run together on the XCD, each starting where the others
+  // are, sweep the key rows together and share their gathers through the
+  // XCD's L2.  Any start is correct; only dQ's order of sums depends on it.
+  // (One thread reads the hint, which other workgroups rewrite at any time,
+  // and hands it to the others, so that every wave walks the same order.)
+  const int ntl = (ce - cb + kTile - 1) / kTile;
+  int rot = 0;
+  if (a.phase && ntl > 1) {
+    if (tid == 0) {
+      const uint32_t frac =
+          (uint32_t)__hip_atomic_load(a.phase + 32 * xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffffu;
+      rot_s = (int)((frac * (uint32_t)ntl) >> 16);
+    }
+    __syncthreads();
+    rot = __builtin_amdgcn_readfirstlane(rot_s);
+    if (rot >= ntl) rot = 0;
+  }
+  auto tile_at = [&](int L) -> int {   // first position of the L-th tile walked (L < ntl)
+    const int x = L + rot;
+    return cb + (x >= ntl ? x - ntl : x) * kTile;
+  };
+  constexpr int kAheadTiles = kAhead / kTile;   // tiles between a tile and its copies' issue
 
   // ---- prologue: operands, statistics, Delta ----------------------------
   V8 Bf[KS_QK > KS_V ? KS_QK : KS_V];      // Q (S waves) or dO (dP waves) of head n
@@ -442,7 +469,7 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
   // repeats its first valid position; its P and dS are 0)
   int32_t key0 = 0, key1 = 0;
   if (copier && cb < ce) {
-    const int c_0 = cb + (lane & 31), c_1 = cb + kTile + (lane & 31);
+    const int c_0 = tile_at(0) + (lane & 31), c_1 = (ntl > 1 ? tile_at(1) : cb) + (lane & 31);
     key0 = rt[c_0 < ce ? c_0 : cb];
     key1 = rt[c_1 < ce ? c_1 : cb];
   }
@@ -512,11 +539,12 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
 
   if (copier && cb < ce) {
     issue(key0, 0);
-    if (!kSingle && cb + kTile < ce) issue(key1, 1);
+    if (!kSingle && ntl > 1) issue(key1, 1);
   }
   int cur = 0, it = 0;
-  for (int c0 = cb; c0 < ce; c0 += kTile, cur ^= (kSingle ? 0 : 1), ++it) {
-    const bool more = c0 + kTile < ce;
+  for (int L = 0; L < ntl; ++L, cur ^= (kSingle ? 0 : 1), ++it) {
+    const int c0 = tile_at(L);
+    const bool more = L + 1 < ntl;
     if (copier) {
       if (more && !kSingle) wait_one_tile();
       else __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
@@ -528,9 +556,17 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
     // wave 3: row indices of the tile whose copies go out at the end of this
     // one (the next with one buffer, the one after with two), into LDS for
     // the copiers
-    if (wave == 3 && c0 + kAhead < ce && lane < kTile) {
-      const int c = c0 + kAhead + lane;
-      keys_s[lane] = rt[c < ce ? c : cb];
+    if (wave == 3 && L + kAheadTiles < ntl && lane < kTile) {
+      const int c = tile_at(L + kAheadTiles) + lane;
+      const int32_t kv = rt[c < ce ? c : cb];
+      keys_s[lane] = kv;
+      // (announce the fraction of the walk reached, for the workgroups that
+      // start next)
+      if (a.phase && lane == 0) {
+        const int x = (c - lane - cb) / kTile;
+        __hip_atomic_store(a.phase + 32 * xcd, (int32_t)(((uint32_t)x << 16) / (uint32_t)ntl), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     // ---- Sᵀ (waves 0, 1) or dPᵀ (waves 2, 3) of positions 16 mb .. +15
     f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -599,7 +635,7 @@ __global__ void __launch_bounds__(256, 2) k_row16(RowArgs a) {
     __syncthreads();
     // every wave is done with this buffer: the copies of the next tile (one
     // buffer) or the one after (two)
-    if (copier && c0 + kAhead < ce) {
+    if (copier && L + kAheadTiles < ntl) {
       const int32_t keyv = keys_s[lane & 31];
       issue(keyv, cur);
     }

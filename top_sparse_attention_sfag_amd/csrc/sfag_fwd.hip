@@ -7,8 +7,9 @@
 //     out[h] = Σ_p exp(z − max) / softmaxSum · V[p]
 // A token without a valid position gets max = −inf, sum = 0 and out = 0.
 //
-// gfx950 mapping (the same tiles as the N1 <= 16 backward kernel): one
-// workgroup per (token, 64-head block), 4 waves of 16 heads.  Per tile of 32
+// gfx950 mapping, k_fwd (up to 32 heads; the same tiles as the N1 <= 16
+// backward kernel): one workgroup per (token, 64-head block), 4 waves of 16
+// heads (k_fwd8 below takes 64-head blocks with 8 waves).  Per tile of 32
 // gathered positions, Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32 (positions as M, the
 // wave's Q rows resident in registers), an online softmax per head (running
 // max and sum; the fp32 output accumulators are rescaled when the max
@@ -30,6 +31,7 @@ typedef __attribute__((address_space(3))) void lvoid;
 constexpr int kTile = 32;   // positions per tile
 constexpr int kXcds = 8;    // blockIdx % 8 picks the XCD
 constexpr int kRun = 16;    // consecutive tokens per XCD run
+constexpr bool kFwd8 = true;   // 64-head blocks (N1 > 32) as 8 waves (k_fwd8)
 
 // Asynchronous global -> LDS copy of 16 bytes per lane (lane l writes at the
 // wave-uniform LDS address l_base + 16 l).  Inline asm on purpose: the
@@ -237,17 +239,242 @@ __global__ void __launch_bounds__(256, 1) k_fwd(FwdArgs a) {
   }
 }
 
+// k_fwd8: the same output for a 64-head block as 8 waves, two per SIMD, so
+// that one wave's MFMAs run while the other waits.  Wave w = 4 ph + hg forms
+// Sᵀ of head group hg (16 heads, Q in registers) over the position half ph
+// of each 32-position tile; the two halves' maxima meet in LDS, each wave
+// turns its half into P (bf16, into LDS as (head, position) rows) with the
+// tile's common running max, and every wave then adds P·V into its own 64
+// output columns for all 64 heads (64 fp32 accumulators a lane instead of
+// 128, which is what leaves room for a second wave).  The per-head rescale
+// factors and the final sums pass through LDS as well.
+template <typename TT, int DR, bool VK>
+__global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
+  constexpr int DQK = 512 + DR;
+  constexpr int KS_QK = DQK / 32;
+  constexpr int KM_BYTES = kTile * 1024;
+  constexpr int KR_BYTES = kTile * DR * 2;
+  constexpr int V_BYTES = VK ? 0 : kTile * 1024;
+  constexpr int BUF = KM_BYTES + KR_BYTES + V_BYTES;
+  constexpr int PST = 72;   // bytes per head row of P (32 positions + 8: conflict-free A reads)
+  typedef typename TT::vec8 V8;
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char ps[64 * PST];
+  __shared__ float xmax[2][64];   // per position half: the tile's max of each head
+  __shared__ __attribute__((aligned(16))) float alpha_s[64];
+  __shared__ float lsum[2][64];
+  __shared__ __attribute__((aligned(16))) float inv_s[64];
+
+  const int b = blockIdx.x;
+  const int xcd = b % kXcds, u = b / kXcds;
+  const int hb = u % a.n_hb;
+  const int tq = u / a.n_hb;
+  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  if (tl >= a.ntok) return;
+  const int64_t t = a.t0 + tl;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
+  const int hg = wave & 3, ph = wave >> 2;
+  const int hl = hg * 16 + n;              // head of this lane within the block (Sᵀ column)
+  const int h = hb * 64 + hl;
+  const bool hv = h < a.G;
+
+  V8 Qf[KS_QK];
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (hv) {
+      if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
+      else v = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
+    }
+    Qf[ks] = as_vec8<V8>(v);
+  }
+  // output accumulators: head block j (heads 16 j + 4 g + i), column block c
+  // (columns 64 wave + 16 c + n)
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.f;   // head hl; l_run: this lane's share of this half
+
+  const int nv = a.nvalid[tl];
+  const int32_t* rt = a.rows + tl * a.E;
+
+  // Gather of the 32 rows of a tile into buffer `buf` (rows past nv repeat a
+  // valid row, masked out of the softmax) in five steps per wave: step j < 4
+  // copies K (and V) row 4w + j, step 4 (w < 4) rope rows 8w .. 8w + 7.
+  // key_l: lane r & 31 holds the key row of the tile's position r.
+  auto tile_key = [&](int c0) -> int {
+    const int cl = c0 + (lane & 31);
+    return rt[cl < nv ? cl : 0];
+  };
+  auto issue_step = [&](int j, int key_l, int buf) {
+    unsigned char* base = smem + buf * BUF;
+    if (j < 4) {
+      const int r = wave * 4 + j;
+      const int64_t key = __builtin_amdgcn_readfirstlane(__shfl(key_l, r, 64));
+      const int gc = lane ^ (r & 7);
+      lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
+      if (!VK) lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
+    } else if (DR > 0 && wave < 4) {
+      const int r_l = wave * 8 + (lane >> 3);
+      const int key_r = __shfl(key_l, r_l, 64);
+      const int gc = (lane & 7) ^ (r_l & 7);
+      lds_load16(a.kr + (int64_t)key_r * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
+    }
+  };
+
+  // Sᵀ operand offsets (rows ph·16 + n, see k_fwd) and the transposed V reads
+  const int x = n & 7;
+  const int oA_even = n * 1024 + 16 * (g ^ x) + ph * 16384;
+  const int oA_odd = n * 1024 + 16 * ((4 + g) ^ x) + ph * 16384;
+  const int oR_even = n * (DR * 2) + 16 * (g ^ x) + ph * 16 * (DR * 2);
+  const int oR_odd = n * (DR * 2) + 16 * ((4 + g) ^ x) + ph * 16 * (DR * 2);
+  const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;
+  const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
+  int oT[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) oT[c] = r1 * 1024 + 16 * ((2 * c + half) ^ x1) + hoff + 128 * wave;
+
+  if (nv > 0) {
+    const int k0 = tile_key(0);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) issue_step(j, k0, 0);
+  }
+  int cur = 0;
+  for (int c0 = 0; c0 < nv; c0 += kTile) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // the next tile's copies, at once (spread between the Sᵀ MFMAs instead:
+    // config 2 forward 3.77 -> 4.26 ms)
+    if (c0 + kTile < nv) {
+      const int key_n = tile_key(c0 + kTile);
+#pragma unroll
+      for (int j = 0; j < 5; ++j) issue_step(j, key_n, cur ^ 1);
+    }
+    const unsigned char* Km = smem + cur * BUF;
+    const unsigned char* Kr = Km + KM_BYTES;
+    const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
+    // ---- Sᵀ of positions ph·16 + 4g + i, head hl
+    auto kaddr = [&](int ks) -> const unsigned char* {
+      if (ks < 16) return Km + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1);
+      return Kr + ((ks & 1) ? oR_odd : oR_even);
+    };
+    f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 kb4[4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) kb4[i] = *(const uint4*)kaddr(i);
+#pragma unroll
+    for (int ks = 0; ks < KS_QK; ++ks) {
+      if (ks + 3 < KS_QK) kb4[(ks + 3) & 3] = *(const uint4*)kaddr(ks + 3);
+      sv = TT::mfma(as_vec8<V8>(kb4[ks & 3]), Qf[ks], sv);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float z[4];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = c0 + ph * 16 + 4 * g + i < nv ? sv[i] * a.scale : -__builtin_inff();
+      tmax = fmaxf(tmax, z[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if (g == 0) xmax[ph][hl] = tmax;
+    __syncthreads();
+    // ---- P with the tile's common running max (finite: the tile holds a
+    // valid position)
+    const float m_new = fmaxf(m_run, fmaxf(xmax[0][hl], xmax[1][hl]));
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
+    float psum = 0.f;
+    uint16_t pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f((z[i] - m_new) * kLog2e);
+      psum += p;
+      pv[i] = TT::from_f(p);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    *(uint2*)(ps + hl * PST + 32 * ph + 8 * g) =
+        make_uint2(pv[0] | ((uint32_t)pv[1] << 16), pv[2] | ((uint32_t)pv[3] << 16));
+    if (ph == 0 && g == 0) alpha_s[hl] = alpha;
+    __syncthreads();
+    // ---- out += P·V over this wave's 64 columns, all 64 heads
+    V8 A8[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned char* pr = ps + (16 * j + n) * PST + 8 * g;
+      const uint2 lo = *(const uint2*)pr, hi = *(const uint2*)(pr + 32);
+      A8[j] = as_vec8<V8>(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const float4 al = *(const float4*)(alpha_s + 16 * j + 4 * g);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[j][c][0] *= al.x;
+        acc[j][c][1] *= al.y;
+        acc[j][c][2] *= al.z;
+        acc[j][c][3] *= al.w;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const unsigned char* p1 = Vm + oT[c];
+      const V8 B8 = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 1024)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j][c] = TT::mfma(A8[j], B8, acc[j][c]);
+    }
+    cur ^= 1;
+  }
+  // ---- statistics and out
+  float l_half = l_run + __shfl_xor(l_run, 16);
+  l_half += __shfl_xor(l_half, 32);
+  __syncthreads();
+  if (g == 0) lsum[ph][hl] = l_half;
+  __syncthreads();
+  if (ph == 0 && g == 0) {
+    const float l_tot = lsum[0][hl] + lsum[1][hl];
+    inv_s[hl] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (hv) {
+      a.smax[t * a.G + h] = m_run;
+      a.ssum[t * a.G + h] = l_tot;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 iv = *(const float4*)(inv_s + 16 * j + 4 * g);
+    const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = hb * 64 + 16 * j + 4 * g + i;
+      if (hh < a.G) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          a.out[(t * a.G + hh) * 512 + 64 * wave + 16 * c + n] = TT::from_f(acc[j][c][i] * ivs[i]);
+      }
+    }
+  }
+}
+
 void launch_fwd(int32_t dtype, bool rope, const FwdArgs& a, hipStream_t s) {
   if (a.ntok == 0) return;
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a.ntok + per - 1) / per * per;
-  const dim3 grid((unsigned)(padded * a.n_hb)), block(256);
+  const dim3 grid((unsigned)(padded * a.n_hb));
   const bool vk = a.v == a.k;   // value passed as the key tensor: gather each row once
+  const bool eight = kFwd8 && a.Gp >= 64;
   auto go = [&](auto tt, auto dr) {
     typedef decltype(tt) T;
     constexpr int D = decltype(dr)::value;
-    if (vk) hipLaunchKernelGGL((k_fwd<T, D, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_fwd<T, D, false>), grid, block, 0, s, a);
+    if (eight) {
+      if (vk) hipLaunchKernelGGL((k_fwd8<T, D, true>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((k_fwd8<T, D, false>), grid, dim3(512), 0, s, a);
+    } else {
+      if (vk) hipLaunchKernelGGL((k_fwd<T, D, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_fwd<T, D, false>), grid, dim3(256), 0, s, a);
+    }
   };
   if (dtype == SFAG_BF16) {
     if (rope) go(BF16(), std::integral_constant<int, 64>());

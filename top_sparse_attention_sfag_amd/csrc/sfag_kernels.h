@@ -107,8 +107,18 @@ void launch_scan_i32(int32_t* a, int64_t n, int32_t* tmp, hipStream_t s);
 void launch_kb_bins(const int32_t* rows, const int32_t* nvalid, int64_t E, int32_t nkb, int64_t ntok, int32_t* cnt,
                     int32_t* flg, int32_t* scan_tmp, int32_t* svals, int32_t* er, int32_t* vis_start, int32_t* vis_key,
                     int32_t* n_vis, hipStream_t s);
+// The outputs of the last chunk's range reduction: dKey|dKeyRope (scaled by
+// kscale) and dValue in the input dtype, columns [0, D), [D, D + Dr) and
+// [D + Dr, AW) of the accumulators.
+struct KbOut {
+  int32_t dtype, D, Dr;
+  float kscale;
+  void *dk, *dkr, *dv;
+};
+// acc[row] = (first ? 0 : acc[row]) + the non-empty ranges' partials in
+// ascending range order; with `out` the sums go to the outputs instead.
 void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
-                      float* acc, hipStream_t s);
+                      float* acc, bool first, const KbOut* out, hipStream_t s);
 void launch_col(int32_t dtype, bool rope, bool partial, const ColArgs& a, hipStream_t s);
 
 }  // namespace sfag

@@ -1084,13 +1084,19 @@ void launch_kb_bins(const int32_t* rows, const int32_t* nvalid, int64_t E, int32
 
 // acc[row] += Σ_tr part[tr][row] over the token ranges whose (range, key
 // block) was non-empty, in ascending range order.
+// (first: the sum starts from 0 rather than acc, which the zero fill made the
+// same bits; OUT: the last chunk's sums go straight to the outputs, rounded
+// as k_cast rounds them, four columns at a time: D and Dr are multiples of 4)
+template <typename TT, bool OUT>
 __global__ void __launch_bounds__(256) k_kb_reduce(const float* __restrict__ part, const int32_t* __restrict__ nonempty,
                                                    int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
-                                                   float* __restrict__ acc) {
+                                                   float* __restrict__ acc, int32_t first, int32_t D, int32_t Dr,
+                                                   float kscale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dkr,
+                                                   uint16_t* __restrict__ dv) {
   const int64_t row = blockIdx.x;
   const int kb = (int)(row / kKB);
   for (int64_t col = threadIdx.x * 4; col < AW; col += 256 * 4) {
-    float4 s = *(const float4*)(acc + row * AW + col);
+    float4 s = first ? make_float4(0.f, 0.f, 0.f, 0.f) : *(const float4*)(acc + row * AW + col);
     for (int tr = 0; tr < nTR; ++tr) {
       if (!nonempty[(int64_t)tr * nKB + kb]) continue;
       const float4 v = *(const float4*)(part + ((int64_t)tr * T2 + row) * AW + col);
@@ -1099,7 +1105,21 @@ __global__ void __launch_bounds__(256) k_kb_reduce(const float* __restrict__ par
       s.z += v.z;
       s.w += v.w;
     }
-    *(float4*)(acc + row * AW + col) = s;
+    if constexpr (OUT) {
+      const int c = (int)col;
+      uint16_t* dst;
+      float m = kscale;
+      if (c < D) dst = dk + row * D + c;
+      else if (c < D + Dr) dst = dkr + row * Dr + (c - D);
+      else {
+        dst = dv + row * D + (c - D - Dr);
+        m = 1.f;
+      }
+      *(uint2*)dst = make_uint2((uint32_t)TT::from_f(s.x * m) | ((uint32_t)TT::from_f(s.y * m) << 16),
+                                (uint32_t)TT::from_f(s.z * m) | ((uint32_t)TT::from_f(s.w * m) << 16));
+    } else {
+      *(float4*)(acc + row * AW + col) = s;
+    }
   }
 }
 
@@ -1131,9 +1151,21 @@ void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows,
 }
 
 void launch_kb_reduce(const float* part, const int32_t* nonempty, int64_t T2, int64_t AW, int32_t nTR, int32_t nKB,
-                      float* acc, hipStream_t s) {
+                      float* acc, bool first, const KbOut* out, hipStream_t s) {
   if (T2 == 0) return;
-  hipLaunchKernelGGL(k_kb_reduce, dim3((unsigned)T2), dim3(256), 0, s, part, nonempty, T2, AW, nTR, nKB, acc);
+  const dim3 grid((unsigned)T2), block(256);
+  const int32_t f = first ? 1 : 0;
+  if (!out) {
+    hipLaunchKernelGGL((k_kb_reduce<BF16, false>), grid, block, 0, s, part, nonempty, T2, AW, nTR, nKB, acc, f, 0, 0,
+                       1.f, nullptr, nullptr, nullptr);
+    return;
+  }
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, part, nonempty, T2, AW, nTR, nKB, acc, f, out->D, out->Dr,
+                       out->kscale, (uint16_t*)out->dk, (uint16_t*)out->dkr, (uint16_t*)out->dv);
+  };
+  if (out->dtype == SFAG_BF16) go(k_kb_reduce<BF16, true>);
+  else go(k_kb_reduce<FP16, true>);
 }
 
 }  // namespace sfag

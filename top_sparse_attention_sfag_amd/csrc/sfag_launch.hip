@@ -319,7 +319,11 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
     TimedScope ts("delta", s);
     launch_delta(plan->dtype, plan->dout, plan->out, delta, d.T1 * d.G, s);
   }
-  {
+  // On the key-block path with positions the range reduction of every chunk
+  // covers every key row: the first chunk's writes the accumulators (no
+  // zero fill) and the last chunk's writes dKey|dKeyRope|dValue (no cast).
+  const bool reduce_out = plan->scatter == kScatterKeyBlock && d.E > 0;
+  if (!reduce_out) {
     TimedScope ts("fill", s);
     launch_fill_u32(acc, (uint64_t)d.T2 * d.AW, 0u, s);
   }
@@ -545,7 +549,9 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
         }
         {
           TimedScope ts("kb_reduce", s);
-          launch_kb_reduce(ka.part, ka.nonempty, d.T2, d.AW, ka.nTR, ka.nKB, acc, s);
+          KbOut ko{plan->dtype, (int32_t)d.D, (int32_t)d.Dr, plan->scale / ds_scale, plan->dk, plan->dkr, plan->dv};
+          launch_kb_reduce(ka.part, ka.nonempty, d.T2, d.AW, ka.nTR, ka.nKB, acc, t0 == 0,
+                           t0 + ntok >= d.T1 ? &ko : nullptr, s);
         }
       }
     } else if (!keyblock) {
@@ -568,7 +574,7 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
     const int rc = check_launch("chunk kernels");
     if (rc != SFAG_OK) return rc;
   }
-  {
+  if (!reduce_out) {
     TimedScope ts("cast", s);
     launch_cast(plan->dtype, acc, d.T2, (int32_t)d.D, (int32_t)d.Dr, plan->scale / ds_scale, plan->dk, plan->dkr,
                 plan->dv, s);

@@ -75,6 +75,9 @@ __device__ __forceinline__ f32x16 mfma32<FP16>(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 64-head blocks in the 4-wave form of k_sdp8 (else k_sdp with 2 waves of 32)
+constexpr bool kSdp16x4 = true;
+
 // Maps a block index to (token of the chunk, head block): each XCD takes runs
 // of kRun consecutive tokens.
 // With `reverse` the last tokens of the chunk come first (under the causal
@@ -438,21 +441,29 @@ __global__ void __launch_bounds__(256, 1) k_sdp(RowArgs a) {
 // blocks); lane (g, n) then holds heads 4g .. 4g + 3 of the wave at position
 // n of each block.  Every wave reads the whole tile from LDS, twice the LDS
 // traffic of 32-head waves.
+//
+// NW = 4 takes a block of 64 heads the same way (4 waves of 16) with one
+// tile buffer, so that two workgroups share a CU (two waves per SIMD again):
+// the next tile's copies go out once every wave has read the buffer, and the
+// other workgroup's work covers their latency.
 // ---------------------------------------------------------------------------
-template <typename TT, int DR, bool VK>
-__global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
+template <typename TT, int DR, bool VK, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int KS_QK = DQK / 32;   // k-steps of 32 along D+Dr (rope last)
   constexpr int KS_V = 512 / 32;
   constexpr int KM_BYTES = kTile * 1024;
   constexpr int KR_BYTES = kTile * DR * 2;
   constexpr int BUF = KM_BYTES + KR_BYTES + (VK ? 0 : kTile * 1024);
+  constexpr bool kOne = NW == 4;        // one tile buffer
+  constexpr int SRB = 32 * NW;          // bytes of a staged (tensor, position) row: 16 NW heads
+  constexpr int SCM = 2 * NW - 1;       // chunk swizzle mask of the staged rows
   typedef typename TT::vec8 V8;
   __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF];
-  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF];
-  // P and dS of a tile as (tensor, position) rows of 128 heads (256 bytes);
-  // 16-byte chunk j of row r sits at chunk j ^ (r & 15)
-  __shared__ __attribute__((aligned(16))) unsigned char stg[2 * kTile * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[kOne ? 16 : BUF];
+  // P and dS of a tile as (tensor, position) rows of the block's heads
+  // (SRB bytes); 16-byte chunk j of row r sits at chunk j ^ (r & SCM)
+  __shared__ __attribute__((aligned(16))) unsigned char stg[2 * kTile * SRB];
 
   int hb;
   const int64_t tl = unit_token(blockIdx.x, 1, hb, a.ntok, a.reverse);
@@ -518,13 +529,13 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
   int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
 
   // The gather of a tile as a fixed list of copy instructions per wave: K
-  // (and V) rows wave + 8j, then rope group `wave` (waves 0..3, 8 rows each).
+  // (and V) rows wave + NW j, then rope group `wave` (waves 0..3, 8 rows each).
   constexpr int kPerRow = VK ? 1 : 2;
-  constexpr int kRowOps = kPerRow * (kTile / 8);
+  constexpr int kRowOps = kPerRow * (kTile / NW);
   constexpr int kOps = kRowOps + (DR > 0 ? 1 : 0);
   auto issue_op = [&](int i, int32_t keyv, uint32_t base) {
     if (i < kRowOps) {
-      const int r = wave + 8 * (i / kPerRow);
+      const int r = wave + NW * (i / kPerRow);
       const int64_t key = __builtin_amdgcn_readlane(keyv, r);
       const int gc = lane ^ (r & 15);
       if (!VK && (i & 1)) lds_load16_at(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
@@ -536,16 +547,21 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
       lds_load16_at(a.kr + key * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
     }
   };
-  // staged rows stored by this wave: tensor wave / 4, rows
-  // 8 (wave % 4) + 4 q + lane / 16 (q = 0, 1), chunk lane % 16
+  // staged rows stored by this wave: tensor wave / (NW / 2), rows
+  // 8 (wave % (NW / 2)) + SR q + lane / (2 NW) (q = 0, 1; SR = 32 / NW rows
+  // per instruction), chunk lane % (2 NW)
   int stg_c0 = -1;
-  const int srow0 = 8 * (wave & 3) + (lane >> 4), sj = lane & 15, sten = wave >> 2;
+  constexpr int SR = 32 / NW;
+  const int sten = wave / (NW / 2);
+  const int srow0 = 8 * (wave % (NW / 2)) * (8 / NW) + lane / (2 * NW), sj = lane % (2 * NW);
   auto stage_out = [&]() {
-    const uint4 v0 = *(const uint4*)(stg + (sten * kTile + srow0) * 256 + ((sj ^ (srow0 & 15)) << 4));
-    const uint4 v1 = *(const uint4*)(stg + (sten * kTile + srow0 + 4) * 256 + ((sj ^ ((srow0 + 4) & 15)) << 4));
-    uint16_t* out = (sten ? a.ds_out : a.p_out) + (tl * a.E + stg_c0 + srow0) * a.Gp + sj * 8;
-    if (stg_c0 + srow0 < nv) *(uint4*)out = v0;
-    if (stg_c0 + srow0 + 4 < nv) *(uint4*)(out + 4 * a.Gp) = v1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = srow0 + SR * q;
+      const uint4 v = *(const uint4*)(stg + (sten * kTile + r) * SRB + ((sj ^ (r & SCM)) << 4));
+      uint16_t* out = (sten ? a.ds_out : a.p_out) + (tl * a.E + stg_c0 + r) * a.Gp + sj * 8;
+      if (stg_c0 + r < nv) *(uint4*)out = v;
+    }
   };
   // LDS offsets of this lane's B-operand reads: row 16 nb + n, chunk
   // 4 ks + g (K|V rows, swizzle r & 15) or 4 ks' + g (rope rows, (r >> 1) & 7)
@@ -589,8 +605,8 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
     for (int ks = 0; ks < KS_V; ++ks) {
       if (!LA) rd(ks, 0);
       else if (ks + 1 < KS_V) rd(ks + 1, (ks + 1) & LA);
-      // the next tile's copies over the first 8 k-steps
-      if (more && ks < 8)
+      // the next tile's copies over the first 8 k-steps (two buffers)
+      if (!kOne && more && ks < 8)
 #pragma unroll
         for (int i = ks * kOps / 8; i < (ks + 1) * kOps / 8; ++i) issue_op(i, keys, nxt_l);
 #pragma unroll
@@ -600,7 +616,7 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
+    if (!kOne) keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
     if constexpr (DR > 0) {
       uint4 bv[KS_QK - KS_V][2];
 #pragma unroll
@@ -628,13 +644,19 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
       wp[nb] = make_uint2(pack2<TT>(pv[0], pv[1]), pack2<TT>(pv[2], pv[3]));
       wd[nb] = make_uint2(pack2<TT>(dv[0], dv[1]), pack2<TT>(dv[2], dv[3]));
     }
-    bar();   // every wave has read the previous staged tile back
+    bar();   // every wave has read the previous staged tile back (and, with one
+             // buffer, is done with this tile's operands)
+    if (kOne && more) {
+#pragma unroll
+      for (int i = 0; i < kOps; ++i) issue_op(i, keys, nxt_l);
+      keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
+    }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int r = 16 * nb + n;
-      const int o = r * 256 + (((2 * wave + (g >> 1)) ^ (r & 15)) << 4) + ((g & 1) << 3);
+      const int o = r * SRB + (((2 * wave + (g >> 1)) ^ (r & SCM)) << 4) + ((g & 1) << 3);
       *(uint2*)(stg + o) = wp[nb];
-      *(uint2*)(stg + kTile * 256 + o) = wd[nb];
+      *(uint2*)(stg + kTile * SRB + o) = wd[nb];
     }
     stg_c0 = c0;
   };
@@ -645,9 +667,13 @@ __global__ void __launch_bounds__(512, 1) k_sdp8(RowArgs a) {
     for (int i = 0; i < kOps; ++i) issue_op(i, keys, b0);
   }
   keys = tile_keys(rt, nv, kTile, lane);
-  for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
-    tile(c0, buf0, buf1);
-    if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+  if constexpr (kOne) {
+    for (int c0 = 0; c0 < nv; c0 += kTile) tile(c0, buf0, buf0);
+  } else {
+    for (int c0 = 0; c0 < nv; c0 += 2 * kTile) {
+      tile(c0, buf0, buf1);
+      if (c0 + kTile < nv) tile(c0 + kTile, buf1, buf0);
+    }
   }
   __syncthreads();
   if (stg_c0 >= 0) stage_out();
@@ -801,17 +827,28 @@ void launch_sdp(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a_in.ntok + per - 1) / per * per;
   RowArgs a = a_in;
-  // 128 heads: k_sdp8 (8 waves of 16 heads)
-  if (a.Gp == 128) {
+  // 128 heads: k_sdp8 (8 waves of 16 heads); 64: its 4-wave form
+  if (a.Gp == 128 || (kSdp16x4 && a.Gp == 64)) {
     a.n_hb = 1;
     const bool vk8 = a.v == a.k;
-    auto go8 = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)padded), dim3(512), 0, s, a); };
+    const bool w8 = a.Gp == 128;
+    auto go8 = [&](auto tt, auto dr, auto vk) {
+      typedef decltype(tt) T;
+      constexpr int D = decltype(dr)::value;
+      constexpr bool V = decltype(vk)::value;
+      if (w8) hipLaunchKernelGGL((k_sdp8<T, D, V, 8>), dim3((unsigned)padded), dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((k_sdp8<T, D, V, 4>), dim3((unsigned)padded), dim3(256), 0, s, a);
+    };
+    auto by_vk = [&](auto tt, auto dr) {
+      if (vk8) go8(tt, dr, std::true_type());
+      else go8(tt, dr, std::false_type());
+    };
     if (dtype == SFAG_BF16) {
-      if (rope) vk8 ? go8(k_sdp8<BF16, 64, true>) : go8(k_sdp8<BF16, 64, false>);
-      else vk8 ? go8(k_sdp8<BF16, 0, true>) : go8(k_sdp8<BF16, 0, false>);
+      if (rope) by_vk(BF16(), std::integral_constant<int, 64>());
+      else by_vk(BF16(), std::integral_constant<int, 0>());
     } else {
-      if (rope) vk8 ? go8(k_sdp8<FP16, 64, true>) : go8(k_sdp8<FP16, 64, false>);
-      else vk8 ? go8(k_sdp8<FP16, 0, true>) : go8(k_sdp8<FP16, 0, false>);
+      if (rope) by_vk(FP16(), std::integral_constant<int, 64>());
+      else by_vk(FP16(), std::integral_constant<int, 0>());
     }
     return;
   }

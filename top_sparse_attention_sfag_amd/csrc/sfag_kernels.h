@@ -96,7 +96,8 @@ void launch_cast(int32_t dtype, const float* acc, int64_t T2, int32_t D, int32_t
 void launch_row(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
 // N1 >= 32: the S/P/dP/dS kernel, then the dQ kernel (together they replace launch_row)
 void launch_sdp(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
-void launch_dq(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s);
+// beside: k_dq runs on the second stream beside the key-block kernels
+void launch_dq(int32_t dtype, bool rope, const RowArgs& a, hipStream_t s, bool beside);
 void launch_keyblock(int32_t dtype, const KbArgs& a, hipStream_t s);
 void launch_visits(const int32_t* ck, const int32_t* svals, const int32_t* rows, int64_t n, int64_t ntok,
                    int32_t nkb, int32_t* flags, int32_t* scan_tmp, int32_t* vis_start, int32_t* vis_key, int32_t* er,

@@ -485,13 +485,13 @@ int run_backward(void* workspace, uint64_t workspaceSize, sfag_plan* plan, void*
         if (!order(s, side->s, kEvSdp)) return fail(SFAG_ERR_RUNTIME, "fork to the second stream failed");
         {
           TimedScope ts("dq", side->s);
-          launch_dq(plan->dtype, rope, ra, side->s);
+          launch_dq(plan->dtype, rope, ra, side->s, true);
         }
         if (hipEventRecord(side->ev[kEvDq], side->s) != hipSuccess)
           return fail(SFAG_ERR_RUNTIME, "second stream event failed");
       } else {
         TimedScope ts("dq", s);
-        launch_dq(plan->dtype, rope, ra, s);
+        launch_dq(plan->dtype, rope, ra, s, false);
       }
     } else if (d.row_split > 1) {
       // a token's positions over row_split workgroups: fp32 dQ sums, then a cast

@@ -77,6 +77,9 @@ __device__ __forceinline__ f32x16 mfma32<FP16>(f16x8 a, f16x8 b, f32x16 c) {
 
 // 64-head blocks in the 4-wave form of k_sdp8 (else k_sdp with 2 waves of 32)
 constexpr bool kSdp16x4 = true;
+// at most 64 heads on the caller's stream: k_dq as 4 waves (else 8 waves,
+// half of them on zero dS)
+constexpr bool kDq64x4 = true;
 
 // Maps a block index to (token of the chunk, head block): each XCD takes runs
 // of kRun consecutive tokens.
@@ -684,13 +687,16 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
 // 64 (w / 4) .. +64 of the block and the 16-column blocks w % 4, w % 4 + 4,
 // ... of dQ|dQrope (blocks 32..35 are the rope columns).
 // ---------------------------------------------------------------------------
-template <typename TT, int DR>
-__global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
+template <typename TT, int DR, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) k_dq(RowArgs a) {
   constexpr int DQK = 512 + DR;
   constexpr int NB = DQK / 64;             // column blocks per wave
   constexpr int KM_BYTES = kTile * 1024;
   constexpr int KR_BYTES = kTile * DR * 2;
-  constexpr int DS_BYTES = kTile * 256;     // 32 positions x 128 heads, 16-bit
+  constexpr int HBW = 16 * NW;             // heads per block: 128 (8 waves) or 64 (4 waves)
+  constexpr int DSR = 2 * HBW;             // bytes of a dS row
+  constexpr int DCM = 2 * NW - 1;          // chunk swizzle mask of the dS rows
+  constexpr int DS_BYTES = kTile * DSR;    // 32 positions x the block's heads, 16-bit
   constexpr int BUF = KM_BYTES + KR_BYTES + DS_BYTES;
   typedef typename TT::vec8 V8;
 
@@ -703,7 +709,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
   const int64_t t = a.t0 + tl;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int hw = wave >> 2, wq = wave & 3;    // head half, column group
-  const int hmax = (int)(a.Gp - hb * 128);    // heads of this block present in the dS rows
+  const int hmax = (int)(a.Gp - hb * HBW);    // heads of this block present in the dS rows
   const int nv = a.nvalid[tl];
   const int32_t* rt = a.rows + tl * a.E;
 
@@ -713,23 +719,22 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // dS rows of the tile (128 heads = 256 bytes each), 4 rows per
-  // instruction: the lane writing position p of row r fetches chunk
-  // p ^ (r & 15); chunks of rows past nv or of heads past the block are
-  // zero-filled instead.
+  // dS rows of the tile (DSR bytes each), 32 / NW rows per instruction: the
+  // lane writing position p of row r fetches chunk p ^ (r & DCM); chunks of
+  // rows past nv or of heads past the block are zero-filled instead.
   int32_t keys = tile_keys(rt, nv, 0, lane);   // row indices of the next tile to gather
   auto issue_tile = [&](int c0, unsigned char* base) {
     unsigned char* dsb = base + KM_BYTES + KR_BYTES;
-    const int r = wave * 4 + (lane >> 4);
+    const int r = wave * (32 / NW) + lane / (2 * NW), cq = lane % (2 * NW);
     const int c = c0 + r;
-    const int q = n ^ (r & 15);
+    const int q = cq ^ (r & DCM);
     const bool live = c < nv && q * 8 < hmax;
     // Zero fill before any asynchronous copy is issued, so that no plain LDS
     // store follows an asynchronous one into the same buffer.
-    if (!live) *(uint4*)(dsb + r * 256 + n * 16) = make_uint4(0, 0, 0, 0);
-    issue_rows<DR, false, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, 8, lane);
+    if (!live) *(uint4*)(dsb + r * DSR + cq * 16) = make_uint4(0, 0, 0, 0);
+    issue_rows<DR, false, false>(a.k, a.kr, nullptr, keys, base, KM_BYTES, KR_BYTES, wave, NW, lane);
     keys = tile_keys(rt, nv, c0 + kTile, lane);
-    if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * 128 + q * 8, dsb + wave * 1024);
+    if (live) lds_load16(a.ds_out + (tl * a.E + c) * a.Gp + hb * HBW + q * 8, dsb + wave * 1024);
   };
 
   // Transposed-read offsets (see lds_read_tr): K rows 4g+(n>>2) and +16, dS
@@ -745,7 +750,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
   // dS: heads 64hw + 16s + 4(n & 3) .. +4 sit in chunk 8hw + 2s + half
   int offD[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) offD[s] = r1 * 256 + (((8 * hw + 2 * s + half) ^ (r1 & 15)) << 4) + hoff;
+  for (int s = 0; s < 4; ++s) offD[s] = r1 * DSR + (((8 * hw + 2 * s + half) ^ (r1 & DCM)) << 4) + hoff;
 
   auto tile = [&](int c0, int cend, const unsigned char* Km, unsigned char* nxt) {
     // (the previous tile's MFMAs stay above this wait: the wait stalls issue)
@@ -760,7 +765,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const unsigned char* p1 = Ds + offD[s];
-      A[s] = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 256)));
+      A[s] = join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * DSR)));
     }
 #pragma unroll
     for (int nb0 = 0; nb0 < NB; nb0 += 3) {
@@ -811,7 +816,7 @@ __global__ void __launch_bounds__(512, 1) k_dq(RowArgs a) {
       const int col = 16 * (wq + 4 * nb) + n;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int hh = hb * 128 + hw * 64 + 16 * s + 4 * g + i;
+        const int hh = hb * HBW + hw * 64 + 16 * s + 4 * g + i;
         if (hh < a.G) {
           const uint16_t v = TT::from_f(acc[s][nb][i] * a.dq_mul);
           if (col < 512) a.dq[(t * a.G + hh) * 512 + col] = v;
@@ -886,20 +891,29 @@ void launch_sdp(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
   }
 }
 
-void launch_dq(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s) {
+void launch_dq(int32_t dtype, bool rope, const RowArgs& a_in, hipStream_t s, bool beside) {
   if (a_in.ntok == 0) return;
   const int64_t per = (int64_t)kXcds * kRun;
   const int64_t padded = (a_in.ntok + per - 1) / per * per;
   RowArgs a = a_in;
-  // k_dq: 128 heads per block
-  a.n_hb = (int32_t)((a.Gp + 127) / 128);
-  const dim3 g2((unsigned)(padded * a.n_hb)), b2(512);
+  // k_dq: 128 heads per block (8 waves); at most 64 heads on the caller's
+  // stream: one block of 64 as 4 waves, two workgroups per CU (64 heads, 8192
+  // tokens: 1.83 -> 1.06 ms).  Beside the key-block kernels the 8-wave form
+  // stays: the 4-wave one takes the CUs first and the key-block launch
+  // behind it loses more than it gains (step 6.90 -> 7.33 ms).
+  const int nw = kDq64x4 && a.Gp <= 64 && !beside ? 4 : 8;
+  a.n_hb = (int32_t)((a.Gp + 16 * nw - 1) / (16 * nw));
+  const dim3 g2((unsigned)(padded * a.n_hb)), b2(64 * nw);
+  auto go = [&](auto kern8, auto kern4) {
+    if (nw == 8) hipLaunchKernelGGL(kern8, g2, b2, 0, s, a);
+    else hipLaunchKernelGGL(kern4, g2, b2, 0, s, a);
+  };
   if (dtype == SFAG_BF16) {
-    if (rope) hipLaunchKernelGGL((k_dq<BF16, 64>), g2, b2, 0, s, a);
-    else hipLaunchKernelGGL((k_dq<BF16, 0>), g2, b2, 0, s, a);
+    if (rope) go(k_dq<BF16, 64, 8>, k_dq<BF16, 64, 4>);
+    else go(k_dq<BF16, 0, 8>, k_dq<BF16, 0, 4>);
   } else {
-    if (rope) hipLaunchKernelGGL((k_dq<FP16, 64>), g2, b2, 0, s, a);
-    else hipLaunchKernelGGL((k_dq<FP16, 0>), g2, b2, 0, s, a);
+    if (rope) go(k_dq<FP16, 64, 8>, k_dq<FP16, 64, 4>);
+    else go(k_dq<FP16, 0, 8>, k_dq<FP16, 0, 4>);
   }
 }
 

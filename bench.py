@@ -173,8 +173,14 @@ def _summarize_profiles(d, config, calib_mb):
       bench.py launches first are recorded beside them as a check.
 
     The backward steps of a counter run are the dispatches between the first
-    and the last k_cast (one per backward call; the forward pass and the index
-    count that make the inputs run before the first call)."""
+    and the last end-of-call kernel (k_cast, or on the key-block path the
+    range reduction that writes the outputs: one per backward call; the
+    forward pass and the index count that make the inputs run before the
+    first call).  When d/trace also holds the per-dispatch kernel trace, the
+    summary adds each kernel group's average over the last backward calls of
+    the run, the serial pass that bench.py times kernels in when the library
+    may overlap k_dq with the key-block kernels, next to the roofline kernel
+    time bench.py printed in that run (d/trace.log)."""
     import re
     from collections import defaultdict
 
@@ -195,8 +201,10 @@ def _summarize_profiles(d, config, calib_mb):
             out.setdefault(i, (r["Kernel_Name"], defaultdict(float)))[1][name] += float(r["Counter_Value"])
         return out
 
+    call_end = re.compile(r"k_cast<|k_kb_reduce<[^>]*true>")
+
     def window(disp):
-        ids = sorted(i for i, (k, _c) in disp.items() if "k_cast<" in k)
+        ids = sorted(i for i, (k, _c) in disp.items() if call_end.search(k))
         if len(ids) < 2:
             return {}, 0
         return {i: v for i, v in disp.items() if ids[0] < i <= ids[-1]}, len(ids) - 1
@@ -229,6 +237,31 @@ def _summarize_profiles(d, config, calib_mb):
         mb = f"{mfma[g]:.3f}" if g in mfma and mfma[g] is not None else "-"
         lines.append(f"{name[:64]:<64} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} "
                      f"{float(r['TotalDurationNs']) / 1e6:>10.3f} {float(r['Percentage']):>6.2f} {mb:>9}")
+    # per-dispatch trace: each group's average over the serial pass (the last
+    # n backward calls, n = bench.py's serial-pass length for the run's steps)
+    trace = _read_csvs(os.path.join(d, "trace"), "kernel_trace.csv")
+    if trace:
+        rows = sorted((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                      for r in trace if "sfag" in r["Kernel_Name"])
+        ends = [j for j, (_i, k, _t) in enumerate(rows) if call_end.search(k)]
+        roof = None
+        log = os.path.join(d, "trace.log")
+        if os.path.exists(log):
+            for line in open(log):
+                if line.startswith("{"):
+                    roof = json.loads(line).get("roofline")
+        n = 5
+        if len(ends) > n:
+            sel = rows[ends[-n - 1] + 1: ends[-1] + 1]
+            lines += ["", f"Serial pass (the last {n} backward calls of the trace run, each kernel alone on the GPU), "
+                          "average per launch:"]
+            for g, pat in _GROUPS.items():
+                ts = [t for _i, k, t in sel if re.search(pat, k)]
+                if ts:
+                    lines.append(f"  {g:<10} {len(ts):>4} launches  {sum(ts) / len(ts) / 1e3:10.1f} us")
+            if roof:
+                lines.append(f"bench.py in the same run: roofline kernel {roof.get('kernel')}, "
+                             f"{roof.get('kernel_ms', 0.0) * 1e3:.1f} us a launch ({roof.get('timing')})")
     with open(os.path.join(out_dir, f"{case.name}_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 

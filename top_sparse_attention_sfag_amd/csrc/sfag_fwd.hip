@@ -32,6 +32,7 @@ constexpr int kTile = 32;   // positions per tile
 constexpr int kXcds = 8;    // blockIdx % 8 picks the XCD
 constexpr int kRun = 16;    // consecutive tokens per XCD run
 constexpr bool kFwd8 = true;   // 64-head blocks (N1 > 32) as 8 waves (k_fwd8)
+constexpr bool kFwdSpread = true;   // k_fwd8 issues a tile's copies between the Sᵀ MFMAs
 
 // Asynchronous global -> LDS copy of 16 bytes per lane (lane l writes at the
 // wave-uniform LDS address l_base + 16 l).  Inline asm on purpose: the
@@ -306,24 +307,34 @@ __global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
   // Gather of the 32 rows of a tile into buffer `buf` (rows past nv repeat a
   // valid row, masked out of the softmax) in five steps per wave: step j < 4
   // copies K (and V) row 4w + j, step 4 (w < 4) rope rows 8w .. 8w + 7.
-  // key_l: lane r & 31 holds the key row of the tile's position r.
-  auto tile_key = [&](int c0) -> int {
-    const int cl = c0 + (lane & 31);
-    return rt[cl < nv ? cl : 0];
+  // The key rows of a step's copies are formed for all five steps at once
+  // (scalar for the wave's K|V rows, one lane shuffle for the rope rows), so
+  // that issuing a step needs no LDS operation and no wait of its own.
+  struct TileKeys {
+    int32_t row[4];
+    int32_t rope;
   };
-  auto issue_step = [&](int j, int key_l, int buf) {
+  auto tile_keys8 = [&](int c0) -> TileKeys {
+    const int cl = c0 + (lane & 31);
+    const int key_l = rt[cl < nv ? cl : 0];   // lane r & 31: key row of the tile's position r
+    TileKeys tk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tk.row[j] = __builtin_amdgcn_readlane(key_l, wave * 4 + j);
+    tk.rope = DR > 0 ? __shfl(key_l, (wave & 3) * 8 + (lane >> 3), 64) : 0;
+    return tk;
+  };
+  auto issue_step = [&](int j, const TileKeys& tk, int buf) {
     unsigned char* base = smem + buf * BUF;
     if (j < 4) {
       const int r = wave * 4 + j;
-      const int64_t key = __builtin_amdgcn_readfirstlane(__shfl(key_l, r, 64));
+      const int64_t key = tk.row[j];
       const int gc = lane ^ (r & 7);
       lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
       if (!VK) lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
     } else if (DR > 0 && wave < 4) {
       const int r_l = wave * 8 + (lane >> 3);
-      const int key_r = __shfl(key_l, r_l, 64);
       const int gc = (lane & 7) ^ (r_l & 7);
-      lds_load16(a.kr + (int64_t)key_r * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
+      lds_load16(a.kr + (int64_t)tk.rope * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
     }
   };
 
@@ -340,7 +351,7 @@ __global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
   for (int c = 0; c < 4; ++c) oT[c] = r1 * 1024 + 16 * ((2 * c + half) ^ x1) + hoff + 128 * wave;
 
   if (nv > 0) {
-    const int k0 = tile_key(0);
+    const TileKeys k0 = tile_keys8(0);
 #pragma unroll
     for (int j = 0; j < 5; ++j) issue_step(j, k0, 0);
   }
@@ -348,12 +359,12 @@ __global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
   for (int c0 = 0; c0 < nv; c0 += kTile) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // the next tile's copies, at once (spread between the Sᵀ MFMAs instead:
-    // config 2 forward 3.77 -> 4.26 ms)
-    if (c0 + kTile < nv) {
-      const int key_n = tile_key(c0 + kTile);
+    // the next tile's copies: at once here, or spread between the Sᵀ MFMAs
+    const bool more = c0 + kTile < nv;
+    const TileKeys tk = tile_keys8(more ? c0 + kTile : c0);
+    if (!kFwdSpread && more) {
 #pragma unroll
-      for (int j = 0; j < 5; ++j) issue_step(j, key_n, cur ^ 1);
+      for (int j = 0; j < 5; ++j) issue_step(j, tk, cur ^ 1);
     }
     const unsigned char* Km = smem + cur * BUF;
     const unsigned char* Kr = Km + KM_BYTES;
@@ -370,6 +381,7 @@ __global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS_QK; ++ks) {
       if (ks + 3 < KS_QK) kb4[(ks + 3) & 3] = *(const uint4*)kaddr(ks + 3);
+      if (kFwdSpread && more && (ks & 1) && (ks >> 1) < 5) issue_step(ks >> 1, tk, cur ^ 1);
       sv = TT::mfma(as_vec8<V8>(kb4[ks & 3]), Qf[ks], sv);
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -536,7 +536,13 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
   constexpr int kPerRow = VK ? 1 : 2;
   constexpr int kRowOps = kPerRow * (kTile / NW);
   constexpr int kOps = kRowOps + (DR > 0 ? 1 : 0);
-  auto issue_op = [&](int i, int32_t keyv, uint32_t base) {
+  // (rkey: this lane's rope row key, rope_key(keyv), formed before the MFMA
+  // loop: a lane shuffle there would wait on LDS and so also on the operand
+  // reads issued ahead of the MFMAs)
+  auto rope_key = [&](int32_t keyv) -> int32_t {
+    return DR > 0 ? __shfl(keyv, (wave & 3) * 8 + (lane >> 3)) : 0;
+  };
+  auto issue_op = [&](int i, int32_t keyv, int32_t rkey, uint32_t base) {
     if (i < kRowOps) {
       const int r = wave + NW * (i / kPerRow);
       const int64_t key = __builtin_amdgcn_readlane(keyv, r);
@@ -545,9 +551,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
       else lds_load16_at(a.k + key * 512 + gc * 8, base + r * 1024);
     } else if (wave < kTile / 8) {
       const int r = wave * 8 + (lane >> 3);
-      const int64_t key = __shfl(keyv, r);
       const int gc = (lane & 7) ^ ((r >> 1) & 7);
-      lds_load16_at(a.kr + key * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
+      lds_load16_at(a.kr + (int64_t)rkey * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
     }
   };
   // staged rows stored by this wave: tensor wave / (NW / 2), rows
@@ -585,6 +590,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
     // that they hold no registers through the MFMA loop
     if (stg_c0 >= 0) stage_out();
     const bool more = c0 + kTile < nv;
+    const int32_t rkey = rope_key(keys);
     const uint32_t nxt_l = lds_off(nxt);
     const unsigned char* Kr = Km + KM_BYTES;
     const unsigned char* Vm = VK ? Km : Kr + KR_BYTES;
@@ -611,7 +617,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
       // the next tile's copies over the first 8 k-steps (two buffers)
       if (!kOne && more && ks < 8)
 #pragma unroll
-        for (int i = ks * kOps / 8; i < (ks + 1) * kOps / 8; ++i) issue_op(i, keys, nxt_l);
+        for (int i = ks * kOps / 8; i < (ks + 1) * kOps / 8; ++i) issue_op(i, keys, rkey, nxt_l);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         S[nb] = TT::mfma(Qf[ks], as_vec8<V8>(kv[ks & LA][nb]), S[nb]);
@@ -651,7 +657,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
              // buffer, is done with this tile's operands)
     if (kOne && more) {
 #pragma unroll
-      for (int i = 0; i < kOps; ++i) issue_op(i, keys, nxt_l);
+      for (int i = 0; i < kOps; ++i) issue_op(i, keys, rkey, nxt_l);
       keys = tile_keys(rt, nv, c0 + 2 * kTile, lane);
     }
 #pragma unroll
@@ -666,8 +672,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) k_sdp8(RowArgs a) {
 
   if (nv > 0) {
     const uint32_t b0 = lds_off(buf0);
+    const int32_t rkey0 = rope_key(keys);
 #pragma unroll
-    for (int i = 0; i < kOps; ++i) issue_op(i, keys, b0);
+    for (int i = 0; i < kOps; ++i) issue_op(i, keys, rkey0, b0);
   }
   keys = tile_keys(rt, nv, kTile, lane);
   if constexpr (kOne) {

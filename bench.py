@@ -114,7 +114,7 @@ def _roofline(case, kernel, kernel_ms, launches_per_step, n_pairs):
 # one stands for.
 _GROUPS = {
     "sdp": r"k_sdp8?<", "dq": r"k_dq<", "row": r"k_row(16)?<", "keyblock": r"k_keyblock<",
-    "col": r"k_col<", "fwd": r"k_fwd<", "kb_reduce": r"k_kb_reduce", "cast": r"k_cast<", "decode": r"k_decode",
+    "col": r"k_col<", "fwd": r"k_fwd8?<", "kb_reduce": r"k_kb_reduce", "cast": r"k_cast<", "decode": r"k_decode",
     "delta": r"k_delta<",
 }
 _SOURCES = ["include/sfag.h", "top_sparse_attention_sfag_amd/build.py"]

@@ -7,16 +7,17 @@
 //     out[h] = Σ_p exp(z − max) / softmaxSum · V[p]
 // A token without a valid position gets max = −inf, sum = 0 and out = 0.
 //
-// gfx950 mapping, k_fwd (up to 32 heads; the same tiles as the N1 <= 16
-// backward kernel): one workgroup per (token, 64-head block), 4 waves of 16
-// heads (k_fwd8 below takes 64-head blocks with 8 waves).  Per tile of 32
-// gathered positions, Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32 (positions as M, the
-// wave's Q rows resident in registers), an online softmax per head (running
-// max and sum; the fp32 output accumulators are rescaled when the max
-// grows), and out += P·V with P taken straight from the Sᵀ accumulator
-// layout as the A operand and V read transposed from LDS
-// (ds_read_b64_tr_b16).  K|Krope|V rows arrive through global_load_lds into
-// a double buffer, 16-byte chunks XOR-swizzled by (row & 7).
+// gfx950 mapping (k_fwd8 below): one workgroup per (token, 64-head block) as
+// 8 waves.  Per tile of 32 gathered positions, Sᵀ = K·Qᵀ on
+// v_mfma_f32_16x16x32 (positions as M, Q rows resident in registers), an
+// online softmax per head (running max and sum; the fp32 output
+// accumulators are rescaled when the max grows), and out += P·V with P from
+// LDS as the A operand and V read transposed from LDS (ds_read_b64_tr_b16).
+// K|Krope|V rows arrive through global_load_lds into a double buffer,
+// 16-byte chunks XOR-swizzled by (row & 7).  With fewer than 64 heads the
+// block's upper head groups are zero (64-head blocks with 8 waves measured
+// faster at 16 heads than 4 waves of which one held the heads: 87.3 -> 63.6
+// ms for 2 x 32768 tokens of 512 blocks of 16).
 #include "sfag_device.h"
 #include "sfag_kernels.h"
 #include "sfag_plan.h"
@@ -31,7 +32,6 @@ typedef __attribute__((address_space(3))) void lvoid;
 constexpr int kTile = 32;   // positions per tile
 constexpr int kXcds = 8;    // blockIdx % 8 picks the XCD
 constexpr int kRun = 16;    // consecutive tokens per XCD run
-constexpr bool kFwd8 = true;   // 64-head blocks (N1 > 32) as 8 waves (k_fwd8)
 constexpr bool kFwdSpread = true;   // k_fwd8 issues a tile's copies between the Sᵀ MFMAs
 
 // Asynchronous global -> LDS copy of 16 bytes per lane (lane l writes at the
@@ -51,197 +51,8 @@ __device__ __forceinline__ void lds_load16(const void* g, void* l) {
 
 }  // namespace
 
-template <typename TT, int DR, bool VK>
-__global__ void __launch_bounds__(256, 1) k_fwd(FwdArgs a) {
-  constexpr int DQK = 512 + DR;
-  constexpr int KS_QK = DQK / 32;
-  constexpr int NB_V = 512 / 16;                // 16-column blocks of out
-  constexpr int KM_BYTES = kTile * 1024;
-  constexpr int KR_BYTES = kTile * DR * 2;
-  constexpr int V_BYTES = VK ? 0 : kTile * 1024;
-  constexpr int BUF = KM_BYTES + KR_BYTES + V_BYTES;
-  typedef typename TT::vec8 V8;
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
-
-  // ---- work unit: (token, head block), XCD-aware order ---------------------
-  const int b = blockIdx.x;
-  const int xcd = b % kXcds, u = b / kXcds;
-  const int hb = u % a.n_hb;
-  const int tq = u / a.n_hb;
-  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
-  if (tl >= a.ntok) return;
-  const int64_t t = a.t0 + tl;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
-  const int h0 = hb * 64 + wave * 16;
-  const bool wave_on = h0 < a.Gp;
-  const int h = h0 + n;
-  const bool hv = h < a.G;
-
-  // B operand of Sᵀ = K·Qᵀ: lane (head n, k-group g) holds dims 32ks + 8g ..
-  V8 Qf[KS_QK];
-#pragma unroll
-  for (int ks = 0; ks < KS_QK; ++ks) {
-    const int d0 = 32 * ks + 8 * g;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (wave_on && hv) {
-      if (d0 < 512) v = *(const uint4*)(a.q + (t * a.G + h) * 512 + d0);
-      else v = *(const uint4*)(a.qr + (t * a.G + h) * DR + (d0 - 512));
-    }
-    Qf[ks] = as_vec8<V8>(v);
-  }
-  f32x4 acc[NB_V];
-#pragma unroll
-  for (int i = 0; i < NB_V; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max (natural units) of head n, and this lane's share of the sum
-  float m_run = -__builtin_inff(), l_run = 0.f;
-
-  const int nv = a.nvalid[tl];
-  const int32_t* rt = a.rows + tl * a.E;
-
-  // Gather the 32 rows of tile c0 into buffer `buf`; rows past nv repeat a
-  // valid row (masked out of the softmax).  Wave w loads rows 8w..8w+7.
-  auto issue_tile = [&](int c0, int buf) {
-    unsigned char* base = smem + buf * BUF;
-    const int r_l = wave * 8 + (lane >> 3);  // rope row handled by this lane
-    const int c_l = c0 + r_l;
-    const int key_l = rt[c_l < nv ? c_l : 0];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = wave * 8 + j;
-      const int64_t key = __builtin_amdgcn_readfirstlane(__shfl(key_l, j * 8, 64));
-      const int gc = lane ^ (r & 7);
-      lds_load16(a.k + key * 512 + gc * 8, base + r * 1024);
-      if (!VK) lds_load16(a.v + key * 512 + gc * 8, base + KM_BYTES + KR_BYTES + r * 1024);
-    }
-    if (DR > 0) {
-      const int pc = lane & 7;
-      const int gc = pc ^ (r_l & 7);
-      lds_load16(a.kr + (int64_t)key_l * DR + gc * 8, base + KM_BYTES + wave * 8 * (DR * 2));
-    }
-  };
-
-  // Per-lane LDS byte offsets (chunk c of row r sits at (c & ~7) | ((c & 7) ^ (r & 7))).
-  const int x = n & 7;
-  const int oA_even = n * 1024 + 16 * (g ^ x);
-  const int oA_odd = n * 1024 + 16 * ((4 + g) ^ x);
-  const int oR_even = n * (DR * 2) + 16 * (g ^ x);
-  const int oR_odd = n * (DR * 2) + 16 * ((4 + g) ^ x);
-  const int r1 = 4 * g + (n >> 2), x1 = r1 & 7;       // V rows r1 and r1 + 16 for the out MFMA
-  const int half = (n & 3) >> 1, hoff = (n & 1) * 8;
-  int oT[4];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) oT[w] = r1 * 1024 + 16 * ((2 * w + half) ^ x1) + hoff;
-
-  if (nv > 0) issue_tile(0, 0);
-  int cur = 0;
-  for (int c0 = 0; c0 < nv; c0 += kTile) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (c0 + kTile < nv) issue_tile(c0 + kTile, cur ^ 1);
-    const unsigned char* Km = smem + cur * BUF;
-    const unsigned char* Kr = Km + KM_BYTES;
-    const unsigned char* Vm = VK ? Km : Km + KM_BYTES + KR_BYTES;
-    if (wave_on) {
-      // Sᵀ: rows = positions mb*16 + 4g + i, column = head n
-      // (operand reads issued three MFMAs ahead; each step pinned in order)
-      constexpr int NS = 2 * KS_QK;                 // MFMAs of the two row blocks
-      auto kaddr = [&](int i) -> const unsigned char* {
-        const int mb = i / KS_QK, ks = i % KS_QK;
-        if (ks < 16) return Km + ((ks & 1) ? oA_odd : oA_even) + 128 * (ks >> 1) + mb * 16384;
-        return Kr + ((ks & 1) ? oR_odd : oR_even) + mb * 16 * (DR * 2);
-      };
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      uint4 kb4[4];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) kb4[i] = *(const uint4*)kaddr(i);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        if (i + 3 < NS) kb4[(i + 3) & 3] = *(const uint4*)kaddr(i + 3);
-        s[i / KS_QK] = TT::mfma(as_vec8<V8>(kb4[i & 3]), Qf[i % KS_QK], s[i / KS_QK]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // online softmax of head n over the tile's valid positions
-      float z[8];
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = mb * 16 + 4 * g + i;
-          z[mb * 4 + i] = c0 + j < nv ? s[mb][i] * a.scale : -__builtin_inff();
-          tmax = fmaxf(tmax, z[mb * 4 + i]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);   // finite: the tile has a valid position
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e);
-      uint16_t pv[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f((z[j] - m_new) * kLog2e);
-        psum += p;
-        pv[j] = TT::from_f(p);
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // rescale the accumulator rows (heads 4g + i) by their heads' alpha
-      float ar[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int nb = 0; nb < NB_V; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nb][i] *= ar[i];
-      // out += P·V: A = P (head n, positions 4g+i and 16+4g+i), B = V rows
-      // 4g..4g+3 and 16+4g..16+4g+3 of one column, read transposed
-      const uint4 pu = make_uint4(pv[0] | ((uint32_t)pv[1] << 16), pv[2] | ((uint32_t)pv[3] << 16),
-                                  pv[4] | ((uint32_t)pv[5] << 16), pv[6] | ((uint32_t)pv[7] << 16));
-      const V8 A8 = as_vec8<V8>(pu);
-      auto vread = [&](int nb) -> V8 {
-        const unsigned char* p1 = Vm + oT[nb & 3] + 128 * (nb >> 2);
-        return join_tr<V8>(lds_read_tr((const uint16_t*)p1), lds_read_tr((const uint16_t*)(p1 + 16 * 1024)));
-      };
-      V8 vb[4];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) vb[i] = vread(i);
-#pragma unroll
-      for (int nb = 0; nb < NB_V; ++nb) {
-        if (nb + 3 < NB_V) vb[(nb + 3) & 3] = vread(nb + 3);
-        acc[nb] = TT::mfma(A8, vb[nb & 3], acc[nb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    cur ^= 1;
-  }
-  if (!wave_on) return;
-  // the sum of head n over the four lanes that share it
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (g == 0 && hv) {
-    a.smax[t * a.G + h] = m_run;
-    a.ssum[t * a.G + h] = l_tot;
-  }
-  float inv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(l_tot, 4 * g + i);
-    inv[i] = li > 0.f ? 1.f / li : 0.f;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB_V; ++nb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = h0 + 4 * g + i;
-      if (hh < a.G) a.out[(t * a.G + hh) * 512 + 16 * nb + n] = TT::from_f(acc[nb][i] * inv[i]);
-    }
-  }
-}
-
-// k_fwd8: the same output for a 64-head block as 8 waves, two per SIMD, so
-// that one wave's MFMAs run while the other waits.  Wave w = 4 ph + hg forms
+// k_fwd8: one workgroup per (token, 64-head block) as 8 waves, two per SIMD,
+// so that one wave's MFMAs run while the other waits.  Wave w = 4 ph + hg forms
 // Sᵀ of head group hg (16 heads, Q in registers) over the position half ph
 // of each 32-position tile; the two halves' maxima meet in LDS, each wave
 // turns its half into P (bf16, into LDS as (head, position) rows) with the
@@ -338,7 +149,8 @@ __global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
     }
   };
 
-  // Sᵀ operand offsets (rows ph·16 + n, see k_fwd) and the transposed V reads
+  // Sᵀ operand offsets (rows ph·16 + n; chunk c of row r sits at chunk
+  // (c & ~7) | ((c & 7) ^ (r & 7))) and the transposed V reads
   const int x = n & 7;
   const int oA_even = n * 1024 + 16 * (g ^ x) + ph * 16384;
   const int oA_odd = n * 1024 + 16 * ((4 + g) ^ x) + ph * 16384;
@@ -476,17 +288,11 @@ void launch_fwd(int32_t dtype, bool rope, const FwdArgs& a, hipStream_t s) {
   const int64_t padded = (a.ntok + per - 1) / per * per;
   const dim3 grid((unsigned)(padded * a.n_hb));
   const bool vk = a.v == a.k;   // value passed as the key tensor: gather each row once
-  const bool eight = kFwd8 && a.Gp >= 64;
   auto go = [&](auto tt, auto dr) {
     typedef decltype(tt) T;
     constexpr int D = decltype(dr)::value;
-    if (eight) {
-      if (vk) hipLaunchKernelGGL((k_fwd8<T, D, true>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((k_fwd8<T, D, false>), grid, dim3(512), 0, s, a);
-    } else {
-      if (vk) hipLaunchKernelGGL((k_fwd<T, D, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((k_fwd<T, D, false>), grid, dim3(256), 0, s, a);
-    }
+    if (vk) hipLaunchKernelGGL((k_fwd8<T, D, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_fwd8<T, D, false>), grid, dim3(512), 0, s, a);
   };
   if (dtype == SFAG_BF16) {
     if (rope) go(BF16(), std::integral_constant<int, 64>());

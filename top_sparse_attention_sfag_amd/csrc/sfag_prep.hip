@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(256) k_decode(const int32_t* __restrict__ idx,
   }
   int32_t bad = 0;
   // (uniform: one token per block)
-  bool srtd = nw > 0 && g.ok && g.Lk <= 32 * nw;
+  bool srtd = nw > 0 && g.ok && g.Lk > 0 && g.Lk <= 32 * nw;
   uint16_t* srt = (uint16_t*)(dsh + nw);
   int64_t Ew = E;                        // positions walked below
   if (srtd) {

@@ -153,10 +153,13 @@ typedef struct sfag_options {
  * length, or (sparseMode 3) after t + Lk − Lq, are masked.
  * scaleValue: finite; used as float32.  sparseBlockSize ∈ {1, 8, 16, 32, 64}.
  * layoutOptional: "BSND" or "TND" (NULL = "BSND").  sparseMode ∈ {0, 3}.
- * preTokens = nextTokens = 2147483647.  deterministic: when true dKey/dValue
- * are bitwise reproducible run to run (key-centric reduction over a
- * key→(token, position) CSR); when false dKey/dValue may differ in the last
- * bits between runs.
+ * preTokens = nextTokens = 2147483647.  deterministic: when true every
+ * output is bitwise reproducible run to run (dKey/dValue from a key-centric
+ * reduction in a fixed order; dQuery summed in a fixed order); when false the
+ * outputs may differ in the last bits between runs (with N1 <= 16 the token
+ * kernel starts each token's walk where its XCD's workgroups are, and a
+ * token's positions may be split over workgroups; fp32 atomics where the
+ * selection is sparse).
  * On SFAG_OK *workspaceSize and *plan are set; the plan must be passed to
  * sfag_backward (which frees it) or to sfag_plan_destroy.  On error *plan is
  * NULL and sfag_last_error() describes the failure.

@@ -81,7 +81,8 @@ typedef struct sfag_plan sfag_plan;
 #define SFAG_TOKEN_SPLIT 2       /* S/P/dP/dS kernel then dQ kernel (up to 128 heads a workgroup; N1 >= 32) */
 #define SFAG_ORDER_AUTO 0
 #define SFAG_ORDER_ASCENDING 1   /* token kernels visit a chunk first token first */
-#define SFAG_ORDER_DESCENDING 2  /* last token first (the default under sparseMode 3) */
+#define SFAG_ORDER_DESCENDING 2  /* last token first (the default under sparseMode 3, except
+                                    with 128 heads and k_dq on a second stream) */
 #define SFAG_CONCURRENT_AUTO 0
 #define SFAG_CONCURRENT_OFF 1
 #define SFAG_CONCURRENT_ON 2

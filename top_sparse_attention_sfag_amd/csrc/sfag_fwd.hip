@@ -82,7 +82,8 @@ __global__ void __launch_bounds__(512, 1) k_fwd8(FwdArgs a) {
   const int xcd = b % kXcds, u = b / kXcds;
   const int hb = u % a.n_hb;
   const int tq = u / a.n_hb;
-  const int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  int64_t tl = ((int64_t)(tq / kRun) * kXcds + xcd) * kRun + (tq % kRun);
+  if (a.reverse) tl = (a.ntok + kXcds * kRun - 1) / (kXcds * kRun) * (kXcds * kRun) - 1 - tl;
   if (tl >= a.ntok) return;
   const int64_t t = a.t0 + tl;
 

@@ -57,6 +57,7 @@ struct FwdArgs {
   int64_t t0, ntok, G, Gp, E;
   int32_t n_hb;   // 64-head blocks per token
   float scale;
+  int32_t reverse;   // visit the chunk's tokens last to first
 };
 void launch_fwd(int32_t dtype, bool rope, const FwdArgs& a, hipStream_t s);
 

@@ -198,6 +198,9 @@ extern "C" int sfag_forward(void* workspace, uint64_t workspaceSize, sfag_plan* 
   fa.E = d.E;
   fa.n_hb = (int32_t)((d.Gp + 63) / 64);
   fa.scale = plan->scale;
+  // causal rows grow with the token: longest tokens first (128 heads, 4096
+  // tokens, top-2048 causal: 3.38 -> 3.32 ms)
+  fa.reverse = d.mode == 3 ? 1 : 0;
   for (int64_t t0 = 0; t0 < d.T1; t0 += d.chunk) {
     const int64_t ntok = std::min<int64_t>(d.chunk, d.T1 - t0);
     {
